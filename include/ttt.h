@@ -1,0 +1,180 @@
+/*
+ * ttt.h - C ABI of the MI355X (gfx950) TTT-E2E prefill / decode library.
+ *
+ * The method ("End-to-End Test-Time Training for Long Context"): a Transformer
+ * with causal sliding-window attention (window k >= b) reads its context in
+ * mini-batches ("chunks") of b positions. For each chunk it scores every
+ * position with the current fast weights W, then takes one SGD step
+ *     W_i = W_{i-1} - eta * (1/b) * sum over the chunk of grad l_p(W_{i-1})
+ * where l_p is the next-token cross entropy (natural log). Only the MLPs of
+ * the last quarter of the blocks are fast weights; embeddings, norms,
+ * attention, the LM head and a second, static MLP branch in each of those
+ * blocks stay frozen but are differentiated through.
+ * Sources: b-lab.team summary, "Test-Time Training (Inner Loop)" and
+ * "Implementation Details for TTT"; technical review "TTT-E2E: Learning a Long
+ * Context into Weights", section 5 (Eq. 9), section 6, section 7 (Algorithms
+ * 1 and 3).
+ *
+ * Conventions for every call:
+ *   - Device pointers are HIP device addresses on the current device; host
+ *     pointers are ordinary process memory. Which is which is stated per
+ *     argument.
+ *   - `stream` is a hipStream_t cast to void* (NULL = the null stream).
+ *     Calls marked "async" only enqueue work on `stream`; the caller keeps its
+ *     buffers alive until that work completes.
+ *   - Return 0 on success or a negative TTT_E* code. Arguments are validated
+ *     before any work is enqueued, so a call that fails validation leaves the
+ *     model unchanged. After a HIP runtime error the model is "poisoned": all
+ *     calls except ttt_reset / ttt_model_destroy / ttt_last_error return
+ *     TTT_ESTATE until ttt_reset succeeds. ttt_last_error() returns a
+ *     thread-local message for the last failure.
+ *   - Matrices passed in are row-major [in][out] (y = x @ W).
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stdint.h>
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_OK 0
+#define TTT_EINVAL (-1)  /* invalid argument or configuration */
+#define TTT_ENOMEM (-2)  /* device allocation failed or over max_device_bytes */
+#define TTT_EHIP (-3)    /* HIP runtime error (model is poisoned) */
+#define TTT_ESTATE (-4)  /* call not valid in this state (e.g. decode before prefill) */
+
+enum ttt_dtype { TTT_FP32 = 0, TTT_BF16 = 1 };
+enum ttt_mlp { TTT_GELU = 0, TTT_SWIGLU = 1 };
+enum ttt_mat { TTT_UP = 0, TTT_GATE = 1, TTT_DOWN = 2 };
+
+/* Model shape and inner-loop hyper-parameters.
+ * n_ttt_blocks tail blocks (the last ones) carry fast MLP weights of hidden
+ * size ttt_hidden plus a static branch of hidden size static_hidden; the other
+ * blocks have one frozen MLP of hidden size mlp_hidden. Attention is
+ * multi-head with n_heads * head_dim columns per projection. RMSNorm with
+ * norm_eps everywhere (pre-attention, pre-MLP, final). RoPE (if rope != 0) on
+ * pairs (i, i + head_dim/2) at absolute positions, base rope_theta.
+ * window = k, mini_batch = b (k >= b is required), lr = eta.
+ * batch = number of independent sequences, each with its own fast weights,
+ * attention cache and position counter. max_positions bounds the stream
+ * length (ids) per sequence. prefill_span bounds how many positions the
+ * frozen lower blocks process per pass (0 = library default).
+ * max_device_bytes (0 = unlimited) caps the library's allocation. */
+typedef struct ttt_config {
+  int32_t vocab, d_model, n_blocks, n_heads, head_dim;
+  int32_t mlp_kind;          /* enum ttt_mlp */
+  int32_t mlp_hidden, n_ttt_blocks, ttt_hidden, static_hidden;
+  int32_t rope;
+  float rope_theta, norm_eps;
+  int32_t window, mini_batch;
+  float lr;
+  int32_t dtype;             /* enum ttt_dtype: storage and GEMM operand type */
+  int32_t batch;
+  int64_t max_positions;
+  int32_t prefill_span;
+  int64_t max_device_bytes;
+} ttt_config;
+
+/* Initial weights, all device pointers in cfg.dtype, row-major [in][out].
+ * Per-block arrays are HOST arrays of n_blocks device pointers.
+ *   embed [V][d], final_norm [d], lm_head [d][V]
+ *   attn_norm[l], mlp_norm[l]: [d]
+ *   wq[l], wk[l], wv[l]: [d][H*hd];  wo[l]: [H*hd][d]
+ *   w_up[l], w_gate[l] (SwiGLU only, else NULL): [d][h];  w_down[l]: [h][d]
+ *     with h = ttt_hidden for tail blocks (the fast, trainable branch) and
+ *     mlp_hidden otherwise
+ *   s_up[l], s_gate[l], s_down[l]: static branch of tail blocks ([d][hs],
+ *     [d][hs], [hs][d]); NULL (or ignored) for other blocks. */
+typedef struct ttt_weights {
+  const void* embed;
+  const void* final_norm;
+  const void* lm_head;
+  const void* const* attn_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+  const void* const* mlp_norm;
+  const void* const* w_up;
+  const void* const* w_gate;
+  const void* const* w_down;
+  const void* const* s_up;
+  const void* const* s_gate;
+  const void* const* s_down;
+} ttt_weights;
+
+typedef struct ttt_model ttt_model;
+
+/* Create a model: validates cfg, allocates library-owned storage (frozen
+ * weights, per-sequence fast weights - an fp32 master plus the cfg.dtype copy
+ * the GEMMs read - attention caches and workspace) and copies `init` into it
+ * (the copy runs on `stream` and is complete when the call returns). The
+ * caller's weight buffers may be freed afterwards. Every sequence starts from
+ * a fresh copy of the initial fast weights (review, Algorithm 1 step 1).
+ * Errors: TTT_EINVAL (k < b, d_model or n_heads or head_dim < 1, n_ttt_blocks
+ * not in [1, n_blocks], odd head_dim with rope, NULL pointers), TTT_ENOMEM,
+ * TTT_EHIP. On error *out is NULL. */
+int ttt_model_create(const ttt_config* cfg, const ttt_weights* init, void* stream,
+                     ttt_model** out);
+
+/* Prefill (review, section 7, Algorithm 1). Async.
+ * tokens: device int32 [batch][n], the next n ids of every sequence.
+ * losses: device float [batch][n] or NULL. Entry [s][i] receives the loss of
+ *   predicting new id i of sequence s, i.e. of position (n_before + i - 1)
+ *   where n_before is the stream length before this call; on the first call
+ *   of a stream entry 0 has no predecessor and is set to NaN.
+ * Every position is scored with the fast weights current for its chunk
+ * (before the update that chunk produces). Whenever chunk c = positions
+ * [c*b, (c+1)*b) has all of its labels (ids up to (c+1)*b), the library runs
+ * the chunk's backward and SGD step. Positions of an incomplete chunk are
+ * scored at the current W and wait for the rest of their chunk.
+ * Errors: TTT_EINVAL (n < 1, stream would exceed max_positions; token ids are
+ * not read on the host, ids outside [0, V) are clamped by the kernels),
+ * TTT_ESTATE (poisoned), TTT_EHIP. */
+int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t n, float* losses, void* stream);
+
+/* Greedy decode with periodic adaptation (review, section 7, Algorithm 3;
+ * summary, "Decoding Multiple Tokens"). Async.
+ * Generates n_new ids per sequence: each is the argmax (lowest id on ties)
+ * of the logits of the last position, computed with the current W. After the
+ * id is appended, if it completes a chunk of b labelled positions, that
+ * chunk's SGD step runs before the next position is computed.
+ * tokens_out: device int32 [batch][n_new]. losses: device float
+ * [batch][n_new] or NULL; entry i = -log p(chosen id i).
+ * Errors: TTT_ESTATE (no prefill yet, or poisoned), TTT_EINVAL (n_new < 1,
+ * exceeds max_positions), TTT_EHIP. */
+int ttt_decode(ttt_model* m, int64_t n_new, int32_t* tokens_out, float* losses, void* stream);
+
+/* Copy the current fp32 fast weights of one trainable matrix of one sequence
+ * into dst (device float, row-major [in][out]: UP/GATE [d][ttt_hidden],
+ * DOWN [ttt_hidden][d]). Async on `stream`. Reflects every completed chunk.
+ * Errors: TTT_EINVAL (seq out of range, block not a tail block, GATE without
+ * SwiGLU, dst NULL). */
+int ttt_get_weights(const ttt_model* m, int32_t seq, int32_t block, int32_t mat, float* dst,
+                    void* stream);
+
+/* Reset every sequence: fast weights <- initial weights, empty caches and
+ * streams (review, Algorithm 2 step 7: per-sequence state is discarded).
+ * Synchronous on `stream`. Clears the poisoned flag if it succeeds. */
+int ttt_reset(ttt_model* m, void* stream);
+
+/* Free everything the model owns (after synchronising the device). NULL ok. */
+void ttt_model_destroy(ttt_model* m);
+
+/* Thread-local description of the last error ("" if none). */
+const char* ttt_last_error(void);
+
+/* Number of positions already in sequence streams (ids appended). */
+int64_t ttt_stream_length(const ttt_model* m);
+
+/* Library device memory in bytes currently allocated by the model. */
+int64_t ttt_device_bytes(const ttt_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H */

@@ -1,0 +1,73 @@
+/*
+ * ttt_kernels.h - single-kernel entry points of the TTT-E2E library, used by
+ * the kernel-level parity tests. Each runs one kernel of the hot path on
+ * `stream` (async) with plain device pointers; dtype is 0 (fp32) or 1
+ * (bf16) for the storage type of the non-fp32 operands. Return 0 or a
+ * negative TTT_E* code (TTT_EINVAL for unsupported sizes / layouts,
+ * TTT_EHIP for launch errors); ttt_last_error() explains.
+ */
+#ifndef TTT_KERNELS_H
+#define TTT_KERNELS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Thread-local message of the last failed ttt_k_* call ("" if none). */
+const char* ttt_k_last_error(void);
+
+/* MFMA GEMM, C[m][n] (epi)= sum_k A(m,k) B(n,k), batched over `batch` with
+ * element strides sA, sB, sC (and sR / sW for the epilogue operands).
+ * layout 0: A[m*lda+k], B[n*ldb+k]; 1: A[m*lda+k], B[k*ldb+n];
+ *        2: A[k*lda+m], B[k*ldb+n]. Contiguous extents must be multiples of 8.
+ * epi 0: C = acc (fp32 if out_f32 else dtype); 1: C = R + acc (fp32);
+ *     2: Wm -= lr * acc (fp32 master, ld ldw), then C = cast(Wm) if C != NULL
+ *        (the inner SGD step, technical review section 5, Eq. 9). */
+int ttt_k_gemm(int32_t dtype, int32_t layout, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K,
+               const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
+               int64_t ldc, int64_t sC, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
+               int64_t sW, float lr, int32_t batch, void* stream);
+
+/* Sliding-window attention forward over a ring cache (query p sees keys
+ * p-window < j <= p; technical review section 2.1 Eq. 1 and section 5).
+ * q, o: [B*M][H*hd] rows (row s*M+i = position pos0+i of sequence s);
+ * kc, vc: [B][cap][H*hd], key position j at slot j % cap (cap multiple of 64);
+ * lse: fp32 [B][H][M] natural-log sum of exp of the scaled scores. */
+int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
+                   float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
+                   float scale, void* stream);
+
+/* Backward of ttt_k_attn_fwd: dq (fp32, rows like q) over each query's whole
+ * window; dk, dv (fp32 [B*M][H*hd]) for the keys at positions pos0..pos0+M-1
+ * only (earlier cached keys are constants). dout like q; delta = fp32
+ * [B][H][M] row sums of dout * o (see ttt_k_attn_delta). */
+int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, const float* lse,
+                   const void* dout, const float* delta, float* dq, float* dk, float* dv, int32_t B, int32_t M,
+                   int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, void* stream);
+int ttt_k_attn_delta(int32_t dtype, const void* o, const void* dout, int32_t B, int32_t M, int32_t H, int32_t hd,
+                     float* delta, void* stream);
+
+/* Fused softmax / cross entropy / logit gradient over fp32 logits [rows][V]
+ * (loss l = -log softmax(z)[label], natural log: b-lab.team summary, loss
+ * function; technical review section 2.2). ids2: device int32 [rows][2] with
+ * ids2[r][1] the label of row r.
+ * labelled != 0: losses[r] = lse - z[label] and, if dz != NULL,
+ *   dz[r] = (softmax - onehot) * scale in dtype.
+ * labelled == 0: lse[r], mx[r] and argmax[r] (lowest index among maxima). */
+int ttt_k_ce(int32_t dtype, const float* logits, int32_t rows, int32_t V, const int32_t* ids2, int32_t labelled,
+             float* losses, void* dz, float scale, float* lse, float* mx, int32_t* argmax, void* stream);
+
+/* RMSNorm y = x * (mean(x^2)+eps)^(-1/2) * g (x fp32 [rows][d], y dtype) and
+ * its backward dres (+)= r*g*dn - x*r^3*mean(x*g*dn) (fp32). */
+int ttt_k_rmsnorm_fwd(int32_t dtype, const float* x, int32_t rows, int32_t d, const void* g, float eps, void* y,
+                      float* rstd, void* stream);
+int ttt_k_rmsnorm_bwd(int32_t dtype, const float* x, const float* rstd, const void* g, const float* dn, int32_t rows,
+                      int32_t d, float* dres, int32_t accumulate, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_KERNELS_H */

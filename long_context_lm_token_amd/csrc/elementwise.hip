@@ -1,0 +1,473 @@
+// Row-wise and elementwise kernels for gfx950 (HBM-bound): embedding gather,
+// RMSNorm forward/backward, RoPE split/pack, MLP activations, fused
+// softmax / cross-entropy / logit-gradient, copies and decode bookkeeping.
+// Each thread moves 16-byte vectors where the row length allows it; a row is
+// owned by one workgroup so that its reductions stay in LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int NT = 256;
+
+template <typename T> __host__ __device__ inline const T* cp(const void* p) { return reinterpret_cast<const T*>(p); }
+template <typename T> __host__ __device__ inline T* mp(void* p) { return reinterpret_cast<T*>(p); }
+
+// ------------------------------- embedding -------------------------------
+template <typename T>
+__global__ void embed_kernel(const int32_t* ids, int64_t ids_ss, int64_t p0, int S, const T* E,
+                             int d, int vocab, float* x) {
+  const int i = blockIdx.x, s = blockIdx.y;
+  int id = ids[s * ids_ss + p0 + i];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  const T* e = E + (int64_t)id * d;
+  float* o = x + ((int64_t)s * S + i) * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) o[c] = to_f32(e[c]);
+}
+
+// ------------------------------- RMSNorm ---------------------------------
+// y = x * (mean(x^2) + eps)^(-1/2) * g ; rstd saved for the backward.
+template <typename T>
+__global__ void rmsnorm_fwd_kernel(const float* x, int d, const T* g, float eps, T* y, float* rstd) {
+  __shared__ float red[16];
+  const int64_t r = blockIdx.x;
+  const float* xr = x + r * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / d + eps);
+  T* yr = y + r * d;
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    yr[c] = from_f32<T>(v.x * rs * to_f32(g[c]));
+    yr[c + 1] = from_f32<T>(v.y * rs * to_f32(g[c + 1]));
+    yr[c + 2] = from_f32<T>(v.z * rs * to_f32(g[c + 2]));
+    yr[c + 3] = from_f32<T>(v.w * rs * to_f32(g[c + 3]));
+  }
+  if (threadIdx.x == 0) rstd[r] = rs;
+}
+
+// dx = r*g*dn - x * r^3 * mean(x*g*dn); dres (+)= dx; optional compute copy.
+template <typename T>
+__global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g, const float* dn,
+                                   int d, float* dres, T* dres_c, bool accumulate) {
+  __shared__ float red[16];
+  const int64_t r = blockIdx.x;
+  const float* xr = x + r * d;
+  const float* dr = dn + r * d;
+  float dot = 0.f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) dot += xr[c] * to_f32(g[c]) * dr[c];
+  dot = block_sum(dot, red);
+  const float rs = rstd[r];
+  const float k = rs * rs * rs * dot / d;
+  float* o = dres + r * d;
+  T* oc = dres_c ? dres_c + r * d : nullptr;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float v = rs * to_f32(g[c]) * dr[c] - xr[c] * k;
+    if (accumulate) v += o[c];
+    o[c] = v;
+    if (oc) oc[c] = from_f32<T>(v);
+  }
+}
+
+// ------------------------------- RoPE ------------------------------------
+// qkv rows [rows][3*H*hd] (q | k | v). Row r = s*S + i is position p0 + i.
+// q -> q out (rotated), k (rotated), v -> ring caches at slot pos % cap.
+template <typename T>
+__global__ void rope_split_kernel(const T* qkv, int S, int H, int hd, int64_t p0, const float2* tab,
+                                  T* q, T* kc, T* vc, int cap, int64_t seq_stride) {
+  const int64_t r = blockIdx.x;
+  const int s = r / S, i = r % S;
+  const int64_t pos = p0 + i;
+  const int HD = H * hd, half = hd / 2;
+  const T* src = qkv + r * 3 * HD;
+  T* kdst = kc + s * seq_stride + (pos % cap) * HD;
+  T* vdst = vc + s * seq_stride + (pos % cap) * HD;
+  T* qdst = q + r * HD;
+  for (int c = threadIdx.x; c < HD; c += blockDim.x) {
+    const int hh = c / hd, e = c % hd;
+    float qv = to_f32(src[c]), kv = to_f32(src[HD + c]);
+    if (tab) {
+      const int pe = e < half ? e : e - half;
+      const float2 cs = tab[pos * half + pe];
+      const int partner = hh * hd + (e < half ? e + half : e - half);
+      const float qp = to_f32(src[partner]), kp = to_f32(src[HD + partner]);
+      if (e < half) {
+        qv = qv * cs.x - qp * cs.y;
+        kv = kv * cs.x - kp * cs.y;
+      } else {
+        qv = qp * cs.y + qv * cs.x;
+        kv = kp * cs.y + kv * cs.x;
+      }
+    }
+    qdst[c] = from_f32<T>(qv);
+    kdst[c] = from_f32<T>(kv);
+    vdst[c] = src[2 * HD + c];
+  }
+}
+
+// inverse rotation of dq, dk (fp32 rows [rows][H*hd]); pack [dq | dk | dv] in T
+template <typename T>
+__global__ void rope_bwd_pack_kernel(const float* dq, const float* dk, const float* dv, int S, int H,
+                                     int hd, int64_t p0, const float2* tab, T* out) {
+  const int64_t r = blockIdx.x;
+  const int i = r % S;
+  const int64_t pos = p0 + i;
+  const int HD = H * hd, half = hd / 2;
+  const float* a = dq + r * HD;
+  const float* b = dk + r * HD;
+  const float* v = dv + r * HD;
+  T* o = out + r * 3 * HD;
+  for (int c = threadIdx.x; c < HD; c += blockDim.x) {
+    const int hh = c / hd, e = c % hd;
+    float x = a[c], y = b[c];
+    if (tab) {
+      const int pe = e < half ? e : e - half;
+      const float2 cs = tab[pos * half + pe];
+      const int partner = hh * hd + (e < half ? e + half : e - half);
+      const float xp = a[partner], yp = b[partner];
+      if (e < half) {
+        x = x * cs.x + xp * cs.y;
+        y = y * cs.x + yp * cs.y;
+      } else {
+        x = -xp * cs.y + x * cs.x;
+        y = -yp * cs.y + y * cs.x;
+      }
+    }
+    o[c] = from_f32<T>(x);
+    o[HD + c] = from_f32<T>(y);
+    o[2 * HD + c] = from_f32<T>(v[c]);
+  }
+}
+
+// ----------------------------- activations -------------------------------
+TTT_DEV float gelu_f(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+TTT_DEV float gelu_g(float x) {
+  return 0.5f * (1.f + erff(x * 0.70710678118654752f)) + x * 0.3989422804014327f * __expf(-0.5f * x * x);
+}
+TTT_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// GELU: a = gelu(z[:, j]); SwiGLU: a = silu(z[:, j]) * z[:, h + j]
+template <typename T>
+__global__ void act_fwd_kernel(const T* z, int h, int64_t ldz, int glu, T* a, int64_t lda) {
+  const int64_t r = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= h) return;
+  const T* zr = z + r * ldz;
+  float v;
+  if (glu) {
+    const float g = to_f32(zr[j]), u = to_f32(zr[h + j]);
+    v = g * sigm(g) * u;
+  } else {
+    v = gelu_f(to_f32(zr[j]));
+  }
+  a[r * lda + j] = from_f32<T>(v);
+}
+
+template <typename T>
+__global__ void act_bwd_kernel(const T* z, const float* da, int hcols, int64_t ldz, int64_t ldda,
+                               int64_t up_off, int glu, T* dz, int64_t lddz) {
+  const int64_t r = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= hcols) return;
+  const T* zr = z + r * ldz;
+  const float g = da[r * ldda + j];
+  T* o = dz + r * lddz;
+  if (glu) {
+    const float zg = to_f32(zr[j]), zu = to_f32(zr[up_off + j]);
+    const float sg = sigm(zg);
+    o[j] = from_f32<T>(g * zu * sg * (1.f + zg * (1.f - sg)));
+    o[up_off + j] = from_f32<T>(g * zg * sg);
+  } else {
+    o[j] = from_f32<T>(g * gelu_g(to_f32(zr[j])));
+  }
+}
+
+// delta[s][h][i] = sum_d dO * O for row s*S+i, head h
+template <typename T>
+__global__ void attn_delta_kernel(const T* o, const T* dout, int H, int hd, int64_t ld, int S,
+                                  float* delta) {
+  const int64_t r = blockIdx.x;
+  const int s = r / S, i = r % S;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int h = w; h < H; h += nw) {
+    float acc = 0.f;
+    for (int e = lane; e < hd; e += 64)
+      acc += to_f32(o[r * ld + h * hd + e]) * to_f32(dout[r * ld + h * hd + e]);
+    acc = wave_sum(acc);
+    if (lane == 0) delta[((int64_t)s * H + h) * S + i] = acc;
+  }
+}
+
+// -------------------------- cross entropy --------------------------------
+// One workgroup per row: max / argmax / sum-exp over V fp32 logits read
+// once into registers; loss = lse - z[label]; dz = (softmax - onehot)*scale.
+constexpr int CE_NT = 512;
+constexpr int CE_PER = 16;  // float4 per thread -> up to 32768 logits
+
+template <typename T>
+__global__ __launch_bounds__(CE_NT) void ce_kernel(CEArgs a) {
+  __shared__ float red[16];
+  __shared__ int redi[16];
+  const int64_t row = blockIdx.x;
+  const int s = row / a.S, i = row % a.S;
+  const int64_t pos = a.p0 + i;
+  const float* z = a.logits + row * a.V;
+  const int nv = a.V / 4;
+  float4 v[CE_PER];
+  float mx = -INFINITY;
+  int am = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < CE_PER; ++k) {
+    const int idx = k * CE_NT + threadIdx.x;
+    if (idx < nv) {
+      v[k] = reinterpret_cast<const float4*>(z)[idx];
+      const float e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (e[c] > mx) { mx = e[c]; am = idx * 4 + c; }
+    }
+  }
+  // block argmax (lowest index among maxima)
+  {
+    float m = mx;
+    int ai = am;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(m, o, 64);
+      const int oi = __shfl_xor(ai, o, 64);
+      if (om > m || (om == m && oi < ai)) { m = om; ai = oi; }
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { red[w] = m; redi[w] = ai; }
+    __syncthreads();
+    m = red[0];
+    ai = redi[0];
+    for (int k = 1; k < CE_NT / 64; ++k)
+      if (red[k] > m || (red[k] == m && redi[k] < ai)) { m = red[k]; ai = redi[k]; }
+    mx = m;
+    am = ai;
+    __syncthreads();
+  }
+  float se = 0.f;
+#pragma unroll
+  for (int k = 0; k < CE_PER; ++k) {
+    const int idx = k * CE_NT + threadIdx.x;
+    if (idx < nv) se += __expf(v[k].x - mx) + __expf(v[k].y - mx) + __expf(v[k].z - mx) + __expf(v[k].w - mx);
+  }
+  se = block_sum(se, red);
+  const float lse = mx + logf(se);
+  const bool has_label = pos + 1 < a.n_ids;
+  int label = -1;
+  if (has_label) {
+    label = a.ids[s * a.ids_seq_stride + pos + 1];
+    label = label < 0 ? 0 : (label >= a.V ? a.V - 1 : label);
+  }
+  if (threadIdx.x == 0) {
+    if (has_label && a.losses) {
+      const int64_t li = pos - a.loss_base;
+      if (li >= 0 && li < a.loss_n) a.losses[s * a.loss_ld + li] = lse - z[label];
+    }
+    if (pos == a.n_ids - 1 && a.last_lse) {
+      a.last_lse[s] = lse;
+      a.last_max[s] = mx;
+      a.last_arg[s] = am;
+    }
+  }
+  if (a.dz && has_label) {
+    T* dz = reinterpret_cast<T*>(a.dz) + row * a.V;
+    const float inv = 1.f / se;
+#pragma unroll
+    for (int k = 0; k < CE_PER; ++k) {
+      const int idx = k * CE_NT + threadIdx.x;
+      if (idx < nv) {
+        const float e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int col = idx * 4 + c;
+          float p = __expf(e[c] - mx) * inv;
+          if (col == label) p -= 1.f;
+          dz[col] = from_f32<T>(p * a.dz_scale);
+        }
+      }
+    }
+  } else if (a.dz) {
+    T* dz = reinterpret_cast<T*>(a.dz) + row * a.V;
+    for (int col = threadIdx.x; col < a.V; col += CE_NT) dz[col] = from_f32<T>(0.f);
+  }
+}
+
+// ------------------------------- copies ----------------------------------
+template <typename S, typename D>
+__global__ void transpose_kernel(const S* src, int rows, int cols, int64_t lds, D* dst, int64_t ldd) {
+  __shared__ float tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 32 x 8
+  for (int k = ty; k < 32; k += 8) {
+    const int r = r0 + k, c = c0 + tx;
+    tile[k][tx] = (r < rows && c < cols) ? to_f32(src[(int64_t)r * lds + c]) : 0.f;
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int c = c0 + k, r = r0 + tx;
+    if (r < rows && c < cols) dst[(int64_t)c * ldd + r] = from_f32<D>(tile[tx][k]);
+  }
+}
+
+__global__ void copy_rows_kernel(const float* src, int64_t sss, float* dst, int64_t dss, int S, int d) {
+  const int i = blockIdx.x, s = blockIdx.y;
+  const float* a = src + s * sss + (int64_t)i * d;
+  float* b = dst + s * dss + (int64_t)i * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) b[c] = a[c];
+}
+
+__global__ void fill_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void decode_emit_kernel(const int32_t* next, const float* lse, const float* mx, int B,
+                                   int32_t* ids, int64_t ids_ss, int64_t pos, int32_t* out,
+                                   int64_t out_ld, int64_t i, float* losses) {
+  const int s = threadIdx.x;
+  if (s >= B) return;
+  const int32_t t = next[s];
+  ids[s * ids_ss + pos] = t;
+  if (out) out[s * out_ld + i] = t;
+  if (losses) losses[s * out_ld + i] = lse[s] - mx[s];
+}
+
+}  // namespace
+
+#define DT_DISPATCH(dt, KERNEL_CALL_BF16, KERNEL_CALL_F32) \
+  do {                                                     \
+    if ((dt) == 1) { KERNEL_CALL_BF16; }                   \
+    else { KERNEL_CALL_F32; }                              \
+  } while (0)
+
+hipError_t embed_launch(const int32_t* ids, int64_t ids_ss, int64_t p0, int S, int B, const void* E,
+                        int d, int vocab, float* x, int dt, hipStream_t st) {
+  if (S <= 0 || B <= 0) return hipSuccess;
+  dim3 g(S, B);
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(embed_kernel<bf16>, g, dim3(NT), 0, st, ids, ids_ss, p0, S, cp<bf16>(E), d, vocab, x),
+      hipLaunchKernelGGL(embed_kernel<float>, g, dim3(NT), 0, st, ids, ids_ss, p0, S, cp<float>(E), d, vocab, x));
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, float eps, void* y,
+                              float* rstd, int dt, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 4) return hipErrorInvalidValue;
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, d, cp<bf16>(g), eps, mp<bf16>(y), rstd),
+      hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, d, cp<float>(g), eps, mp<float>(y), rstd));
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, const float* dn, int rows,
+                              int d, float* dres, void* dres_c, bool accumulate, int dt, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<bf16>(g), dn, d, dres, mp<bf16>(dres_c), accumulate),
+      hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<float>(g), dn, d, dres, mp<float>(dres_c), accumulate));
+  return hipGetLastError();
+}
+
+hipError_t rope_split_launch(const void* qkv, int rows, int S, int H, int hd, int64_t p0,
+                             const float2* tab, void* q, void* kc, void* vc, int cap,
+                             int64_t seq_stride, int dt, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(rope_split_kernel<bf16>, dim3(rows), dim3(NT), 0, st, cp<bf16>(qkv), S, H, hd, p0, tab, mp<bf16>(q), mp<bf16>(kc), mp<bf16>(vc), cap, seq_stride),
+      hipLaunchKernelGGL(rope_split_kernel<float>, dim3(rows), dim3(NT), 0, st, cp<float>(qkv), S, H, hd, p0, tab, mp<float>(q), mp<float>(kc), mp<float>(vc), cap, seq_stride));
+  return hipGetLastError();
+}
+
+hipError_t rope_bwd_pack_launch(const float* dq, const float* dk, const float* dv, int rows, int S, int H,
+                                int hd, int64_t p0, const float2* tab, void* dqkv, int dt, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(rope_bwd_pack_kernel<bf16>, dim3(rows), dim3(NT), 0, st, dq, dk, dv, S, H, hd, p0, tab, mp<bf16>(dqkv)),
+      hipLaunchKernelGGL(rope_bwd_pack_kernel<float>, dim3(rows), dim3(NT), 0, st, dq, dk, dv, S, H, hd, p0, tab, mp<float>(dqkv)));
+  return hipGetLastError();
+}
+
+hipError_t act_fwd_launch(const void* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
+                          int dt, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  dim3 g((h + NT - 1) / NT, rows);
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(act_fwd_kernel<bf16>, g, dim3(NT), 0, st, cp<bf16>(z), h, ldz, glu, mp<bf16>(a), lda),
+      hipLaunchKernelGGL(act_fwd_kernel<float>, g, dim3(NT), 0, st, cp<float>(z), h, ldz, glu, mp<float>(a), lda));
+  return hipGetLastError();
+}
+
+hipError_t act_bwd_launch(const void* z, const float* da, int rows, int hcols, int64_t ldz, int64_t ldda,
+                          int64_t up_off, int glu, void* dz, int64_t lddz, int dt, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  dim3 g((hcols + NT - 1) / NT, rows);
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(act_bwd_kernel<bf16>, g, dim3(NT), 0, st, cp<bf16>(z), da, hcols, ldz, ldda, up_off, glu, mp<bf16>(dz), lddz),
+      hipLaunchKernelGGL(act_bwd_kernel<float>, g, dim3(NT), 0, st, cp<float>(z), da, hcols, ldz, ldda, up_off, glu, mp<float>(dz), lddz));
+  return hipGetLastError();
+}
+
+hipError_t attn_delta_launch(const void* o, const void* dout, int rows, int H, int hd, int64_t ld, int S,
+                             float* delta, int dt, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(rows), dim3(NT), 0, st, cp<bf16>(o), cp<bf16>(dout), H, hd, ld, S, delta),
+      hipLaunchKernelGGL(attn_delta_kernel<float>, dim3(rows), dim3(NT), 0, st, cp<float>(o), cp<float>(dout), H, hd, ld, S, delta));
+  return hipGetLastError();
+}
+
+hipError_t ce_launch(const CEArgs& a, int dt, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.V % 4 || a.V > CE_NT * CE_PER * 4) return hipErrorInvalidValue;
+  DT_DISPATCH(dt,
+      hipLaunchKernelGGL(ce_kernel<bf16>, dim3(a.rows), dim3(CE_NT), 0, st, a),
+      hipLaunchKernelGGL(ce_kernel<float>, dim3(a.rows), dim3(CE_NT), 0, st, a));
+  return hipGetLastError();
+}
+
+hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, int sdt, void* dst,
+                            int64_t ldd, int ddt, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 g((cols + 31) / 32, (rows + 31) / 32);
+  if (sdt == 1 && ddt == 1)
+    hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd);
+  else if (sdt == 1 && ddt == 0)
+    hipLaunchKernelGGL((transpose_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd);
+  else if (sdt == 0 && ddt == 1)
+    hipLaunchKernelGGL((transpose_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd);
+  else
+    hipLaunchKernelGGL((transpose_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd);
+  return hipGetLastError();
+}
+
+hipError_t copy_rows_f32_launch(const float* src, int64_t sss, float* dst, int64_t dss, int S, int d, int B,
+                                hipStream_t st) {
+  if (S <= 0 || B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(S, B), dim3(NT), 0, st, src, sss, dst, dss, S, d);
+  return hipGetLastError();
+}
+
+hipError_t fill_f32_launch(float* p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + NT - 1) / NT;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(NT), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t decode_emit_launch(const int32_t* next, const float* lse, const float* mx, int B, int32_t* ids,
+                              int64_t ids_ss, int64_t pos, int32_t* out, int64_t out_ld, int64_t i,
+                              float* losses, hipStream_t st) {
+  hipLaunchKernelGGL(decode_emit_kernel, dim3(1), dim3(((B + 63) / 64) * 64), 0, st, next, lse, mx, B, ids,
+                     ids_ss, pos, out, out_ld, i, losses);
+  return hipGetLastError();
+}

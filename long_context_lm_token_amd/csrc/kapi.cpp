@@ -1,0 +1,109 @@
+// Single-kernel C entry points (include/ttt_kernels.h) for kernel-level tests.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ttt.h"
+#include "../../include/ttt_kernels.h"
+#include "kernels.h"
+
+namespace {
+thread_local std::string k_err;
+int kfail(int code, const char* msg) {
+  k_err = msg;
+  return code;
+}
+int kdone(hipError_t e) {
+  if (e == hipErrorInvalidValue) return kfail(TTT_EINVAL, "unsupported size or layout");
+  if (e != hipSuccess) return kfail(TTT_EHIP, hipGetErrorString(e));
+  return TTT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+const char* ttt_k_last_error(void) { return k_err.c_str(); }
+
+int ttt_k_gemm(int32_t dtype, int32_t layout, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K,
+               const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
+               int64_t ldc, int64_t sC, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
+               int64_t sW, float lr, int32_t batch, void* stream) {
+  if (layout < 0 || layout > 2 || epi < 0 || epi > 2 || M < 0 || N < 0 || K < 0 || batch < 1)
+    return kfail(TTT_EINVAL, "bad gemm arguments");
+  const int v = dtype == 1 ? 8 : 4;
+  if (N % v || (layout == 0 && K % v) || (layout == 1 && K % v) || (layout == 2 && M % v))
+    return kfail(TTT_EINVAL, "contiguous extents must be multiples of the vector width");
+  if (epi == 1 && !R) return kfail(TTT_EINVAL, "EPI_ADD needs R");
+  if (epi == 2 && !Wm) return kfail(TTT_EINVAL, "EPI_SGD needs Wm");
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = A; g.lda = lda; g.sA = sA; g.B = B; g.ldb = ldb; g.sB = sB; g.C = C; g.ldc = ldc; g.sC = sC;
+  g.M = M; g.N = N; g.K = K; g.R = R; g.ldr = ldr; g.sR = sR; g.Wm = Wm; g.ldw = ldw; g.sW = sW; g.lr = lr;
+  return kdone(gemm_launch(g, dtype, layout, epi, out_f32 != 0, batch, static_cast<hipStream_t>(stream)));
+}
+
+static AttnArgs mk(const void* q, const void* kc, const void* vc, int32_t cap, int32_t B, int32_t M, int32_t H,
+                   int32_t hd, int64_t pos0, int32_t window, float scale) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  const int64_t HD = (int64_t)H * hd;
+  a.q = q; a.ldq = HD; a.kc = kc; a.vc = vc; a.ldk = HD; a.seq_stride = (int64_t)cap * HD; a.cap = cap;
+  a.M = M; a.H = H; a.hd = hd; a.B = B; a.pos0 = pos0; a.window = window; a.scale = scale;
+  return a;
+}
+
+int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
+                   float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
+                   float scale, void* stream) {
+  if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
+    return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
+  AttnArgs a = mk(q, kc, vc, cap, B, M, H, hd, pos0, window, scale);
+  a.o = o; a.ldo = (int64_t)H * hd; a.lse = lse;
+  return kdone(attn_fwd_launch(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, const float* lse,
+                   const void* dout, const float* delta, float* dq, float* dk, float* dv, int32_t B, int32_t M,
+                   int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, void* stream) {
+  if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
+    return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
+  AttnArgs a = mk(q, kc, vc, cap, B, M, H, hd, pos0, window, scale);
+  const int64_t HD = (int64_t)H * hd;
+  a.lse = const_cast<float*>(lse); a.dout = dout; a.lddo = HD; a.delta = delta;
+  a.dq = dq; a.lddq = HD; a.dk = dk; a.dv = dv; a.lddk = HD;
+  return kdone(attn_bwd_launch(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int ttt_k_attn_delta(int32_t dtype, const void* o, const void* dout, int32_t B, int32_t M, int32_t H, int32_t hd,
+                     float* delta, void* stream) {
+  return kdone(attn_delta_launch(o, dout, B * M, H, hd, (int64_t)H * hd, M, delta, dtype,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int ttt_k_ce(int32_t dtype, const float* logits, int32_t rows, int32_t V, const int32_t* ids2, int32_t labelled,
+             float* losses, void* dz, float scale, float* lse, float* mx, int32_t* argmax, void* stream) {
+  // each row is a one-position "sequence" at position 0 whose label is ids2[r][1]
+  CEArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = logits; a.rows = rows; a.S = 1; a.V = V;
+  a.ids = ids2; a.ids_seq_stride = 2; a.p0 = 0; a.n_ids = labelled ? 2 : 1;
+  a.dz = labelled ? dz : nullptr; a.dz_scale = scale;
+  a.losses = labelled ? losses : nullptr; a.loss_base = 0; a.loss_ld = 1; a.loss_n = 1;
+  if (!labelled) { a.last_lse = lse; a.last_max = mx; a.last_arg = argmax; }
+  return kdone(ce_launch(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int ttt_k_rmsnorm_fwd(int32_t dtype, const float* x, int32_t rows, int32_t d, const void* g, float eps, void* y,
+                      float* rstd, void* stream) {
+  return kdone(rmsnorm_fwd_launch(x, rows, d, g, eps, y, rstd, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int ttt_k_rmsnorm_bwd(int32_t dtype, const float* x, const float* rstd, const void* g, const float* dn, int32_t rows,
+                      int32_t d, float* dres, int32_t accumulate, void* stream) {
+  return kdone(rmsnorm_bwd_launch(x, rstd, g, dn, rows, d, dres, nullptr, accumulate != 0, dtype,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Internal launchers of the gfx950 kernels (host side). All pointers are
+// device pointers; `dt` is 0 for fp32 storage, 1 for bf16 storage.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SGD = 2 };
+enum { GEMM_NN = 0 /* A K-contig, B K-contig */, GEMM_NT = 1 /* A K-contig, B N-contig */,
+       GEMM_TT = 2 /* A M-contig, B N-contig */ };
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;  // batch strides in elements
+  int M, N, K;
+  const float* R;      // EPI_ADD: C = R + acc (R may alias C)
+  int64_t ldr, sR;
+  float* Wm;           // EPI_SGD: Wm -= lr * acc; C (if non-null) = cast(Wm)
+  int64_t ldw, sW;
+  float lr;
+};
+
+hipError_t gemm_launch(const GemmArgs& p, int dt, int layout, int epi, bool out_f32, int batch,
+                       hipStream_t st);
+
+// Attention over a ring cache. Queries: rows [s*M + i] of q (row stride ldq,
+// head h at column h*hd), position pos0 + i. Keys/values of sequence s at
+// absolute position j live in kc/vc + s*seq_stride + (j % cap)*ldk + h*hd.
+struct AttnArgs {
+  const void* q; int64_t ldq;
+  const void* kc; const void* vc; int64_t ldk; int64_t seq_stride; int cap;
+  void* o; int64_t ldo;          // output rows like q
+  float* lse;                    // [B][H][M] natural-log sum exp of scaled scores
+  int M, H, hd, B;
+  int64_t pos0;
+  int window;
+  float scale;
+  // backward
+  const void* dout; int64_t lddo;   // dO rows like q
+  const float* delta;               // [B][H][M] rowsum(dO * O)
+  float* dq; int64_t lddq;          // fp32 rows like q
+  float* dk; float* dv; int64_t lddk;  // fp32 [B*M][H*hd] for keys at pos0..pos0+M-1
+};
+
+hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st);
+hipError_t attn_bwd_launch(const AttnArgs& a, int dt, hipStream_t st);
+
+// elementwise / row kernels
+hipError_t embed_launch(const int32_t* ids, int64_t ids_seq_stride, int64_t p0, int S, int B,
+                        const void* E, int d, int vocab, float* x, int dt, hipStream_t st);
+hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, float eps, void* y,
+                              float* rstd, int dt, hipStream_t st);
+hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, const float* dn,
+                              int rows, int d, float* dres, void* dres_c, bool accumulate, int dt,
+                              hipStream_t st);
+hipError_t rope_split_launch(const void* qkv, int rows, int S, int H, int hd, int64_t p0,
+                             const float2* rope_tab, void* q, void* kc, void* vc, int cap,
+                             int64_t seq_stride, int dt, hipStream_t st);
+hipError_t rope_bwd_pack_launch(const float* dq, const float* dk, const float* dv, int rows, int S,
+                                int H, int hd, int64_t p0, const float2* rope_tab, void* dqkv,
+                                int dt, hipStream_t st);
+hipError_t act_fwd_launch(const void* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
+                          int dt, hipStream_t st);
+hipError_t act_bwd_launch(const void* z, const float* da, int rows, int hcols, int64_t ldz,
+                          int64_t ldda, int64_t up_off, int glu, void* dz, int64_t lddz, int dt,
+                          hipStream_t st);
+hipError_t attn_delta_launch(const void* o, const void* dout, int rows, int H, int hd, int64_t ld,
+                             int S, float* delta, int dt, hipStream_t st);
+
+// Cross entropy over rows of fp32 logits. Row r = s*S + i is position p0+i of
+// sequence s; its label is ids[s][p0+i+1] when p0+i+1 < n_ids.
+struct CEArgs {
+  const float* logits; int rows, S, V;
+  const int32_t* ids; int64_t ids_seq_stride; int64_t p0, n_ids;
+  void* dz; float dz_scale;            // NULL: no gradient
+  float* losses; int64_t loss_base, loss_ld, loss_n;  // losses[s*loss_ld + (p - loss_base)]
+  float* last_lse; float* last_max; int32_t* last_arg;  // per sequence, row of position n_ids-1
+};
+hipError_t ce_launch(const CEArgs& a, int dt, hipStream_t st);
+
+hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, int src_dt, void* dst,
+                            int64_t ldd, int dst_dt, hipStream_t st);
+hipError_t copy_rows_f32_launch(const float* src, int64_t src_seq_stride, float* dst,
+                                int64_t dst_seq_stride, int S, int d, int B, hipStream_t st);
+hipError_t fill_f32_launch(float* p, int64_t n, float v, hipStream_t st);
+hipError_t decode_emit_launch(const int32_t* next, const float* lse, const float* mx, int B,
+                              int32_t* ids, int64_t ids_seq_stride, int64_t pos, int32_t* tokens_out,
+                              int64_t out_ld, int64_t i, float* losses, hipStream_t st);

@@ -1,0 +1,772 @@
+// Host runtime of the TTT-E2E library: model state, memory layout, the
+// prefill chunk scheduler and decode loop, weight upload and read-back.
+//
+// The inner loop (technical review "TTT-E2E: Learning a Long Context into
+// Weights", section 7, Algorithm 1; section 5, Eq. 9):
+//   for each chunk of b positions, in order: score every position with the
+//   current fast weights W (causal sliding-window attention), record the
+//   losses, differentiate their mean with respect to W, apply
+//   W <- W - eta * grad, keep only the K/V rows the window still needs.
+//
+// Layout (all device memory owned by the model):
+//   * frozen blocks 0 .. t0-1 and the attention of block t0 do not depend on
+//     W, so their forward runs over long spans of new positions at once
+//     ("span pass": GEMMs with M = batch * span); it ends by storing the
+//     residual after block t0's attention for every position (ystage);
+//   * the tail (MLP of block t0, blocks t0+1 .. L-1, final norm, head, CE)
+//     runs per chunk: forward at W_c, backward through the tail, and the SGD
+//     step fused into each trainable matrix's weight-gradient GEMM;
+//   * every block keeps a ring cache of K/V rows indexed by absolute position
+//     modulo its capacity (>= window + rows written per pass);
+//   * weights are stored transposed, [out][in], so the forward GEMM reads
+//     both operands K-contiguous; tail MLPs are stored per sequence with the
+//     trainable and static branches concatenated along the hidden dim (one
+//     GEMM per projection), the trainable rows/columns first; an fp32 master
+//     of the trainable part is kept for bf16 models.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ttt.h"
+#include "../../include/ttt_prof.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+struct Prof {
+  int cls = -1;  // kernel class being timed, -1 = off
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<double> work;
+};
+
+}  // namespace
+
+struct ttt_model {
+  ttt_config cfg;
+  int dt;             // 0 fp32, 1 bf16
+  size_t es;          // element size of the compute dtype
+  int L, t0, nt, H, hd, HD, d, V, h, ht, hs, hf, mg;  // mg = 2 for SwiGLU
+  int64_t maxpos;
+  int span;
+  int cap_s, cap_t;
+  float scale;
+
+  // frozen weights
+  void* embed = nullptr;
+  void* gfin = nullptr;
+  void* wout_t = nullptr;  // [V][d]
+  std::vector<void*> g_attn, g_mlp, wqkv_t, wo_t, wgu_t, wd_t;  // wgu_t/wd_t: frozen blocks only
+
+  // fast weights, per tail block j: [B][...] compute copies and fp32 masters
+  std::vector<void*> f_gu, f_d;      // [B][mg*hf][d], [B][d][hf]
+  std::vector<float*> m_gu, m_d;     // [B][mg*ht][d], [B][d][ht] (bf16 models only)
+  std::vector<void*> i_gu, i_d;      // initial copies (one sequence)
+  std::vector<float*> im_gu, im_d;
+
+  // caches and stream state
+  std::vector<void*> kc, vc;
+  int32_t* ids = nullptr;     // [B][maxpos]
+  float* ystage = nullptr;    // [B][maxpos][d]
+  float2* rope = nullptr;     // [maxpos][hd/2]
+  int64_t n_ids = 0;
+  int64_t chunk = 0;
+  float *last_lse = nullptr, *last_max = nullptr;
+  int32_t* last_arg = nullptr;
+
+  // span-pass workspace (rows = B * span)
+  float *sX = nullptr, *sR = nullptr, *sL = nullptr;
+  void *sU = nullptr, *sQKV = nullptr, *sQ = nullptr, *sO = nullptr, *sZ = nullptr, *sA = nullptr;
+
+  // tail workspace (rows = B * b), per tail block where saved for the backward
+  std::vector<float*> tx, ty, tr1, tr2, tlse;
+  std::vector<void*> tn, tq, to, tz, ta;
+  float *txL = nullptr, *trf = nullptr, *tlog = nullptr;
+  void *tf = nullptr, *tdz = nullptr, *tU = nullptr, *tQKV = nullptr;
+  float *dres = nullptr, *dn = nullptr, *dA = nullptr, *delta = nullptr, *dq = nullptr, *dk = nullptr,
+        *dv = nullptr;
+  void *dres_c = nullptr, *dZ = nullptr, *dO = nullptr, *dqkv = nullptr;
+
+  bool poisoned = false;
+  int64_t bytes = 0;
+  std::vector<void*> allocs;
+  Prof prof;
+};
+
+namespace {
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// ---------- allocation ----------
+struct Alloc {
+  ttt_model* m;
+  bool ok = true;
+  std::string why;
+  void* get(int64_t bytes) {
+    if (!ok) return nullptr;
+    bytes = round_up(std::max<int64_t>(bytes, 256), 256);
+    if (m->cfg.max_device_bytes > 0 && m->bytes + bytes > m->cfg.max_device_bytes) {
+      ok = false;
+      why = "allocation exceeds max_device_bytes";
+      return nullptr;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      ok = false;
+      why = "hipMalloc failed";
+      return nullptr;
+    }
+    m->allocs.push_back(p);
+    m->bytes += bytes;
+    return p;
+  }
+  float* f32(int64_t n) { return static_cast<float*>(get(n * 4)); }
+  void* el(int64_t n) { return get(n * (int64_t)m->es); }
+};
+
+// ---------- profiling of one kernel class ----------
+void prof_begin(ttt_model* m, int cls, hipStream_t st, hipEvent_t* e0) {
+  *e0 = nullptr;
+  if (m->prof.cls != cls) return;
+  Prof& p = m->prof;
+  if (p.used + 2 > p.pool.size()) {
+    for (int i = 0; i < 256; ++i) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      p.pool.push_back(e);
+    }
+  }
+  *e0 = p.pool[p.used];
+  (void)hipEventRecord(*e0, st);
+}
+void prof_end(ttt_model* m, int cls, hipStream_t st, hipEvent_t e0, double work) {
+  if (m->prof.cls != cls || !e0) return;
+  Prof& p = m->prof;
+  hipEvent_t e1 = p.pool[p.used + 1];
+  (void)hipEventRecord(e1, st);
+  p.used += 2;
+  p.work.push_back(work);
+}
+
+// ---------- thin wrappers that launch and check ----------
+struct Ctx {
+  ttt_model* m;
+  hipStream_t st;
+  hipError_t err = hipSuccess;
+  const char* where = "";
+  void chk(hipError_t e, const char* w) {
+    if (err == hipSuccess && e != hipSuccess) {
+      err = e;
+      where = w;
+    }
+  }
+  // C = A . B^T-ish per GemmArgs, optionally batched over sequences
+  void gemm(int layout, int epi, bool out_f32, const GemmArgs& a, int batch = 1) {
+    hipEvent_t e0;
+    prof_begin(m, TTT_PROF_GEMM, st, &e0);
+    chk(gemm_launch(a, m->dt, layout, epi, out_f32, batch, st), "gemm");
+    prof_end(m, TTT_PROF_GEMM, st, e0, 2.0 * a.M * a.N * (double)a.K * batch);
+  }
+};
+
+GemmArgs ga(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int M, int N,
+            int K) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K;
+  return g;
+}
+
+inline char* off(void* p, int64_t elems, size_t es) { return static_cast<char*>(p) + elems * (int64_t)es; }
+
+// ---------- the span pass: frozen prefix over positions [p0, p0+S) ----------
+void span_pass(Ctx& c, int64_t p0, int S) {
+  ttt_model* m = c.m;
+  const int B = m->cfg.batch, d = m->d, HD = m->HD, R = B * S;
+  const size_t es = m->es;
+  c.chk(embed_launch(m->ids, m->maxpos, p0, S, B, m->embed, d, m->V, m->sX, m->dt, c.st), "embed");
+  for (int l = 0; l <= m->t0; ++l) {
+    c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_attn[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
+    c.gemm(GEMM_NN, EPI_STORE, false, ga(m->sU, d, m->wqkv_t[l], d, m->sQKV, 3 * HD, R, 3 * HD, d));
+    c.chk(rope_split_launch(m->sQKV, R, S, m->H, m->hd, p0, m->cfg.rope ? m->rope : nullptr, m->sQ,
+                            m->kc[l], m->vc[l], m->cap_s, (int64_t)m->cap_s * HD, m->dt, c.st),
+          "rope");
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = m->sQ; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
+    a.seq_stride = (int64_t)m->cap_s * HD; a.cap = m->cap_s; a.o = m->sO; a.ldo = HD; a.lse = m->sL;
+    a.M = S; a.H = m->H; a.hd = m->hd; a.B = B; a.pos0 = p0; a.window = m->cfg.window; a.scale = m->scale;
+    {
+      hipEvent_t e0;
+      prof_begin(m, TTT_PROF_ATTN_FWD, c.st, &e0);
+      c.chk(attn_fwd_launch(a, m->dt, c.st), "attn_fwd");
+      double pairs = 0;
+      for (int i = 0; i < S; ++i) pairs += std::min<int64_t>(p0 + i + 1, m->cfg.window);
+      prof_end(m, TTT_PROF_ATTN_FWD, c.st, e0, 4.0 * m->hd * m->H * pairs * B);
+    }
+    GemmArgs g = ga(m->sO, HD, m->wo_t[l], HD, m->sX, d, R, d, HD);
+    g.R = m->sX; g.ldr = d;
+    c.gemm(GEMM_NN, EPI_ADD, true, g);
+    if (l == m->t0) break;
+    c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_mlp[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
+    const int h = m->h, zw = m->mg * h;
+    c.gemm(GEMM_NN, EPI_STORE, false, ga(m->sU, d, m->wgu_t[l], d, m->sZ, zw, R, zw, d));
+    c.chk(act_fwd_launch(m->sZ, R, h, zw, m->mg == 2, m->sA, h, m->dt, c.st), "act");
+    g = ga(m->sA, h, m->wd_t[l], h, m->sX, d, R, d, h);
+    g.R = m->sX; g.ldr = d;
+    c.gemm(GEMM_NN, EPI_ADD, true, g);
+  }
+  (void)es;
+  c.chk(copy_rows_f32_launch(m->sX, (int64_t)S * d, m->ystage + p0 * d, m->maxpos * d, S, d, B, c.st), "copy");
+}
+
+// ---------- the tail over positions [P0, P0+M) of every sequence ----------
+// bwd: run the backward and the SGD step (a complete chunk, M == b).
+void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_base, int64_t loss_n) {
+  ttt_model* m = c.m;
+  const int B = m->cfg.batch, d = m->d, HD = m->HD, R = B * M, V = m->V;
+  const int hf = m->hf, ht = m->ht, mg = m->mg, zw = mg * hf;
+  const size_t es = m->es;
+  const float eps = m->cfg.norm_eps;
+  const int64_t sgu = (int64_t)zw * d, sd = (int64_t)d * hf;        // per-seq fast strides
+  const int64_t smgu = (int64_t)mg * ht * d, smd = (int64_t)d * ht;  // per-seq master strides
+
+  c.chk(copy_rows_f32_launch(m->ystage + P0 * d, m->maxpos * d, m->tx[0], (int64_t)M * d, M, d, B, c.st), "copy");
+  for (int j = 0; j < m->nt; ++j) {
+    const int l = m->t0 + j;
+    float* y = m->tx[j];  // block t0: the residual after its attention
+    if (j >= 1) {
+      y = m->ty[j];
+      c.chk(rmsnorm_fwd_launch(m->tx[j], R, d, m->g_attn[l], eps, m->tU, m->tr1[j], m->dt, c.st), "norm");
+      c.gemm(GEMM_NN, EPI_STORE, false, ga(m->tU, d, m->wqkv_t[l], d, m->tQKV, 3 * HD, R, 3 * HD, d));
+      c.chk(rope_split_launch(m->tQKV, R, M, m->H, m->hd, P0, m->cfg.rope ? m->rope : nullptr, m->tq[j],
+                              m->kc[l], m->vc[l], m->cap_t, (int64_t)m->cap_t * HD, m->dt, c.st),
+            "rope");
+      AttnArgs a;
+      memset(&a, 0, sizeof(a));
+      a.q = m->tq[j]; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
+      a.seq_stride = (int64_t)m->cap_t * HD; a.cap = m->cap_t; a.o = m->to[j]; a.ldo = HD;
+      a.lse = m->tlse[j]; a.M = M; a.H = m->H; a.hd = m->hd; a.B = B; a.pos0 = P0;
+      a.window = m->cfg.window; a.scale = m->scale;
+      hipEvent_t e0;
+      prof_begin(m, TTT_PROF_ATTN_FWD, c.st, &e0);
+      c.chk(attn_fwd_launch(a, m->dt, c.st), "attn_fwd");
+      double pairs = 0;
+      for (int i = 0; i < M; ++i) pairs += std::min<int64_t>(P0 + i + 1, m->cfg.window);
+      prof_end(m, TTT_PROF_ATTN_FWD, c.st, e0, 4.0 * m->hd * m->H * pairs * B);
+      GemmArgs g = ga(m->to[j], HD, m->wo_t[l], HD, y, d, R, d, HD);
+      g.R = m->tx[j]; g.ldr = d;
+      c.gemm(GEMM_NN, EPI_ADD, true, g);
+    }
+    c.chk(rmsnorm_fwd_launch(y, R, d, m->g_mlp[l], eps, m->tn[j], m->tr2[j], m->dt, c.st), "norm");
+    GemmArgs g = ga(m->tn[j], d, m->f_gu[j], d, m->tz[j], zw, M, zw, d);
+    g.sA = (int64_t)M * d; g.sB = sgu; g.sC = (int64_t)M * zw;
+    c.gemm(GEMM_NN, EPI_STORE, false, g, B);
+    c.chk(act_fwd_launch(m->tz[j], R, hf, zw, mg == 2, m->ta[j], hf, m->dt, c.st), "act");
+    float* xo = (j + 1 < m->nt) ? m->tx[j + 1] : m->txL;
+    g = ga(m->ta[j], hf, m->f_d[j], hf, xo, d, M, d, hf);
+    g.sA = (int64_t)M * hf; g.sB = sd; g.sC = (int64_t)M * d;
+    g.R = y; g.ldr = d; g.sR = (int64_t)M * d;
+    c.gemm(GEMM_NN, EPI_ADD, true, g, B);
+  }
+  c.chk(rmsnorm_fwd_launch(m->txL, R, d, m->gfin, eps, m->tf, m->trf, m->dt, c.st), "norm");
+  c.gemm(GEMM_NN, EPI_STORE, true, ga(m->tf, d, m->wout_t, d, m->tlog, V, R, V, d));
+  {
+    CEArgs a;
+    memset(&a, 0, sizeof(a));
+    a.logits = m->tlog; a.rows = R; a.S = M; a.V = V;
+    a.ids = m->ids; a.ids_seq_stride = m->maxpos; a.p0 = P0; a.n_ids = m->n_ids;
+    a.dz = bwd ? m->tdz : nullptr; a.dz_scale = 1.f / m->cfg.mini_batch;
+    a.losses = losses; a.loss_base = loss_base; a.loss_ld = loss_n; a.loss_n = loss_n;
+    a.last_lse = m->last_lse; a.last_max = m->last_max; a.last_arg = m->last_arg;
+    hipEvent_t e0;
+    prof_begin(m, TTT_PROF_CE, c.st, &e0);
+    c.chk(ce_launch(a, m->dt, c.st), "ce");
+    prof_end(m, TTT_PROF_CE, c.st, e0, (double)R * V * (4.0 + (bwd ? es : 0)));
+  }
+  if (!bwd) return;
+
+  // ---------------- backward ----------------
+  c.gemm(GEMM_NT, EPI_STORE, true, ga(m->tdz, V, m->wout_t, d, m->dn, d, R, d, V));
+  c.chk(rmsnorm_bwd_launch(m->txL, m->trf, m->gfin, m->dn, R, d, m->dres, m->dres_c, false, m->dt, c.st),
+        "norm_bwd");
+  const bool master = m->dt == 1;
+  for (int j = m->nt - 1; j >= 0; --j) {
+    const int l = m->t0 + j;
+    const int hcols = j == 0 ? ht : hf;
+    // dA = dres . W_down (reads W_c before its update below)
+    GemmArgs g = ga(m->dres_c, d, m->f_d[j], hf, m->dA, hf, M, hcols, d);
+    g.sA = (int64_t)M * d; g.sB = sd; g.sC = (int64_t)M * hf;
+    c.gemm(GEMM_NT, EPI_STORE, true, g, B);
+    // W_down trainable columns: W^T[d][ht] -= eta * dres^T . A
+    g = ga(m->dres_c, d, m->ta[j], hf, master ? m->f_d[j] : nullptr, hf, d, ht, M);
+    g.sA = (int64_t)M * d; g.sB = (int64_t)M * hf; g.sC = sd;
+    g.Wm = master ? m->m_d[j] : static_cast<float*>(m->f_d[j]);
+    g.ldw = master ? ht : hf; g.sW = master ? smd : sd;
+    g.lr = m->cfg.lr;
+    c.gemm(GEMM_TT, EPI_SGD, false, g, B);
+    c.chk(act_bwd_launch(m->tz[j], m->dA, R, hcols, zw, hf, hf, mg == 2, m->dZ, zw, m->dt, c.st), "act_bwd");
+    if (j >= 1) {
+      g = ga(m->dZ, zw, m->f_gu[j], d, m->dn, d, M, d, zw);
+      g.sA = (int64_t)M * zw; g.sB = sgu; g.sC = (int64_t)M * d;
+      c.gemm(GEMM_NT, EPI_STORE, true, g, B);
+    }
+    // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ^T . n
+    for (int part = 0; part < mg; ++part) {
+      const int64_t zoff = (int64_t)part * hf;           // column of dZ / row of the compute copy
+      const int64_t moff = (int64_t)part * ht * d;       // row block of the master
+      g = ga(off(m->dZ, zoff, es), zw, m->tn[j], d, master ? off(m->f_gu[j], zoff * d, es) : nullptr, d, ht,
+             d, M);
+      g.sA = (int64_t)M * zw; g.sB = (int64_t)M * d; g.sC = sgu;
+      g.Wm = master ? m->m_gu[j] + moff : reinterpret_cast<float*>(off(m->f_gu[j], zoff * d, es));
+      g.ldw = d; g.sW = master ? smgu : sgu;
+      g.lr = m->cfg.lr;
+      c.gemm(GEMM_TT, EPI_SGD, false, g, B);
+    }
+    if (j == 0) break;
+    c.chk(rmsnorm_bwd_launch(m->ty[j], m->tr2[j], m->g_mlp[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
+                             c.st),
+          "norm_bwd");
+    // attention sublayer
+    c.gemm(GEMM_NT, EPI_STORE, false, ga(m->dres_c, d, m->wo_t[l], HD, m->dO, HD, R, HD, d));
+    c.chk(attn_delta_launch(m->to[j], m->dO, R, m->H, m->hd, HD, M, m->delta, m->dt, c.st), "delta");
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = m->tq[j]; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
+    a.seq_stride = (int64_t)m->cap_t * HD; a.cap = m->cap_t; a.o = m->to[j]; a.ldo = HD;
+    a.lse = m->tlse[j]; a.M = M; a.H = m->H; a.hd = m->hd; a.B = B; a.pos0 = P0;
+    a.window = m->cfg.window; a.scale = m->scale;
+    a.dout = m->dO; a.lddo = HD; a.delta = m->delta; a.dq = m->dq; a.lddq = HD;
+    a.dk = m->dk; a.dv = m->dv; a.lddk = HD;
+    {
+      hipEvent_t e0;
+      prof_begin(m, TTT_PROF_ATTN_BWD, c.st, &e0);
+      c.chk(attn_bwd_launch(a, m->dt, c.st), "attn_bwd");
+      double pairs = 0;
+      for (int i = 0; i < M; ++i) pairs += std::min<int64_t>(P0 + i + 1, m->cfg.window);
+      const double inchunk = (double)M * (M + 1) / 2.0;
+      prof_end(m, TTT_PROF_ATTN_BWD, c.st, e0, (4.0 * pairs + 4.0 * inchunk) * m->hd * m->H * B);
+    }
+    c.chk(rope_bwd_pack_launch(m->dq, m->dk, m->dv, R, M, m->H, m->hd, P0, m->cfg.rope ? m->rope : nullptr,
+                               m->dqkv, m->dt, c.st),
+          "rope_bwd");
+    c.gemm(GEMM_NT, EPI_STORE, true, ga(m->dqkv, 3 * HD, m->wqkv_t[l], d, m->dn, d, R, d, 3 * HD));
+    c.chk(rmsnorm_bwd_launch(m->tx[j], m->tr1[j], m->g_attn[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
+                             c.st),
+          "norm_bwd");
+  }
+}
+
+int finish(Ctx& c) {
+  if (c.err != hipSuccess) {
+    c.m->poisoned = true;
+    return fail(TTT_EHIP, std::string("HIP error in ") + c.where + ": " + hipGetErrorString(c.err));
+  }
+  return TTT_OK;
+}
+
+int validate(const ttt_config* c) {
+  if (!c) return fail(TTT_EINVAL, "cfg is NULL");
+  if (c->vocab < 1 || c->d_model < 1 || c->n_blocks < 1 || c->n_heads < 1 || c->head_dim < 1)
+    return fail(TTT_EINVAL, "sizes must be positive");
+  if (c->n_ttt_blocks < 1 || c->n_ttt_blocks > c->n_blocks) return fail(TTT_EINVAL, "n_ttt_blocks out of range");
+  if (c->window < c->mini_batch) return fail(TTT_EINVAL, "window k must be >= mini_batch b");
+  if (c->mini_batch < 1) return fail(TTT_EINVAL, "mini_batch must be >= 1");
+  if (c->dtype != TTT_FP32 && c->dtype != TTT_BF16) return fail(TTT_EINVAL, "dtype");
+  if (c->mlp_kind != TTT_GELU && c->mlp_kind != TTT_SWIGLU) return fail(TTT_EINVAL, "mlp_kind");
+  if (c->batch < 1 || c->max_positions < 2) return fail(TTT_EINVAL, "batch / max_positions");
+  const int hd = c->head_dim;
+  if (c->dtype == TTT_BF16 && hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return fail(TTT_EINVAL, "head_dim must be 16, 32, 64 or 128 for bf16");
+  if (c->dtype == TTT_FP32 && hd != 16 && hd != 32 && hd != 64)
+    return fail(TTT_EINVAL, "head_dim must be 16, 32 or 64 for fp32");
+  if (c->rope && (hd % 2)) return fail(TTT_EINVAL, "rope needs an even head_dim");
+  const int vec = 8;  // every contiguous extent a multiple of 8 elements
+  const int tail_h = c->ttt_hidden + c->static_hidden;
+  if (c->d_model % vec || (c->n_heads * hd) % vec || c->vocab % vec || c->mlp_hidden % vec ||
+      c->ttt_hidden % vec || c->static_hidden < 0 || tail_h % vec)
+    return fail(TTT_EINVAL, "d_model, n_heads*head_dim, vocab and hidden sizes must be multiples of 8");
+  if (c->vocab > 32768) return fail(TTT_EINVAL, "vocab above 32768 is not supported");
+  if (c->ttt_hidden < 8) return fail(TTT_EINVAL, "ttt_hidden must be >= 8");
+  return TTT_OK;
+}
+
+// transpose an [in][out] user matrix into rows [row0, row0+out) of a [.][in]
+// buffer (ld = in) or into columns (ldd given)
+hipError_t put_t(const void* src, int in, int out, void* dst, int64_t ldd, int sdt, int ddt, hipStream_t st) {
+  return transpose_launch(src, in, out, out, sdt, dst, ldd, ddt, st);
+}
+
+}  // namespace
+
+// ============================ C ABI ============================
+
+extern "C" {
+
+const char* ttt_last_error(void) { return g_err.c_str(); }
+
+int64_t ttt_stream_length(const ttt_model* m) { return m ? m->n_ids : 0; }
+int64_t ttt_device_bytes(const ttt_model* m) { return m ? m->bytes : 0; }
+
+void ttt_model_destroy(ttt_model* m) {
+  if (!m) return;
+  (void)hipDeviceSynchronize();
+  for (void* p : m->allocs) (void)hipFree(p);
+  for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
+  delete m;
+}
+
+static int reset_state(ttt_model* m, hipStream_t st) {
+  const int B = m->cfg.batch;
+  hipError_t e = hipSuccess;
+  auto ck = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+  for (int j = 0; j < m->nt; ++j) {
+    const int64_t ngu = (int64_t)m->mg * m->hf * m->d, nd = (int64_t)m->d * m->hf;
+    for (int s = 0; s < B; ++s) {
+      ck(hipMemcpyAsync(off(m->f_gu[j], s * ngu, m->es), m->i_gu[j], ngu * m->es, hipMemcpyDeviceToDevice, st));
+      ck(hipMemcpyAsync(off(m->f_d[j], s * nd, m->es), m->i_d[j], nd * m->es, hipMemcpyDeviceToDevice, st));
+      if (m->dt == 1) {
+        const int64_t mgu = (int64_t)m->mg * m->ht * m->d, md = (int64_t)m->d * m->ht;
+        ck(hipMemcpyAsync(m->m_gu[j] + s * mgu, m->im_gu[j], mgu * 4, hipMemcpyDeviceToDevice, st));
+        ck(hipMemcpyAsync(m->m_d[j] + s * md, m->im_d[j], md * 4, hipMemcpyDeviceToDevice, st));
+      }
+    }
+  }
+  // caches hold finite values (zeros): masked keys multiply by exactly zero
+  for (int l = 0; l < m->L; ++l) {
+    const int cap = l < m->t0 + 1 ? m->cap_s : m->cap_t;
+    const int64_t n = (int64_t)B * cap * m->HD;
+    ck(hipMemsetAsync(m->kc[l], 0, n * m->es, st));
+    ck(hipMemsetAsync(m->vc[l], 0, n * m->es, st));
+  }
+  ck(hipStreamSynchronize(st));
+  m->n_ids = 0;
+  m->chunk = 0;
+  if (e != hipSuccess) {
+    m->poisoned = true;
+    return fail(TTT_EHIP, std::string("reset: ") + hipGetErrorString(e));
+  }
+  m->poisoned = false;
+  return TTT_OK;
+}
+
+int ttt_reset(ttt_model* m, void* stream) {
+  if (!m) return fail(TTT_EINVAL, "model is NULL");
+  return reset_state(m, static_cast<hipStream_t>(stream));
+}
+
+int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, ttt_model** out) {
+  if (!out) return fail(TTT_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!w || !w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv ||
+      !w->wo || !w->mlp_norm || !w->w_up || !w->w_down)
+    return fail(TTT_EINVAL, "weights: NULL pointer");
+  const bool glu = cfg->mlp_kind == TTT_SWIGLU;
+  const int L = cfg->n_blocks, t0 = L - cfg->n_ttt_blocks;
+  for (int l = 0; l < L; ++l) {
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->w_up[l] ||
+        !w->w_down[l] || (glu && (!w->w_gate || !w->w_gate[l])))
+      return fail(TTT_EINVAL, "weights: NULL block pointer");
+    if (l >= t0 && cfg->static_hidden > 0 &&
+        (!w->s_up || !w->s_down || !w->s_up[l] || !w->s_down[l] || (glu && (!w->s_gate || !w->s_gate[l]))))
+      return fail(TTT_EINVAL, "weights: NULL static-branch pointer");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ttt_model* m = new ttt_model();
+  m->cfg = *cfg;
+  m->dt = cfg->dtype == TTT_BF16 ? 1 : 0;
+  m->es = m->dt ? 2 : 4;
+  m->L = L; m->t0 = t0; m->nt = cfg->n_ttt_blocks; m->H = cfg->n_heads; m->hd = cfg->head_dim;
+  m->HD = m->H * m->hd; m->d = cfg->d_model; m->V = cfg->vocab; m->h = cfg->mlp_hidden;
+  m->ht = cfg->ttt_hidden; m->hs = cfg->static_hidden; m->hf = m->ht + m->hs; m->mg = glu ? 2 : 1;
+  m->maxpos = cfg->max_positions;
+  const int b = cfg->mini_batch, B = cfg->batch;
+  int span = cfg->prefill_span > 0 ? cfg->prefill_span : 16384;
+  span = (int)std::min<int64_t>(span, m->maxpos);
+  span = std::max(span, 1);
+  m->span = span;
+  m->cap_s = (int)round_up(cfg->window + span, 64);
+  m->cap_t = (int)round_up(cfg->window + b, 64);
+  m->scale = 1.f / std::sqrt((float)m->hd);
+  const int d = m->d, HD = m->HD, V = m->V, hf = m->hf, ht = m->ht, hs = m->hs, mg = m->mg, h = m->h;
+  const size_t es = m->es;
+  Alloc A{m};
+
+  // frozen weights
+  m->embed = A.el((int64_t)V * d);
+  m->gfin = A.el(d);
+  m->wout_t = A.el((int64_t)V * d);
+  m->g_attn.resize(L); m->g_mlp.resize(L); m->wqkv_t.resize(L); m->wo_t.resize(L);
+  m->wgu_t.assign(L, nullptr); m->wd_t.assign(L, nullptr);
+  for (int l = 0; l < L; ++l) {
+    m->g_attn[l] = A.el(d);
+    m->g_mlp[l] = A.el(d);
+    m->wqkv_t[l] = A.el((int64_t)3 * HD * d);
+    m->wo_t[l] = A.el((int64_t)d * HD);
+    if (l < t0) {
+      m->wgu_t[l] = A.el((int64_t)mg * h * d);
+      m->wd_t[l] = A.el((int64_t)d * h);
+    }
+  }
+  m->f_gu.resize(m->nt); m->f_d.resize(m->nt); m->i_gu.resize(m->nt); m->i_d.resize(m->nt);
+  m->m_gu.assign(m->nt, nullptr); m->m_d.assign(m->nt, nullptr);
+  m->im_gu.assign(m->nt, nullptr); m->im_d.assign(m->nt, nullptr);
+  for (int j = 0; j < m->nt; ++j) {
+    m->f_gu[j] = A.el((int64_t)B * mg * hf * d);
+    m->f_d[j] = A.el((int64_t)B * d * hf);
+    m->i_gu[j] = A.el((int64_t)mg * hf * d);
+    m->i_d[j] = A.el((int64_t)d * hf);
+    if (m->dt == 1) {
+      m->m_gu[j] = A.f32((int64_t)B * mg * ht * d);
+      m->m_d[j] = A.f32((int64_t)B * d * ht);
+      m->im_gu[j] = A.f32((int64_t)mg * ht * d);
+      m->im_d[j] = A.f32((int64_t)d * ht);
+    }
+  }
+  m->kc.resize(L); m->vc.resize(L);
+  for (int l = 0; l < L; ++l) {
+    const int cap = l <= t0 ? m->cap_s : m->cap_t;
+    m->kc[l] = A.el((int64_t)B * cap * HD);
+    m->vc[l] = A.el((int64_t)B * cap * HD);
+  }
+  m->ids = static_cast<int32_t*>(A.get((int64_t)B * m->maxpos * 4));
+  m->ystage = A.f32((int64_t)B * m->maxpos * d);
+  if (cfg->rope) m->rope = static_cast<float2*>(A.get(m->maxpos * (m->hd / 2) * 8));
+  m->last_lse = A.f32(B); m->last_max = A.f32(B);
+  m->last_arg = static_cast<int32_t*>(A.get(B * 4));
+  // span workspace
+  const int64_t Rs = (int64_t)B * span;
+  m->sX = A.f32(Rs * d); m->sR = A.f32(Rs); m->sL = A.f32(Rs * m->H);
+  m->sU = A.el(Rs * d); m->sQKV = A.el(Rs * 3 * HD); m->sQ = A.el(Rs * HD); m->sO = A.el(Rs * HD);
+  m->sZ = A.el(Rs * mg * h); m->sA = A.el(Rs * h);
+  // tail workspace
+  const int64_t Rt = (int64_t)B * b;
+  const int nt = m->nt;
+  m->tx.resize(nt); m->ty.assign(nt, nullptr); m->tr1.assign(nt, nullptr); m->tr2.resize(nt);
+  m->tlse.assign(nt, nullptr); m->tn.resize(nt); m->tq.assign(nt, nullptr); m->to.assign(nt, nullptr);
+  m->tz.resize(nt); m->ta.resize(nt);
+  for (int j = 0; j < nt; ++j) {
+    m->tx[j] = A.f32(Rt * d);
+    if (j >= 1) {
+      m->ty[j] = A.f32(Rt * d); m->tr1[j] = A.f32(Rt); m->tlse[j] = A.f32(Rt * m->H);
+      m->tq[j] = A.el(Rt * HD); m->to[j] = A.el(Rt * HD);
+    }
+    m->tr2[j] = A.f32(Rt); m->tn[j] = A.el(Rt * d);
+    m->tz[j] = A.el(Rt * mg * hf); m->ta[j] = A.el(Rt * hf);
+  }
+  m->txL = A.f32(Rt * d); m->trf = A.f32(Rt); m->tlog = A.f32(Rt * V);
+  m->tf = A.el(Rt * d); m->tdz = A.el(Rt * V); m->tU = A.el(Rt * d); m->tQKV = A.el(Rt * 3 * HD);
+  m->dres = A.f32(Rt * d); m->dn = A.f32(Rt * d); m->dA = A.f32(Rt * hf); m->delta = A.f32(Rt * m->H);
+  m->dq = A.f32(Rt * HD); m->dk = A.f32(Rt * HD); m->dv = A.f32(Rt * HD);
+  m->dres_c = A.el(Rt * d); m->dZ = A.el(Rt * mg * hf); m->dO = A.el(Rt * HD); m->dqkv = A.el(Rt * 3 * HD);
+  if (!A.ok) {
+    rc = fail(TTT_ENOMEM, A.why);
+    ttt_model_destroy(m);
+    return rc;
+  }
+
+  // ---- upload: transpose [in][out] -> [out][in] ----
+  hipError_t e = hipSuccess;
+  auto ck = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+  const int dt = m->dt;
+  ck(hipMemcpyAsync(m->embed, w->embed, (int64_t)V * d * es, hipMemcpyDeviceToDevice, st));
+  ck(hipMemcpyAsync(m->gfin, w->final_norm, d * es, hipMemcpyDeviceToDevice, st));
+  ck(put_t(w->lm_head, d, V, m->wout_t, d, dt, dt, st));
+  for (int l = 0; l < L; ++l) {
+    ck(hipMemcpyAsync(m->g_attn[l], w->attn_norm[l], d * es, hipMemcpyDeviceToDevice, st));
+    ck(hipMemcpyAsync(m->g_mlp[l], w->mlp_norm[l], d * es, hipMemcpyDeviceToDevice, st));
+    ck(put_t(w->wq[l], d, HD, m->wqkv_t[l], d, dt, dt, st));
+    ck(put_t(w->wk[l], d, HD, off(m->wqkv_t[l], (int64_t)HD * d, es), d, dt, dt, st));
+    ck(put_t(w->wv[l], d, HD, off(m->wqkv_t[l], (int64_t)2 * HD * d, es), d, dt, dt, st));
+    ck(put_t(w->wo[l], HD, d, m->wo_t[l], HD, dt, dt, st));
+    if (l < t0) {
+      if (glu) {
+        ck(put_t(w->w_gate[l], d, h, m->wgu_t[l], d, dt, dt, st));
+        ck(put_t(w->w_up[l], d, h, off(m->wgu_t[l], (int64_t)h * d, es), d, dt, dt, st));
+      } else {
+        ck(put_t(w->w_up[l], d, h, m->wgu_t[l], d, dt, dt, st));
+      }
+      ck(put_t(w->w_down[l], h, d, m->wd_t[l], h, dt, dt, st));
+    } else {
+      const int j = l - t0;
+      // concatenated [gate_t | gate_s | up_t | up_s] rows (SwiGLU) or [up_t | up_s]
+      const void* tr[2] = {glu ? w->w_gate[l] : w->w_up[l], w->w_up[l]};
+      const void* sr[2] = {glu ? w->s_gate[l] : (hs ? w->s_up[l] : nullptr), hs ? w->s_up[l] : nullptr};
+      for (int part = 0; part < mg; ++part) {
+        void* base = off(m->i_gu[j], (int64_t)part * hf * d, es);
+        ck(put_t(tr[part], d, ht, base, d, dt, dt, st));
+        if (hs) ck(put_t(sr[part], d, hs, off(base, (int64_t)ht * d, es), d, dt, dt, st));
+        if (dt == 1) ck(put_t(tr[part], d, ht, m->im_gu[j] + (int64_t)part * ht * d, d, dt, 0, st));
+      }
+      ck(put_t(w->w_down[l], ht, d, m->i_d[j], hf, dt, dt, st));
+      if (hs) ck(put_t(w->s_down[l], hs, d, off(m->i_d[j], ht, es), hf, dt, dt, st));
+      if (dt == 1) ck(put_t(w->w_down[l], ht, d, m->im_d[j], ht, dt, 0, st));
+    }
+  }
+  if (cfg->rope) {
+    const int half = m->hd / 2;
+    // angles p * theta^(-2i/hd) in fp64 (an fp32 product loses ~1e-2 rad at p ~ 1e5)
+    std::vector<double> inv(half);
+    for (int i = 0; i < half; ++i) inv[i] = std::pow((double)cfg->rope_theta, -2.0 * i / m->hd);
+    std::vector<float2> tab((size_t)m->maxpos * half);
+    for (int64_t p = 0; p < m->maxpos; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double a = (double)p * inv[i];
+        tab[p * half + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+      }
+    ck(hipMemcpyAsync(m->rope, tab.data(), tab.size() * 8, hipMemcpyHostToDevice, st));
+    ck(hipStreamSynchronize(st));
+  }
+  ck(hipMemsetAsync(m->ids, 0, (int64_t)B * m->maxpos * 4, st));
+  if (e != hipSuccess) {
+    rc = fail(TTT_EHIP, std::string("create: ") + hipGetErrorString(e));
+    ttt_model_destroy(m);
+    return rc;
+  }
+  rc = reset_state(m, st);
+  if (rc) {
+    ttt_model_destroy(m);
+    return rc;
+  }
+  *out = m;
+  return TTT_OK;
+}
+
+int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t n, float* losses, void* stream) {
+  if (!m) return fail(TTT_EINVAL, "model is NULL");
+  if (m->poisoned) return fail(TTT_ESTATE, "model is poisoned by an earlier HIP error; call ttt_reset");
+  if (!tokens || n < 1) return fail(TTT_EINVAL, "tokens NULL or n < 1");
+  if (m->n_ids + n > m->maxpos) return fail(TTT_EINVAL, "stream would exceed max_positions");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Ctx c{m, st};
+  const int B = m->cfg.batch, b = m->cfg.mini_batch;
+  const int64_t n0 = m->n_ids;
+  c.chk(hipMemcpy2DAsync(m->ids + n0, m->maxpos * 4, tokens, n * 4, n * 4, B, hipMemcpyDeviceToDevice, st),
+        "copy ids");
+  if (losses && n0 == 0) {
+    // the first id of a stream has no predecessor
+    for (int s = 0; s < B; ++s) c.chk(fill_f32_launch(losses + s * n, 1, NAN, st), "fill");
+  }
+  // frozen prefix over the new positions
+  for (int64_t p = n0; p < n0 + n; p += m->span) {
+    const int S = (int)std::min<int64_t>(m->span, n0 + n - p);
+    span_pass(c, p, S);
+  }
+  m->n_ids = n0 + n;
+  const int64_t n_lab = m->n_ids - 1;
+  const int64_t loss_base = n0 - 1;
+  while ((m->chunk + 1) * b <= n_lab && c.err == hipSuccess) {
+    tail_pass(c, m->chunk * b, b, true, losses, loss_base, n);
+    ++m->chunk;
+  }
+  const int64_t p0 = m->chunk * b;
+  if (p0 < m->n_ids) tail_pass(c, p0, (int)(m->n_ids - p0), false, losses, loss_base, n);
+  return finish(c);
+}
+
+int ttt_decode(ttt_model* m, int64_t n_new, int32_t* tokens_out, float* losses, void* stream) {
+  if (!m) return fail(TTT_EINVAL, "model is NULL");
+  if (m->poisoned) return fail(TTT_ESTATE, "model is poisoned by an earlier HIP error; call ttt_reset");
+  if (m->n_ids < 1) return fail(TTT_ESTATE, "decode before any prefill");
+  if (n_new < 1) return fail(TTT_EINVAL, "n_new < 1");
+  if (m->n_ids + n_new > m->maxpos) return fail(TTT_EINVAL, "decode would exceed max_positions");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Ctx c{m, st};
+  const int B = m->cfg.batch, b = m->cfg.mini_batch;
+  for (int64_t i = 0; i < n_new && c.err == hipSuccess; ++i) {
+    const int64_t pos = m->n_ids;  // the new id lands here
+    c.chk(decode_emit_launch(m->last_arg, m->last_lse, m->last_max, B, m->ids, m->maxpos, pos, tokens_out, n_new,
+                             i, losses, st),
+          "emit");
+    m->n_ids = pos + 1;
+    const int64_t n_lab = m->n_ids - 1;
+    // a completed chunk is applied before the next position is computed
+    while ((m->chunk + 1) * b <= n_lab && c.err == hipSuccess) {
+      tail_pass(c, m->chunk * b, b, true, nullptr, 0, 0);
+      ++m->chunk;
+    }
+    // forward of the new position with the current W: its logits pick the next id
+    span_pass(c, pos, 1);
+    tail_pass(c, pos, 1, false, nullptr, 0, 0);
+  }
+  return finish(c);
+}
+
+int ttt_get_weights(const ttt_model* m, int32_t seq, int32_t block, int32_t mat, float* dst, void* stream) {
+  if (!m) return fail(TTT_EINVAL, "model is NULL");
+  if (!dst) return fail(TTT_EINVAL, "dst is NULL");
+  if (seq < 0 || seq >= m->cfg.batch) return fail(TTT_EINVAL, "seq out of range");
+  if (block < m->t0 || block >= m->L) return fail(TTT_EINVAL, "block is not a tail (fast-weight) block");
+  if (mat != TTT_UP && mat != TTT_GATE && mat != TTT_DOWN) return fail(TTT_EINVAL, "mat");
+  if (mat == TTT_GATE && m->mg != 2) return fail(TTT_EINVAL, "GATE needs a SwiGLU model");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int j = block - m->t0, d = m->d, ht = m->ht, hf = m->hf, mg = m->mg;
+  hipError_t e;
+  if (mat == TTT_DOWN) {
+    // stored [d][ht] -> user [ht][d]
+    if (m->dt == 1)
+      e = transpose_launch(m->m_d[j] + (int64_t)seq * d * ht, d, ht, ht, 0, dst, d, 0, st);
+    else
+      e = transpose_launch(off(m->f_d[j], (int64_t)seq * d * hf, 4), d, ht, hf, 0, dst, d, 0, st);
+  } else {
+    const int part = (mat == TTT_GATE || mg == 1) ? 0 : 1;
+    // stored rows [ht][d] -> user [d][ht]
+    if (m->dt == 1)
+      e = transpose_launch(m->m_gu[j] + (int64_t)seq * mg * ht * d + (int64_t)part * ht * d, ht, d, d, 0, dst, ht, 0,
+                           st);
+    else
+      e = transpose_launch(off(m->f_gu[j], (int64_t)seq * mg * hf * d + (int64_t)part * hf * d, 4), ht, d, d, 0, dst,
+                           ht, 0, st);
+  }
+  if (e != hipSuccess) return fail(TTT_EHIP, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+// ---- kernel timing (HIP events around each launch of one kernel class) ----
+int ttt_prof_begin(ttt_model* m, int32_t kernel_class) {
+  if (!m) return fail(TTT_EINVAL, "model is NULL");
+  if (kernel_class < TTT_PROF_GEMM || kernel_class > TTT_PROF_CE) return fail(TTT_EINVAL, "kernel_class");
+  m->prof.cls = kernel_class;
+  m->prof.used = 0;
+  m->prof.work.clear();
+  return TTT_OK;
+}
+
+int ttt_prof_end(ttt_model* m, double* total_ms, int64_t* launches, double* total_work) {
+  if (!m) return fail(TTT_EINVAL, "model is NULL");
+  Prof& p = m->prof;
+  double ms = 0;
+  for (size_t i = 0; i + 1 < p.used; i += 2) {
+    if (hipEventSynchronize(p.pool[i + 1]) != hipSuccess) return fail(TTT_EHIP, "event sync");
+    float t = 0;
+    if (hipEventElapsedTime(&t, p.pool[i], p.pool[i + 1]) != hipSuccess) return fail(TTT_EHIP, "event time");
+    ms += t;
+  }
+  double work = 0;
+  for (double x : p.work) work += x;
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = (int64_t)p.work.size();
+  if (total_work) *total_work = work;
+  p.cls = -1;
+  p.used = 0;
+  p.work.clear();
+  return TTT_OK;
+}
+
+}  // extern "C"

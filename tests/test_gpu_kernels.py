@@ -1,0 +1,225 @@
+"""Kernel-level parity: each HIP kernel of the hot path against the oracle's
+definition of the same operation (fp64, on the same bf16/fp32 inputs)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_lm_token_amd import binding as bd
+from oracle import ttt_oracle as O
+from tests.gpu_util import kdt, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [torch.float32, torch.bfloat16]
+
+
+def rnd(shape, seed, dtype, scale=1.0):
+    a = np.random.default_rng(seed).standard_normal(shape) * scale
+    t = torch.as_tensor(a, dtype=torch.float32).to(dtype)
+    return t.float().numpy().astype(np.float64), t.cuda()
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------- GEMM ---------------------------------------
+
+def run_gemm(dtype, layout, epi, M, N, K, batch=1, out_f32=True, lr=0.0):
+    lib = bd.load()
+    A, Ad = rnd((batch, M, K), 1, dtype)
+    Bm, Bd = rnd((batch, N, K), 2, dtype)
+    if layout >= 2:
+        Ad = Ad.transpose(1, 2).contiguous()
+    if layout >= 1:
+        Bd = Bd.transpose(1, 2).contiguous()
+    lda = K if layout < 2 else M
+    ldb = K if layout == 0 else N
+    ref = np.einsum("zmk,znk->zmn", A, Bm)
+    R = Rd = Wm = Wd = None
+    cdt = torch.float32 if (out_f32 or epi == 1) else dtype
+    C = torch.zeros((batch, M, N), dtype=cdt, device="cuda")
+    if epi == 1:
+        R, Rd = rnd((batch, M, N), 3, torch.float32)
+        ref = R + ref
+    if epi == 2:
+        Wm, Wd = rnd((batch, M, N), 4, torch.float32)
+        ref = Wm - lr * ref
+        C = torch.zeros((batch, M, N), dtype=dtype, device="cuda")
+    rc = lib.ttt_k_gemm(kdt(dtype), layout, epi, int(out_f32), M, N, K, bd.ptr(Ad), lda, M * K, bd.ptr(Bd),
+                        ldb, N * K, bd.ptr(C), N, M * N, bd.ptr(Rd), N, M * N, bd.ptr(Wd), N, M * N,
+                        lr, batch, bd.stream_ptr())
+    bd.check(rc, kernel=True)
+    sync()
+    return ref, C.float().cpu().numpy(), (Wd.cpu().numpy() if Wd is not None else None)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", [0, 1, 2])
+@pytest.mark.parametrize("shape", [(200, 136, 72), (1, 64, 96), (256, 256, 512), (72, 328, 1000)])
+def test_gemm_store(dtype, layout, shape):
+    M, N, K = shape
+    if layout == 2 and M % 8:
+        M = 8
+    ref, got, _ = run_gemm(dtype, layout, 0, M, N, K, batch=2)
+    tol = 1e-5 if dtype == torch.float32 else 1e-5
+    err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err < tol * math.sqrt(K) * 4, err
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gemm_store_compute_dtype(dtype):
+    ref, got, _ = run_gemm(dtype, 0, 0, 130, 64, 64, out_f32=False)
+    rt = 1e-6 if dtype == torch.float32 else 2 ** -8
+    np.testing.assert_allclose(got, ref, rtol=rt, atol=rt * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_gemm_residual_add(dtype, layout):
+    ref, got, _ = run_gemm(dtype, layout, 1, 150, 96, 200)
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gemm_sgd_epilogue(dtype):
+    """W <- W - lr * (A^T-contracted gradient); compute copy = cast(W)."""
+    lr = 0.37
+    ref, got_c, got_w = run_gemm(dtype, 2, 2, 96, 136, 300, batch=2, lr=lr)
+    np.testing.assert_allclose(got_w, ref, rtol=1e-5, atol=1e-4)
+    rt = 1e-7 if dtype == torch.float32 else 2 ** -8
+    np.testing.assert_allclose(got_c, got_w, rtol=rt, atol=0)
+
+
+# ---------------------------- attention --------------------------------------
+
+def attn_case(dtype, B, M, H, hd, pos0, window, seed=0):
+    cap = ((window + M + 63) // 64) * 64
+    HD = H * hd
+    lo = max(0, pos0 - window + 1)
+    npos = pos0 + M - lo
+    K, _ = rnd((B, npos, H, hd), seed + 1, dtype)
+    V, _ = rnd((B, npos, H, hd), seed + 2, dtype)
+    q, qd = rnd((B, M, H, hd), seed + 3, dtype)
+    kc = np.zeros((B, cap, HD))
+    vc = np.zeros((B, cap, HD))
+    for i, p in enumerate(range(lo, pos0 + M)):
+        kc[:, p % cap] = K[:, i].reshape(B, HD)
+        vc[:, p % cap] = V[:, i].reshape(B, HD)
+    kcd, vcd = to_dev(kc, dtype), to_dev(vc, dtype)
+    return dict(cap=cap, K=K, V=V, q=q, qd=qd.reshape(B * M, HD).contiguous(), kcd=kcd, vcd=vcd, lo=lo)
+
+
+@pytest.mark.parametrize("dtype,hd", [(torch.float32, 16), (torch.float32, 64), (torch.bfloat16, 64),
+                                      (torch.bfloat16, 128)])
+@pytest.mark.parametrize("B,M,H,pos0,window", [(1, 100, 2, 0, 128), (2, 64, 3, 300, 96),
+                                               (1, 200, 2, 1000, 64), (1, 1, 2, 517, 256)])
+def test_attention_fwd_bwd(dtype, hd, B, M, H, pos0, window):
+    lib = bd.load()
+    c = attn_case(dtype, B, M, H, hd, pos0, window)
+    HD = H * hd
+    scale = 1.0 / math.sqrt(hd)
+    o = torch.zeros((B * M, HD), dtype=dtype, device="cuda")
+    lse = torch.zeros((B, H, M), dtype=torch.float32, device="cuda")
+    bd.check(lib.ttt_k_attn_fwd(kdt(dtype), bd.ptr(c["qd"]), bd.ptr(c["kcd"]), bd.ptr(c["vcd"]), c["cap"],
+                                bd.ptr(o), bd.ptr(lse), B, M, H, hd, pos0, window, scale, bd.stream_ptr()),
+             kernel=True)
+    do, dod = rnd((B, M, H, hd), 9, dtype)
+    dod = dod.reshape(B * M, HD).contiguous()
+    delta = torch.zeros((B, H, M), dtype=torch.float32, device="cuda")
+    bd.check(lib.ttt_k_attn_delta(kdt(dtype), bd.ptr(o), bd.ptr(dod), B, M, H, hd, bd.ptr(delta),
+                                  bd.stream_ptr()), kernel=True)
+    dq = torch.zeros((B * M, HD), dtype=torch.float32, device="cuda")
+    dk = torch.zeros_like(dq)
+    dv = torch.zeros_like(dq)
+    bd.check(lib.ttt_k_attn_bwd(kdt(dtype), bd.ptr(c["qd"]), bd.ptr(c["kcd"]), bd.ptr(c["vcd"]), c["cap"],
+                                bd.ptr(lse), bd.ptr(dod), bd.ptr(delta), bd.ptr(dq), bd.ptr(dk), bd.ptr(dv),
+                                B, M, H, hd, pos0, window, scale, bd.stream_ptr()), kernel=True)
+    sync()
+    qpos = np.arange(pos0, pos0 + M)
+    kpos = np.arange(c["lo"], pos0 + M)
+    o_g = o.float().cpu().numpy().reshape(B, M, H, hd)
+    dq_g = dq.cpu().numpy().reshape(B, M, H, hd)
+    dk_g = dk.cpu().numpy().reshape(B, M, H, hd)
+    dv_g = dv.cpu().numpy().reshape(B, M, H, hd)
+    lse_g = lse.cpu().numpy()
+    bf = dtype == torch.bfloat16
+    for s in range(B):
+        o_r, P = O.window_attention(c["q"][s], c["K"][s], c["V"][s], qpos, kpos, window)
+        tol = 3e-2 if bf else 2e-5
+        np.testing.assert_allclose(o_g[s], o_r, atol=tol * np.abs(o_r).max(), rtol=0)
+        # lse of the scaled scores
+        sc = np.einsum("mhd,nhd->hmn", c["q"][s], c["K"][s]) * scale
+        sc = np.where(O.window_mask(qpos, kpos, window)[None], sc, -np.inf)
+        mx = sc.max(-1, keepdims=True)
+        lse_r = (np.log(np.exp(sc - mx).sum(-1, keepdims=True)) + mx)[..., 0]
+        np.testing.assert_allclose(lse_g[s], lse_r, atol=1e-2 if bf else 1e-5, rtol=0)
+        dq_r, dK_r, dV_r = O.window_attention_bwd(c["q"][s], c["K"][s], c["V"][s], P,
+                                                  do[s] if not bf else do[s])
+        # with bf16, O is rounded before it enters delta: compare with loose bounds
+        tb = 5e-2 if bf else 5e-5
+        np.testing.assert_allclose(dq_g[s], dq_r, atol=tb * np.abs(dq_r).max(), rtol=0)
+        np.testing.assert_allclose(dk_g[s], dK_r[-M:], atol=tb * np.abs(dK_r[-M:]).max(), rtol=0)
+        np.testing.assert_allclose(dv_g[s], dV_r[-M:], atol=tb * np.abs(dV_r[-M:]).max(), rtol=0)
+
+
+# ------------------------------ CE -------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("V", [256, 32000])
+def test_cross_entropy(dtype, V):
+    lib = bd.load()
+    rows = 37
+    z, zd = rnd((rows, V), 5, torch.float32, scale=3.0)
+    rng = np.random.default_rng(6)
+    labels = rng.integers(0, V, rows)
+    z[3, [10, 20]] = z[3].max() + 1.0          # planted tie: argmax must be 10
+    zd = to_dev(z, torch.float32)
+    ids2 = to_dev(np.stack([np.zeros(rows), labels], 1), torch.int32)
+    losses = torch.zeros(rows, device="cuda")
+    dz = torch.zeros((rows, V), dtype=dtype, device="cuda")
+    scale = 1.0 / 512
+    bd.check(lib.ttt_k_ce(kdt(dtype), bd.ptr(zd), rows, V, bd.ptr(ids2), 1, bd.ptr(losses), bd.ptr(dz), scale,
+                          None, None, None, bd.stream_ptr()), kernel=True)
+    lse = torch.zeros(rows, device="cuda")
+    mx = torch.zeros(rows, device="cuda")
+    am = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    bd.check(lib.ttt_k_ce(kdt(dtype), bd.ptr(zd), rows, V, bd.ptr(ids2), 0, None, None, scale, bd.ptr(lse),
+                          bd.ptr(mx), bd.ptr(am), bd.stream_ptr()), kernel=True)
+    sync()
+    l_r, g_r = O.cross_entropy(z, labels)
+    np.testing.assert_allclose(losses.cpu().numpy(), l_r, atol=1e-4, rtol=0)
+    rt = 1e-5 if dtype == torch.float32 else 2 ** -8
+    np.testing.assert_allclose(dz.float().cpu().numpy(), g_r * scale, rtol=rt, atol=rt * scale * 1e-3)
+    assert am.cpu().numpy()[3] == 10
+    np.testing.assert_array_equal(am.cpu().numpy(), np.argmax(z, axis=1))
+    np.testing.assert_allclose(lse.cpu().numpy(), l_r + z[np.arange(rows), labels], atol=1e-4)
+    np.testing.assert_allclose(mx.cpu().numpy(), z.max(1), atol=0)
+
+
+# ----------------------------- RMSNorm ---------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("d", [64, 3072])
+def test_rmsnorm(dtype, d):
+    lib = bd.load()
+    rows = 19
+    x, xd = rnd((rows, d), 7, torch.float32, scale=2.0)
+    g, gd = rnd((d,), 8, dtype)
+    y = torch.zeros((rows, d), dtype=dtype, device="cuda")
+    r = torch.zeros(rows, device="cuda")
+    bd.check(lib.ttt_k_rmsnorm_fwd(kdt(dtype), bd.ptr(xd), rows, d, bd.ptr(gd), 1e-6, bd.ptr(y), bd.ptr(r),
+                                   bd.stream_ptr()), kernel=True)
+    dn, dnd = rnd((rows, d), 9, torch.float32)
+    res0, res = rnd((rows, d), 10, torch.float32)
+    bd.check(lib.ttt_k_rmsnorm_bwd(kdt(dtype), bd.ptr(xd), bd.ptr(r), bd.ptr(gd), bd.ptr(dnd), rows, d, bd.ptr(res),
+                                   1, bd.stream_ptr()), kernel=True)
+    sync()
+    y_r, r_r = O.rmsnorm_fwd(x, g, 1e-6)
+    rt = 1e-5 if dtype == torch.float32 else 2 ** -8
+    np.testing.assert_allclose(y.float().cpu().numpy(), y_r, rtol=rt, atol=rt * np.abs(y_r).max() * 1e-2)
+    np.testing.assert_allclose(r.cpu().numpy(), r_r[:, 0], rtol=1e-5)
+    dx_r = O.rmsnorm_bwd(x, g, r_r, dn) + res0
+    np.testing.assert_allclose(res.cpu().numpy(), dx_r, rtol=1e-4, atol=1e-4)
