@@ -127,23 +127,25 @@ def window_attention(q, K, V, qpos, kpos, window):
     """
     hd = q.shape[-1]
     mask = window_mask(qpos, kpos, window)
-    s = np.einsum("mhd,nhd->hmn", q, K) / math.sqrt(hd)
+    qh, Kh, Vh = q.transpose(1, 0, 2), K.transpose(1, 0, 2), V.transpose(1, 0, 2)
+    s = (qh @ Kh.transpose(0, 2, 1)) / math.sqrt(hd)          # [H][m][n]
     s = np.where(mask[None], s, -np.inf)
     s = s - s.max(axis=-1, keepdims=True)
     e = np.exp(s)
     P = e / e.sum(axis=-1, keepdims=True)
-    o = np.einsum("hmn,nhd->mhd", P, V)
+    o = (P @ Vh).transpose(1, 0, 2)                           # [m][H][hd]
     return o, P
 
 
 def window_attention_bwd(q, K, V, P, do):
     """Gradients of window_attention given P: returns dq, dK, dV."""
     hd = q.shape[-1]
-    dP = np.einsum("mhd,nhd->hmn", do, V)
+    qh, Kh, Vh, doh = (a.transpose(1, 0, 2) for a in (q, K, V, do))
+    dP = doh @ Vh.transpose(0, 2, 1)                               # [H][m][n]
     dS = P * (dP - np.sum(dP * P, axis=-1, keepdims=True))
-    dq = np.einsum("hmn,nhd->mhd", dS, K) / math.sqrt(hd)
-    dK = np.einsum("hmn,mhd->nhd", dS, q) / math.sqrt(hd)
-    dV = np.einsum("hmn,mhd->nhd", P, do)
+    dq = (dS @ Kh).transpose(1, 0, 2) / math.sqrt(hd)
+    dK = (dS.transpose(0, 2, 1) @ qh).transpose(1, 0, 2) / math.sqrt(hd)
+    dV = (P.transpose(0, 2, 1) @ doh).transpose(1, 0, 2)
     return dq, dK, dV
 
 
@@ -171,8 +173,9 @@ def sgd_step(w, g, lr):
 class Oracle:
     """One sequence's TTT-E2E state: fast weights, attention cache, stream."""
 
-    def __init__(self, cfg: dict, weights: dict, cache_fp64: bool | None = None):
+    def __init__(self, cfg: dict, weights: dict, cache_fp64: bool | None = None, progress=None):
         self.cfg = cfg
+        self.progress = progress        # optional callable(str), called once per block
         self.w32 = weights              # fp32 (bf16-exact) numpy arrays, [in][out]
         total = sum(v.size for v in weights.values())
         self._keep64 = (total < 300_000_000) if cache_fp64 is None else cache_fp64
@@ -256,6 +259,8 @@ class Oracle:
             if rec is not None:
                 tape["blocks"][l] = rec
             x = xn
+            if self.progress:
+                self.progress(f"oracle forward block {l} positions {p0}..{p0 + m - 1}")
         f, rf = rmsnorm_fwd(x, self.p("final_norm"), eps)
         z = f @ self.p("lm_head")
         tape.update(xL=x, rf=rf, f=f)
@@ -332,6 +337,8 @@ class Oracle:
             du = (dq.reshape(m, -1) @ self.p(pre + "wq").T + dk.reshape(m, -1) @ self.p(pre + "wk").T
                   + dv.reshape(m, -1) @ self.p(pre + "wv").T)
             dx = dy + rmsnorm_bwd(rec["x"], self.p(pre + "attn_norm"), rec["r1"], du)
+            if self.progress:
+                self.progress(f"oracle backward block {l}")
         return G
 
     # ---- one chunk: score at W_c, gradient, update ----
