@@ -175,10 +175,15 @@ struct Ctx {
   }
   // C = A . B^T-ish per GemmArgs, optionally batched over sequences
   void gemm(int layout, int epi, bool out_f32, const GemmArgs& a, int batch = 1) {
+    // class of this launch for the timing hooks: every GEMM, or the forward
+    // (K-contiguous operands, plain store in the compute dtype) instantiation
+    int cls = TTT_PROF_GEMM;
+    if (m->prof.cls == TTT_PROF_GEMM_FWD)
+      cls = (layout == GEMM_NN && epi == EPI_STORE && !out_f32) ? TTT_PROF_GEMM_FWD : -2;
     hipEvent_t e0;
-    prof_begin(m, TTT_PROF_GEMM, st, &e0);
+    prof_begin(m, cls, st, &e0);
     chk(gemm_launch(a, m->dt, layout, epi, out_f32, batch, st), "gemm");
-    prof_end(m, TTT_PROF_GEMM, st, e0, 2.0 * a.M * a.N * (double)a.K * batch);
+    prof_end(m, cls, st, e0, 2.0 * a.M * a.N * (double)a.K * batch);
   }
 };
 
@@ -741,7 +746,7 @@ int ttt_get_weights(const ttt_model* m, int32_t seq, int32_t block, int32_t mat,
 // ---- kernel timing (HIP events around each launch of one kernel class) ----
 int ttt_prof_begin(ttt_model* m, int32_t kernel_class) {
   if (!m) return fail(TTT_EINVAL, "model is NULL");
-  if (kernel_class < TTT_PROF_GEMM || kernel_class > TTT_PROF_CE) return fail(TTT_EINVAL, "kernel_class");
+  if (kernel_class < TTT_PROF_GEMM || kernel_class > TTT_PROF_GEMM_FWD) return fail(TTT_EINVAL, "kernel_class");
   m->prof.cls = kernel_class;
   m->prof.used = 0;
   m->prof.work.clear();
