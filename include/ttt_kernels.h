@@ -18,17 +18,23 @@ extern "C" {
 /* Thread-local message of the last failed ttt_k_* call ("" if none). */
 const char* ttt_k_last_error(void);
 
-/* MFMA GEMM, C[m][n] (epi)= sum_k A(m,k) B(n,k), batched over `batch` with
- * element strides sA, sB, sC (and sR / sW for the epilogue operands).
- * layout 0: A[m*lda+k], B[n*ldb+k]; 1: A[m*lda+k], B[k*ldb+n];
- *        2: A[k*lda+m], B[k*ldb+n]. Contiguous extents must be multiples of 8.
+/* MFMA GEMM, C[m][n] (epi)= sum_k A[m*lda+k] B[n*ldb+k] (both operands
+ * K-contiguous; K a multiple of 8 for bf16, 4 for fp32), batched over
+ * `batch` with element strides sA, sB, sC (sC2, sR, sW for the epilogue).
  * epi 0: C = acc (fp32 if out_f32 else dtype); 1: C = R + acc (fp32);
- *     2: Wm -= lr * acc (fp32 master, ld ldw), then C = cast(Wm) if C != NULL
- *        (the inner SGD step, technical review section 5, Eq. 9). */
-int ttt_k_gemm(int32_t dtype, int32_t layout, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K,
-               const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
-               int64_t ldc, int64_t sC, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
-               int64_t sW, float lr, int32_t batch, void* stream);
+ *     2: Wm -= lr * acc (fp32 master, ld ldw), then C[m][n] = cast(Wm) if C
+ *        and C2[n*ldc2+m] = cast(Wm) if C2 (the inner SGD step, technical
+ *        review section 5, Eq. 9, with both compute layouts refreshed).
+ * ws: fp32 workspace of ws_elems elements for split-K partial sums (may be
+ *     NULL; the kernel then runs without splitting K). */
+int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* A,
+               int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc, int64_t sC,
+               void* C2, int64_t ldc2, int64_t sC2, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
+               int64_t sW, float lr, int32_t batch, float* ws, int64_t ws_elems, void* stream);
+
+/* Test hook: force the GEMM block tile (0 automatic, 1 = 256x256, 3 = 128x128
+ * with split-K when the tile count is low). Process-wide. */
+void ttt_k_gemm_tile(int32_t cfg);
 
 /* Sliding-window attention forward over a ring cache (query p sees keys
  * p-window < j <= p; technical review section 2.1 Eq. 1 and section 5).

@@ -75,9 +75,11 @@ def load():
     lib.ttt_prof_begin.argtypes = [c_vp, c_i32]
     lib.ttt_prof_end.argtypes = [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64),
                                  ctypes.POINTER(ctypes.c_double)]
-    lib.ttt_k_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_i64, c_i64, c_vp,
-                               c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
-                               c_f32, c_i32, c_vp]
+    lib.ttt_k_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
+                               c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
+                               c_f32, c_i32, c_vp, c_i64, c_vp]
+    lib.ttt_k_gemm_tile.argtypes = [c_i32]
+    lib.ttt_k_gemm_tile.restype = None
     lib.ttt_k_attn_fwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_f32, c_vp]
     lib.ttt_k_attn_bwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,

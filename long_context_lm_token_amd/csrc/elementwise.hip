@@ -302,16 +302,19 @@ __global__ __launch_bounds__(CE_NT) void ce_kernel(CEArgs a) {
 
 // ------------------------------- copies ----------------------------------
 template <typename S, typename D>
-__global__ void transpose_kernel(const S* src, int rows, int cols, int64_t lds, D* dst, int64_t ldd) {
-  __shared__ float tile[32][33];
-  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 32 x 8
-  for (int k = ty; k < 32; k += 8) {
+__global__ void transpose_kernel(const S* src, int rows, int cols, int64_t lds, D* dst, int64_t ldd, int64_t s_src,
+                                 int64_t s_dst) {
+  __shared__ float tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  src += blockIdx.z * s_src;
+  dst += blockIdx.z * s_dst;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 256 threads: 64 x 4
+  for (int k = ty; k < 64; k += 4) {
     const int r = r0 + k, c = c0 + tx;
     tile[k][tx] = (r < rows && c < cols) ? to_f32(src[(int64_t)r * lds + c]) : 0.f;
   }
   __syncthreads();
-  for (int k = ty; k < 32; k += 8) {
+  for (int k = ty; k < 64; k += 4) {
     const int c = c0 + k, r = r0 + tx;
     if (r < rows && c < cols) dst[(int64_t)c * ldd + r] = from_f32<D>(tile[tx][k]);
   }
@@ -434,18 +437,18 @@ hipError_t ce_launch(const CEArgs& a, int dt, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, int sdt, void* dst,
-                            int64_t ldd, int ddt, hipStream_t st) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  dim3 g((cols + 31) / 32, (rows + 31) / 32);
+hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, int sdt, void* dst, int64_t ldd,
+                            int ddt, hipStream_t st, int batch, int64_t s_src, int64_t s_dst) {
+  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
+  dim3 g((cols + 63) / 64, (rows + 63) / 64, batch);
   if (sdt == 1 && ddt == 1)
-    hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd);
+    hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
   else if (sdt == 1 && ddt == 0)
-    hipLaunchKernelGGL((transpose_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd);
+    hipLaunchKernelGGL((transpose_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
   else if (sdt == 0 && ddt == 1)
-    hipLaunchKernelGGL((transpose_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd);
+    hipLaunchKernelGGL((transpose_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
   else
-    hipLaunchKernelGGL((transpose_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd);
+    hipLaunchKernelGGL((transpose_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
   return hipGetLastError();
 }
 

@@ -1,25 +1,31 @@
-// MFMA GEMM for gfx950: C[m][n] (epilogue)= sum_k A(m,k) * B(n,k).
+// MFMA GEMM for gfx950: C[m][n] (epilogue)= sum_k A[m][k] * B[n][k].
 //
-// A(m,k) is read from a row-major array either K-contiguous (A[m*lda+k]) or
-// M-contiguous (A[k*lda+m]); B(n,k) likewise (B[n*ldb+k] or B[k*ldb+n]).
-// This covers the three products of a linear layer y = x W:
-//   forward   y  = x  . W      (A K-contiguous, B = W^T stored [out][in])
-//   input grad dx = dy . W^T   (A K-contiguous, B = the same [out][in] array
-//                               read N-contiguous)
-//   weight grad dW^T = dy^T . x (A and B both read M/N-contiguous; the
-//                               reduction runs over the tokens of a chunk)
-// and the weight-grad epilogue applies the inner SGD step
-// W <- W - eta * G directly to the fp32 master (review "TTT-E2E: Learning a
-// Long Context into Weights", section 5, Eq. 9), refreshing the compute copy.
+// Both operands are read K-contiguous (row-major [rows][ld]). Every product
+// of a linear layer y = x W is brought to this form by the data layout:
+//   forward      y  = x . W      A = x [t][in],    B = W stored [out][in]
+//   input grad   dx = dy . W^T   A = dy [t][out],  B = W stored [in][out]
+//   weight grad  dW^T = dy^T . x A = dy^T [out][t], B = x^T [in][t]
+// (the weight grad reduces over the tokens of a chunk). The weight-grad
+// epilogue applies the inner SGD step W <- W - eta * G to the fp32 master
+// and refreshes the compute copies (technical review "TTT-E2E: Learning a
+// Long Context into Weights", section 5, Eq. 9).
 //
-// Tiling: 256 threads = 4 wave64s, block tile 128x128, each wave 64x64 as
-// 2x2 MFMA 32x32 tiles (bf16: v_mfma_f32_32x32x16_bf16, fp32:
-// v_mfma_f32_32x32x2f32), fp32 accumulation. Operands are staged through LDS
-// K-contiguous with a padded row stride (conflict-free 16-byte fragment
-// reads); M/N-contiguous operands are transposed in registers on the way in.
-// Two LDS stages; global loads of tile k+1 are in flight during the MFMAs of
-// tile k. Block ids are remapped so that each XCD gets a contiguous run of
-// tiles in grouped-M order (L2 reuse of A rows and B columns).
+// Tiling: block tile BM x BN computed by a WGM x WGN grid of wave64s, each
+// owning a (BM/WGM) x (BN/WGN) tile of 32x32 MFMA tiles (bf16:
+// v_mfma_f32_32x32x16_bf16, fp32: v_mfma_f32_32x32x2f32), fp32 accumulation.
+// Configurations: 256x256 with 8 waves (128x64 wave tiles, two waves per
+// SIMD) for large M*N, 128x128 with 4 waves (64x64 wave tiles) otherwise. Larger wave tiles reuse each LDS
+// fragment for more MFMAs (LDS bandwidth is the limit of 64x64 wave tiles). Operands are
+// staged global -> registers -> LDS (two stages, loads of tile k+1 in flight
+// during the MFMAs of tile k) with a padded row stride that keeps the 16-byte
+// fragment reads conflict-free. Block ids are remapped so that each XCD runs
+// a contiguous run of tiles in grouped-M order (L2 reuse).
+//
+// Split-K: with `splits` > 1 every block handles a K range and writes fp32
+// partial tiles to a workspace; gemm_reduce sums them in a fixed order and
+// applies the epilogue (deterministic, no atomics).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,17 +35,14 @@ template <typename T> struct GT;
 template <> struct GT<bf16> {
   static constexpr int BK = 64, KS = 16, VEC = 8, PAD = 8;
   typedef bf16x8 frag;
+  typedef bf16x8 vec;
 };
 template <> struct GT<float> {
   static constexpr int BK = 16, KS = 2, VEC = 4, PAD = 2;
   typedef float frag;
+  typedef f32x4 vec;
 };
 
-constexpr int BM = 128, BN = 128, NT = 256;
-
-template <typename T> struct Vec;
-template <> struct Vec<bf16> { typedef bf16x8 type; };
-template <> struct Vec<float> { typedef f32x4 type; };
 
 TTT_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -48,72 +51,35 @@ TTT_DEV f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Stage one 128 x BK operand tile into registers.
-// KMAJ: array [rows][ld] with k contiguous; else array [k][ld] with rows contiguous.
-template <typename T, bool KMAJ>
+// One ROWS x BK operand tile, K-contiguous in global memory and in LDS,
+// loaded by NT threads.
+template <typename T, int ROWS, int NT>
 struct TileLoader {
   typedef GT<T> G;
-  typedef typename Vec<T>::type V;
-  static constexpr int NV = BM * G::BK / (NT * G::VEC);  // vectors per thread
+  typedef typename G::vec V;
+  static constexpr int VPR = G::BK / G::VEC;          // vectors per row
+  static constexpr int NV = ROWS * VPR / NT;          // vectors per thread
   V v[NV];
 
-  TTT_DEV void load(const T* __restrict__ base, int64_t ld, int row0, int nrows, int k0, int K) {
-    const int t = threadIdx.x;
-    if constexpr (KMAJ) {
-      constexpr int VPR = G::BK / G::VEC;  // vectors per row
+  TTT_DEV void load(const T* __restrict__ base, int64_t ld, int row0, int nrows, int k0, int k1) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int vi = i * NT + t;
-        const int r = vi / VPR, kc = (vi % VPR) * G::VEC;
-        const int gr = row0 + r, gk = k0 + kc;
-        if (gr < nrows && gk < K)
-          v[i] = *reinterpret_cast<const V*>(base + (int64_t)gr * ld + gk);
-        else
-          v[i] = V{};
-      }
-    } else {
-      constexpr int TPR = BM / G::VEC;  // threads per k-row group
-      const int kb = t / TPR, mb = t % TPR;
-      const int gr = row0 + mb * G::VEC;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int gk = k0 + kb * NV + j;
-        if (gk < K && gr < nrows)
-          v[j] = *reinterpret_cast<const V*>(base + (int64_t)gk * ld + gr);
-        else
-          v[j] = V{};
-      }
+    for (int i = 0; i < NV; ++i) {
+      const int vi = i * NT + threadIdx.x;
+      const int r = vi / VPR, kc = (vi % VPR) * G::VEC;
+      const int gr = row0 + r, gk = k0 + kc;
+      if (gr < nrows && gk < k1)
+        v[i] = *reinterpret_cast<const V*>(base + (int64_t)gr * ld + gk);
+      else
+        v[i] = V{};
     }
   }
-
-  // write into LDS tile s[BM][BK+PAD] (k contiguous)
-  TTT_DEV void store(T* s) {
+  TTT_DEV void store(T* s) const {
     constexpr int LS = G::BK + G::PAD;
-    const int t = threadIdx.x;
-    if constexpr (KMAJ) {
-      constexpr int VPR = G::BK / G::VEC;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int vi = i * NT + t;
-        const int r = vi / VPR, kc = (vi % VPR) * G::VEC;
-        *reinterpret_cast<V*>(s + r * LS + kc) = v[i];
-      }
-    } else {
-      constexpr int TPR = BM / G::VEC;
-      const int kb = t / TPR, mb = t % TPR;
-#pragma unroll
-      for (int e = 0; e < G::VEC; ++e) {
-        T* dst = s + (mb * G::VEC + e) * LS + kb * NV;
-        if constexpr (NV == 4) {
-          bf16x4 w;
-          w[0] = v[0][e]; w[1] = v[1][e]; w[2] = v[2][e]; w[3] = v[3][e];
-          *reinterpret_cast<bf16x4*>(dst) = w;
-        } else {
-          float2 w;
-          w.x = v[0][e]; w.y = v[1][e];
-          *reinterpret_cast<float2*>(dst) = w;
-        }
-      }
+    for (int i = 0; i < NV; ++i) {
+      const int vi = i * NT + threadIdx.x;
+      const int r = vi / VPR, kc = (vi % VPR) * G::VEC;
+      *reinterpret_cast<V*>(s + r * LS + kc) = v[i];
     }
   }
 };
@@ -124,69 +90,103 @@ TTT_DEV typename GT<T>::frag read_frag(const T* s, int row, int k) {
   return *reinterpret_cast<const typename GT<T>::frag*>(s + row * LS + k);
 }
 
-template <typename T, bool AK, bool BKM, int EPI, typename OutT>
-__global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
-  typedef GT<T> G;
-  constexpr int LS = G::BK + G::PAD;
-  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * LS];
-
-  // ---- tile schedule: XCD-contiguous remap, then grouped-M order ----
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+// tile index -> (tm, tn): XCD-contiguous remap, then grouped-M order
+TTT_DEV void tile_coords(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
   const int ntiles = tiles_m * tiles_n;
-  int t = blockIdx.x;
   if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
   constexpr int GROUP = 8;
   const int group = t / (GROUP * tiles_n);
   const int first_m = group * GROUP;
   const int gsz = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (t % (GROUP * tiles_n)) % gsz;
-  const int tn = (t % (GROUP * tiles_n)) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  *tm = first_m + (t % (GROUP * tiles_n)) % gsz;
+  *tn = (t % (GROUP * tiles_n)) / gsz;
+}
 
+// Apply the epilogue to one element (row, col) of batch z.
+template <int EPI, typename OutT, typename T>
+TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
+  if constexpr (EPI == EPI_STORE) {
+    OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+    C[(int64_t)row * p.ldc + col] = from_f32<OutT>(v);
+  } else if constexpr (EPI == EPI_ADD) {
+    float* C = reinterpret_cast<float*>(p.C) + z * p.sC;
+    C[(int64_t)row * p.ldc + col] = p.R[z * p.sR + (int64_t)row * p.ldr + col] + v;
+  } else {
+    // EPI_SGD: fp32 master step, then the compute copies [row][col] and [col][row]
+    float* wp = p.Wm + z * p.sW + (int64_t)row * p.ldw + col;
+    const float nw = *wp - p.lr * v;
+    *wp = nw;
+    if (p.C) reinterpret_cast<T*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<T>(nw);
+    if (p.C2) reinterpret_cast<T*>(p.C2)[z * p.sC2 + (int64_t)col * p.ldc2 + row] = from_f32<T>(nw);
+  }
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int splits, float* part) {
+  typedef GT<T> G;
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int LS = G::BK + G::PAD;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
+  constexpr int TI = WTM / 32, TJ = WTN / 32;     // MFMA tiles per wave
+  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * LS];
+
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int z = blockIdx.z;
   const T* A = reinterpret_cast<const T*>(p.A) + z * p.sA;
   const T* B = reinterpret_cast<const T*>(p.B) + z * p.sB;
 
+  // K range of this split (multiples of BK)
+  const int nk_all = (p.K + G::BK - 1) / G::BK;
+  const int per = (nk_all + splits - 1) / splits;
+  const int kt0 = blockIdx.y * per;
+  const int kt1 = min(nk_all, kt0 + per);
+  const int k_end = min(p.K, kt1 * G::BK);
+
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WGN, wn = w % WGN;
 
-  TileLoader<T, AK> la;
-  TileLoader<T, BKM> lb;
-  f32x16 acc[2][2];
+  TileLoader<T, BM, NT> la;
+  TileLoader<T, BN, NT> lb;
+  f32x16 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
-  const int nk = (p.K + G::BK - 1) / G::BK;
-  la.load(A, p.lda, m0, p.M, 0, p.K);
-  lb.load(B, p.ldb, n0, p.N, 0, p.K);
-  la.store(smem[0]);
-  lb.store(smem[0] + BM * LS);
+  if (kt0 < kt1) {
+    la.load(A, p.lda, m0, p.M, kt0 * G::BK, k_end);
+    lb.load(B, p.ldb, n0, p.N, kt0 * G::BK, k_end);
+    la.store(smem[0]);
+    lb.store(smem[0] + BM * LS);
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(A, p.lda, m0, p.M, (kt + 1) * G::BK, p.K);
-      lb.load(B, p.ldb, n0, p.N, (kt + 1) * G::BK, p.K);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) {
+      la.load(A, p.lda, m0, p.M, (kt + 1) * G::BK, k_end);
+      lb.load(B, p.ldb, n0, p.N, (kt + 1) * G::BK, k_end);
     }
-    const T* sa = smem[cur];
-    const T* sb = smem[cur] + BM * LS;
+    const T* sa = smem[cur] + wm * WTM * LS;
+    const T* sb = smem[cur] + BM * LS + wn * WTN * LS;
 #pragma unroll
     for (int ks = 0; ks < G::BK / G::KS; ++ks) {
       const int kk = ks * G::KS + (lane >> 5) * (G::KS / 2);
-      typename G::frag fa[2], fb[2];
+      typename G::frag fa[TI], fb[TJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = read_frag(sa, wm * 64 + i * 32 + (lane & 31), kk);
+      for (int i = 0; i < TI; ++i) fa[i] = read_frag(sa, i * 32 + (lane & 31), kk);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = read_frag(sb, wn * 64 + j * 32 + (lane & 31), kk);
+      for (int j = 0; j < TJ; ++j) fb[j] = read_frag(sb, j * 32 + (lane & 31), kk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
     }
-    if (kt + 1 < nk) {
+    if (more) {
       la.store(smem[cur ^ 1]);
       lb.store(smem[cur ^ 1] + BM * LS);
     }
@@ -194,62 +194,89 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   }
 
   // ---- epilogue ----
-  OutT* C = p.C ? reinterpret_cast<OutT*>(p.C) + z * p.sC : nullptr;
-  const float* R = p.R ? p.R + z * p.sR : nullptr;
-  float* Wm = p.Wm ? p.Wm + z * p.sW : nullptr;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < TJ; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
       if (col >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         if (row >= p.M) continue;
         const float v = acc[i][j][r];
-        if constexpr (EPI == EPI_STORE) {
-          C[(int64_t)row * p.ldc + col] = from_f32<OutT>(v);
-        } else if constexpr (EPI == EPI_ADD) {
-          C[(int64_t)row * p.ldc + col] = from_f32<OutT>(R[(int64_t)row * p.ldr + col] + v);
-        } else {  // EPI_SGD: fp32 master step, refresh the compute copy
-          float* wp = Wm + (int64_t)row * p.ldw + col;
-          const float nw = *wp - p.lr * v;
-          *wp = nw;
-          if (C) C[(int64_t)row * p.ldc + col] = from_f32<OutT>(nw);
-        }
+        if (splits > 1)
+          part[(((int64_t)blockIdx.y * gridDim.z + z) * p.M + row) * p.N + col] = v;
+        else
+          apply<EPI, OutT, T>(p, z, row, col, v);
       }
     }
 }
 
-template <typename T, bool AK, bool BKM, int EPI, typename OutT>
-hipError_t launch_t(const GemmArgs& p, int batch, hipStream_t st) {
+// sum split-K partials in order and apply the epilogue
+template <typename T, int EPI, typename OutT>
+__global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __restrict__ part) {
+  const int64_t MN = (int64_t)p.M * p.N;
+  const int z = blockIdx.y;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += part[((int64_t)s * batch + z) * MN + e];
+    apply<EPI, OutT, T>(p, z, (int)(e / p.N), (int)(e % p.N), v);
+  }
+}
+
+int g_force_tile = 0;  // test hook: 0 auto, 1 = 256x256, 3 = 128x128 (+ split-K)
+
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
+hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<T, AK, BKM, EPI, OutT>), dim3(tiles, 1, batch), dim3(NT), 0, st, p);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI, OutT>), dim3(tiles, splits, batch),
+                     dim3(WGM * WGN * 64), 0, st, p, splits, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t MN = (int64_t)p.M * p.N;
+  int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
+  hipLaunchKernelGGL((gemm_reduce<T, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
   return hipGetLastError();
 }
 
+template <typename T, int EPI, typename OutT>
+hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipStream_t st) {
+  // 256x256 tiles when they give >= 2 blocks per CU; otherwise 128x128,
+  // split along K when even that leaves CUs idle
+  constexpr int CUS = 256;
+  const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * batch;
+  const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
+  if (g_force_tile == 1 || (!g_force_tile && t256 >= 2 * CUS))
+    return launch_t<T, 256, 256, 2, 4, EPI, OutT>(p, batch, 1, nullptr, st);
+  int splits = 1;
+  const int nk = (p.K + GT<T>::BK - 1) / GT<T>::BK;
+  while (t128 * splits < 2 * CUS && nk / (splits * 2) >= 8 && splits < 8 &&
+         (int64_t)(splits * 2) * batch * p.M * p.N <= ws_elems)
+    splits *= 2;
+  if (splits > 1 && ws) return launch_t<T, 128, 128, 2, 2, EPI, OutT>(p, batch, splits, ws, st);
+  return launch_t<T, 128, 128, 2, 2, EPI, OutT>(p, batch, 1, nullptr, st);
+}
+
 template <typename T>
-hipError_t dispatch(const GemmArgs& p, int layout, int epi, bool out_f32, int batch, hipStream_t st) {
-  // layout: 0 = A K-contig / B K-contig, 1 = A K-contig / B N-contig, 2 = A M-contig / B N-contig
-#define TTT_EPI_CASES(AK, BKM)                                                              \
-  if (epi == EPI_STORE)                                                                    \
-    return out_f32 ? launch_t<T, AK, BKM, EPI_STORE, float>(p, batch, st)                  \
-                   : launch_t<T, AK, BKM, EPI_STORE, T>(p, batch, st);                     \
-  if (epi == EPI_ADD) return launch_t<T, AK, BKM, EPI_ADD, float>(p, batch, st);           \
-  if (epi == EPI_SGD) return launch_t<T, AK, BKM, EPI_SGD, T>(p, batch, st);
-  if (layout == 0) { TTT_EPI_CASES(true, true) }
-  if (layout == 1) { TTT_EPI_CASES(true, false) }
-  if (layout == 2) { TTT_EPI_CASES(false, false) }
-#undef TTT_EPI_CASES
+hipError_t dispatch(const GemmArgs& p, int epi, bool out_f32, int batch, float* ws, int64_t ws_elems,
+                    hipStream_t st) {
+  if (epi == EPI_STORE)
+    return out_f32 ? pick<T, EPI_STORE, float>(p, batch, ws, ws_elems, st)
+                   : pick<T, EPI_STORE, T>(p, batch, ws, ws_elems, st);
+  if (epi == EPI_ADD) return pick<T, EPI_ADD, float>(p, batch, ws, ws_elems, st);
+  if (epi == EPI_SGD) return pick<T, EPI_SGD, T>(p, batch, ws, ws_elems, st);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t gemm_launch(const GemmArgs& p, int dtype, int layout, int epi, bool out_f32, int batch,
+void gemm_force_tile(int cfg) { g_force_tile = cfg; }
+
+hipError_t gemm_launch(const GemmArgs& p, int dtype, int epi, bool out_f32, int batch, float* ws, int64_t ws_elems,
                        hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
-  if (dtype == 1) return dispatch<bf16>(p, layout, epi, out_f32, batch, st);
-  return dispatch<float>(p, layout, epi, out_f32, batch, st);
+  if (p.K % (dtype == 1 ? 8 : 4)) return hipErrorInvalidValue;
+  if (dtype == 1) return dispatch<bf16>(p, epi, out_f32, batch, ws, ws_elems, st);
+  return dispatch<float>(p, epi, out_f32, batch, ws, ws_elems, st);
 }

@@ -26,23 +26,24 @@ extern "C" {
 
 const char* ttt_k_last_error(void) { return k_err.c_str(); }
 
-int ttt_k_gemm(int32_t dtype, int32_t layout, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K,
-               const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
-               int64_t ldc, int64_t sC, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
-               int64_t sW, float lr, int32_t batch, void* stream) {
-  if (layout < 0 || layout > 2 || epi < 0 || epi > 2 || M < 0 || N < 0 || K < 0 || batch < 1)
-    return kfail(TTT_EINVAL, "bad gemm arguments");
+int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* A,
+               int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc, int64_t sC,
+               void* C2, int64_t ldc2, int64_t sC2, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
+               int64_t sW, float lr, int32_t batch, float* ws, int64_t ws_elems, void* stream) {
+  if (epi < 0 || epi > 2 || M < 0 || N < 0 || K < 0 || batch < 1) return kfail(TTT_EINVAL, "bad gemm arguments");
   const int v = dtype == 1 ? 8 : 4;
-  if (N % v || (layout == 0 && K % v) || (layout == 1 && K % v) || (layout == 2 && M % v))
-    return kfail(TTT_EINVAL, "contiguous extents must be multiples of the vector width");
+  if (K % v) return kfail(TTT_EINVAL, "K must be a multiple of the vector width");
   if (epi == 1 && !R) return kfail(TTT_EINVAL, "EPI_ADD needs R");
   if (epi == 2 && !Wm) return kfail(TTT_EINVAL, "EPI_SGD needs Wm");
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.A = A; g.lda = lda; g.sA = sA; g.B = B; g.ldb = ldb; g.sB = sB; g.C = C; g.ldc = ldc; g.sC = sC;
+  g.C2 = C2; g.ldc2 = ldc2; g.sC2 = sC2;
   g.M = M; g.N = N; g.K = K; g.R = R; g.ldr = ldr; g.sR = sR; g.Wm = Wm; g.ldw = ldw; g.sW = sW; g.lr = lr;
-  return kdone(gemm_launch(g, dtype, layout, epi, out_f32 != 0, batch, static_cast<hipStream_t>(stream)));
+  return kdone(gemm_launch(g, dtype, epi, out_f32 != 0, batch, ws, ws_elems, static_cast<hipStream_t>(stream)));
 }
+
+void ttt_k_gemm_tile(int32_t cfg) { gemm_force_tile(cfg); }
 
 static AttnArgs mk(const void* q, const void* kc, const void* vc, int32_t cap, int32_t B, int32_t M, int32_t H,
                    int32_t hd, int64_t pos0, int32_t window, float scale) {

@@ -5,9 +5,8 @@
 #include <stdint.h>
 
 enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SGD = 2 };
-enum { GEMM_NN = 0 /* A K-contig, B K-contig */, GEMM_NT = 1 /* A K-contig, B N-contig */,
-       GEMM_TT = 2 /* A M-contig, B N-contig */ };
 
+// C[m][n] (epilogue)= sum_k A[m*lda + k] * B[n*ldb + k], batched over z.
 struct GemmArgs {
   const void* A;
   const void* B;
@@ -17,13 +16,17 @@ struct GemmArgs {
   int M, N, K;
   const float* R;      // EPI_ADD: C = R + acc (R may alias C)
   int64_t ldr, sR;
-  float* Wm;           // EPI_SGD: Wm -= lr * acc; C (if non-null) = cast(Wm)
+  float* Wm;           // EPI_SGD: Wm -= lr * acc; C[m][n] and C2[n][m] (if non-null) = cast(Wm)
   int64_t ldw, sW;
+  void* C2;
+  int64_t ldc2, sC2;
   float lr;
 };
 
-hipError_t gemm_launch(const GemmArgs& p, int dt, int layout, int epi, bool out_f32, int batch,
-                       hipStream_t st);
+// ws: fp32 split-K workspace of ws_elems elements (may be null: no split)
+hipError_t gemm_launch(const GemmArgs& p, int dt, int epi, bool out_f32, int batch, float* ws,
+                       int64_t ws_elems, hipStream_t st);
+void gemm_force_tile(int cfg);  // test hook (0 = automatic choice)
 
 // Attention over a ring cache. Queries: rows [s*M + i] of q (row stride ldq,
 // head h at column h*hd), position pos0 + i. Keys/values of sequence s at
@@ -80,8 +83,10 @@ struct CEArgs {
 };
 hipError_t ce_launch(const CEArgs& a, int dt, hipStream_t st);
 
+// dst[z][c][r] = src[z][r][c] for r < rows, c < cols (strides in elements)
 hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, int src_dt, void* dst,
-                            int64_t ldd, int dst_dt, hipStream_t st);
+                            int64_t ldd, int dst_dt, hipStream_t st, int batch = 1, int64_t s_src = 0,
+                            int64_t s_dst = 0);
 hipError_t copy_rows_f32_launch(const float* src, int64_t src_seq_stride, float* dst,
                                 int64_t dst_seq_stride, int S, int d, int B, hipStream_t st);
 hipError_t fill_f32_launch(float* p, int64_t n, float v, hipStream_t st);

@@ -68,12 +68,16 @@ struct ttt_model {
   void* embed = nullptr;
   void* gfin = nullptr;
   void* wout_t = nullptr;  // [V][d]
+  void* wout_b = nullptr;  // [d][V] (input-grad layout)
   std::vector<void*> g_attn, g_mlp, wqkv_t, wo_t, wgu_t, wd_t;  // wgu_t/wd_t: frozen blocks only
+  std::vector<void*> wqkv_b, wo_b;  // tail blocks t0+1..L-1: [d][3HD], [HD][d] (input-grad layout)
 
-  // fast weights, per tail block j: [B][...] compute copies and fp32 masters
+  // fast weights, per tail block j: [B][...] compute copies in both layouts
+  // (forward [out][in], input-grad [in][out]) and fp32 masters
   std::vector<void*> f_gu, f_d;      // [B][mg*hf][d], [B][d][hf]
+  std::vector<void*> fb_gu, fb_d;    // [B][d][mg*hf], [B][hf][d]
   std::vector<float*> m_gu, m_d;     // [B][mg*ht][d], [B][d][ht] (bf16 models only)
-  std::vector<void*> i_gu, i_d;      // initial copies (one sequence)
+  std::vector<void*> i_gu, i_d, ib_gu, ib_d;  // initial copies (one sequence)
   std::vector<float*> im_gu, im_d;
 
   // caches and stream state
@@ -98,6 +102,10 @@ struct ttt_model {
   float *dres = nullptr, *dn = nullptr, *dA = nullptr, *delta = nullptr, *dq = nullptr, *dk = nullptr,
         *dv = nullptr;
   void *dres_c = nullptr, *dZ = nullptr, *dO = nullptr, *dqkv = nullptr;
+  // token-contiguous operands of the weight-gradient GEMMs: [B][cols][b]
+  void *Tdres = nullptr, *Ta = nullptr, *Tdz = nullptr, *Tn = nullptr;
+  float* ws = nullptr;  // split-K partials
+  int64_t ws_elems = 0;
 
   bool poisoned = false;
   int64_t bytes = 0;
@@ -174,16 +182,19 @@ struct Ctx {
     }
   }
   // C = A . B^T-ish per GemmArgs, optionally batched over sequences
-  void gemm(int layout, int epi, bool out_f32, const GemmArgs& a, int batch = 1) {
-    // class of this launch for the timing hooks: every GEMM, or the forward
-    // (K-contiguous operands, plain store in the compute dtype) instantiation
+  void gemm(int epi, bool out_f32, const GemmArgs& a, int batch = 1) {
+    // class of this launch for the timing hooks: every GEMM, or the plain
+    // store in the compute dtype (forward projections)
     int cls = TTT_PROF_GEMM;
-    if (m->prof.cls == TTT_PROF_GEMM_FWD)
-      cls = (layout == GEMM_NN && epi == EPI_STORE && !out_f32) ? TTT_PROF_GEMM_FWD : -2;
+    if (m->prof.cls == TTT_PROF_GEMM_FWD) cls = (epi == EPI_STORE && !out_f32) ? TTT_PROF_GEMM_FWD : -2;
     hipEvent_t e0;
     prof_begin(m, cls, st, &e0);
-    chk(gemm_launch(a, m->dt, layout, epi, out_f32, batch, st), "gemm");
+    chk(gemm_launch(a, m->dt, epi, out_f32, batch, m->ws, m->ws_elems, st), "gemm");
     prof_end(m, cls, st, e0, 2.0 * a.M * a.N * (double)a.K * batch);
+  }
+  void transpose(const void* src, int rows, int cols, int64_t lds, void* dst, int64_t ldd, int batch,
+                 int64_t s_src, int64_t s_dst) {
+    chk(transpose_launch(src, rows, cols, lds, m->dt, dst, ldd, m->dt, st, batch, s_src, s_dst), "transpose");
   }
 };
 
@@ -206,7 +217,7 @@ void span_pass(Ctx& c, int64_t p0, int S) {
   c.chk(embed_launch(m->ids, m->maxpos, p0, S, B, m->embed, d, m->V, m->sX, m->dt, c.st), "embed");
   for (int l = 0; l <= m->t0; ++l) {
     c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_attn[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
-    c.gemm(GEMM_NN, EPI_STORE, false, ga(m->sU, d, m->wqkv_t[l], d, m->sQKV, 3 * HD, R, 3 * HD, d));
+    c.gemm(EPI_STORE, false, ga(m->sU, d, m->wqkv_t[l], d, m->sQKV, 3 * HD, R, 3 * HD, d));
     c.chk(rope_split_launch(m->sQKV, R, S, m->H, m->hd, p0, m->cfg.rope ? m->rope : nullptr, m->sQ,
                             m->kc[l], m->vc[l], m->cap_s, (int64_t)m->cap_s * HD, m->dt, c.st),
           "rope");
@@ -225,15 +236,15 @@ void span_pass(Ctx& c, int64_t p0, int S) {
     }
     GemmArgs g = ga(m->sO, HD, m->wo_t[l], HD, m->sX, d, R, d, HD);
     g.R = m->sX; g.ldr = d;
-    c.gemm(GEMM_NN, EPI_ADD, true, g);
+    c.gemm(EPI_ADD, true, g);
     if (l == m->t0) break;
     c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_mlp[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
     const int h = m->h, zw = m->mg * h;
-    c.gemm(GEMM_NN, EPI_STORE, false, ga(m->sU, d, m->wgu_t[l], d, m->sZ, zw, R, zw, d));
+    c.gemm(EPI_STORE, false, ga(m->sU, d, m->wgu_t[l], d, m->sZ, zw, R, zw, d));
     c.chk(act_fwd_launch(m->sZ, R, h, zw, m->mg == 2, m->sA, h, m->dt, c.st), "act");
     g = ga(m->sA, h, m->wd_t[l], h, m->sX, d, R, d, h);
     g.R = m->sX; g.ldr = d;
-    c.gemm(GEMM_NN, EPI_ADD, true, g);
+    c.gemm(EPI_ADD, true, g);
   }
   (void)es;
   c.chk(copy_rows_f32_launch(m->sX, (int64_t)S * d, m->ystage + p0 * d, m->maxpos * d, S, d, B, c.st), "copy");
@@ -257,7 +268,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     if (j >= 1) {
       y = m->ty[j];
       c.chk(rmsnorm_fwd_launch(m->tx[j], R, d, m->g_attn[l], eps, m->tU, m->tr1[j], m->dt, c.st), "norm");
-      c.gemm(GEMM_NN, EPI_STORE, false, ga(m->tU, d, m->wqkv_t[l], d, m->tQKV, 3 * HD, R, 3 * HD, d));
+      c.gemm(EPI_STORE, false, ga(m->tU, d, m->wqkv_t[l], d, m->tQKV, 3 * HD, R, 3 * HD, d));
       c.chk(rope_split_launch(m->tQKV, R, M, m->H, m->hd, P0, m->cfg.rope ? m->rope : nullptr, m->tq[j],
                               m->kc[l], m->vc[l], m->cap_t, (int64_t)m->cap_t * HD, m->dt, c.st),
             "rope");
@@ -275,21 +286,21 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       prof_end(m, TTT_PROF_ATTN_FWD, c.st, e0, 4.0 * m->hd * m->H * pairs * B);
       GemmArgs g = ga(m->to[j], HD, m->wo_t[l], HD, y, d, R, d, HD);
       g.R = m->tx[j]; g.ldr = d;
-      c.gemm(GEMM_NN, EPI_ADD, true, g);
+      c.gemm(EPI_ADD, true, g);
     }
     c.chk(rmsnorm_fwd_launch(y, R, d, m->g_mlp[l], eps, m->tn[j], m->tr2[j], m->dt, c.st), "norm");
     GemmArgs g = ga(m->tn[j], d, m->f_gu[j], d, m->tz[j], zw, M, zw, d);
     g.sA = (int64_t)M * d; g.sB = sgu; g.sC = (int64_t)M * zw;
-    c.gemm(GEMM_NN, EPI_STORE, false, g, B);
+    c.gemm(EPI_STORE, false, g, B);
     c.chk(act_fwd_launch(m->tz[j], R, hf, zw, mg == 2, m->ta[j], hf, m->dt, c.st), "act");
     float* xo = (j + 1 < m->nt) ? m->tx[j + 1] : m->txL;
     g = ga(m->ta[j], hf, m->f_d[j], hf, xo, d, M, d, hf);
     g.sA = (int64_t)M * hf; g.sB = sd; g.sC = (int64_t)M * d;
     g.R = y; g.ldr = d; g.sR = (int64_t)M * d;
-    c.gemm(GEMM_NN, EPI_ADD, true, g, B);
+    c.gemm(EPI_ADD, true, g, B);
   }
   c.chk(rmsnorm_fwd_launch(m->txL, R, d, m->gfin, eps, m->tf, m->trf, m->dt, c.st), "norm");
-  c.gemm(GEMM_NN, EPI_STORE, true, ga(m->tf, d, m->wout_t, d, m->tlog, V, R, V, d));
+  c.gemm(EPI_STORE, true, ga(m->tf, d, m->wout_t, d, m->tlog, V, R, V, d));
   {
     CEArgs a;
     memset(&a, 0, sizeof(a));
@@ -306,48 +317,59 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
   if (!bwd) return;
 
   // ---------------- backward ----------------
-  c.gemm(GEMM_NT, EPI_STORE, true, ga(m->tdz, V, m->wout_t, d, m->dn, d, R, d, V));
+  // every product below reads both operands K-contiguous: input grads use the
+  // [in][out] copies of the weights, weight grads use token-contiguous
+  // (transposed) copies of the activations and output gradients
+  c.gemm(EPI_STORE, true, ga(m->tdz, V, m->wout_b, V, m->dn, d, R, d, V));
   c.chk(rmsnorm_bwd_launch(m->txL, m->trf, m->gfin, m->dn, R, d, m->dres, m->dres_c, false, m->dt, c.st),
         "norm_bwd");
   const bool master = m->dt == 1;
+  const int64_t sbgu = (int64_t)d * zw, sbd = (int64_t)hf * d;  // per-seq strides of the [in][out] copies
   for (int j = m->nt - 1; j >= 0; --j) {
     const int l = m->t0 + j;
     const int hcols = j == 0 ? ht : hf;
-    // dA = dres . W_down (reads W_c before its update below)
-    GemmArgs g = ga(m->dres_c, d, m->f_d[j], hf, m->dA, hf, M, hcols, d);
-    g.sA = (int64_t)M * d; g.sB = sd; g.sC = (int64_t)M * hf;
-    c.gemm(GEMM_NT, EPI_STORE, true, g, B);
-    // W_down trainable columns: W^T[d][ht] -= eta * dres^T . A
-    g = ga(m->dres_c, d, m->ta[j], hf, master ? m->f_d[j] : nullptr, hf, d, ht, M);
-    g.sA = (int64_t)M * d; g.sB = (int64_t)M * hf; g.sC = sd;
+    // dA = dres . W_down^T  (reads W_c before its update below)
+    GemmArgs g = ga(m->dres_c, d, m->fb_d[j], d, m->dA, hf, M, hcols, d);
+    g.sA = (int64_t)M * d; g.sB = sbd; g.sC = (int64_t)M * hf;
+    c.gemm(EPI_STORE, true, g, B);
+    // W_down trainable columns: W^T[d][ht] -= eta * dres^T . A_t
+    c.transpose(m->dres_c, M, d, d, m->Tdres, M, B, (int64_t)M * d, (int64_t)d * M);
+    c.transpose(m->ta[j], M, ht, hf, m->Ta, M, B, (int64_t)M * hf, (int64_t)ht * M);
+    g = ga(m->Tdres, M, m->Ta, M, master ? m->f_d[j] : nullptr, hf, d, ht, M);
+    g.sA = (int64_t)d * M; g.sB = (int64_t)ht * M; g.sC = sd;
     g.Wm = master ? m->m_d[j] : static_cast<float*>(m->f_d[j]);
     g.ldw = master ? ht : hf; g.sW = master ? smd : sd;
+    g.C2 = m->fb_d[j]; g.ldc2 = d; g.sC2 = sbd;
     g.lr = m->cfg.lr;
-    c.gemm(GEMM_TT, EPI_SGD, false, g, B);
+    c.gemm(EPI_SGD, false, g, B);
     c.chk(act_bwd_launch(m->tz[j], m->dA, R, hcols, zw, hf, hf, mg == 2, m->dZ, zw, m->dt, c.st), "act_bwd");
     if (j >= 1) {
-      g = ga(m->dZ, zw, m->f_gu[j], d, m->dn, d, M, d, zw);
-      g.sA = (int64_t)M * zw; g.sB = sgu; g.sC = (int64_t)M * d;
-      c.gemm(GEMM_NT, EPI_STORE, true, g, B);
+      // dn = dZ . W_gu^T (reads W_c before its update below)
+      g = ga(m->dZ, zw, m->fb_gu[j], zw, m->dn, d, M, d, zw);
+      g.sA = (int64_t)M * zw; g.sB = sbgu; g.sC = (int64_t)M * d;
+      c.gemm(EPI_STORE, true, g, B);
     }
-    // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ^T . n
+    // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ_t^T . n
+    c.transpose(m->tn[j], M, d, d, m->Tn, M, B, (int64_t)M * d, (int64_t)d * M);
     for (int part = 0; part < mg; ++part) {
-      const int64_t zoff = (int64_t)part * hf;           // column of dZ / row of the compute copy
-      const int64_t moff = (int64_t)part * ht * d;       // row block of the master
-      g = ga(off(m->dZ, zoff, es), zw, m->tn[j], d, master ? off(m->f_gu[j], zoff * d, es) : nullptr, d, ht,
-             d, M);
-      g.sA = (int64_t)M * zw; g.sB = (int64_t)M * d; g.sC = sgu;
+      const int64_t zoff = (int64_t)part * hf;      // column of dZ / row of the forward copy
+      const int64_t moff = (int64_t)part * ht * d;  // row block of the master
+      void* tdz = off(m->Tdz, (int64_t)part * B * ht * M, es);
+      c.transpose(off(m->dZ, zoff, es), M, ht, zw, tdz, M, B, (int64_t)M * zw, (int64_t)ht * M);
+      g = ga(tdz, M, m->Tn, M, master ? off(m->f_gu[j], zoff * d, es) : nullptr, d, ht, d, M);
+      g.sA = (int64_t)ht * M; g.sB = (int64_t)d * M; g.sC = sgu;
       g.Wm = master ? m->m_gu[j] + moff : reinterpret_cast<float*>(off(m->f_gu[j], zoff * d, es));
       g.ldw = d; g.sW = master ? smgu : sgu;
+      g.C2 = off(m->fb_gu[j], zoff, es); g.ldc2 = zw; g.sC2 = sbgu;
       g.lr = m->cfg.lr;
-      c.gemm(GEMM_TT, EPI_SGD, false, g, B);
+      c.gemm(EPI_SGD, false, g, B);
     }
     if (j == 0) break;
     c.chk(rmsnorm_bwd_launch(m->ty[j], m->tr2[j], m->g_mlp[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
                              c.st),
           "norm_bwd");
     // attention sublayer
-    c.gemm(GEMM_NT, EPI_STORE, false, ga(m->dres_c, d, m->wo_t[l], HD, m->dO, HD, R, HD, d));
+    c.gemm(EPI_STORE, false, ga(m->dres_c, d, m->wo_b[l], d, m->dO, HD, R, HD, d));
     c.chk(attn_delta_launch(m->to[j], m->dO, R, m->H, m->hd, HD, M, m->delta, m->dt, c.st), "delta");
     AttnArgs a;
     memset(&a, 0, sizeof(a));
@@ -369,7 +391,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     c.chk(rope_bwd_pack_launch(m->dq, m->dk, m->dv, R, M, m->H, m->hd, P0, m->cfg.rope ? m->rope : nullptr,
                                m->dqkv, m->dt, c.st),
           "rope_bwd");
-    c.gemm(GEMM_NT, EPI_STORE, true, ga(m->dqkv, 3 * HD, m->wqkv_t[l], d, m->dn, d, R, d, 3 * HD));
+    c.gemm(EPI_STORE, true, ga(m->dqkv, 3 * HD, m->wqkv_b[l], 3 * HD, m->dn, d, R, d, 3 * HD));
     c.chk(rmsnorm_bwd_launch(m->tx[j], m->tr1[j], m->g_attn[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
                              c.st),
           "norm_bwd");
@@ -444,6 +466,8 @@ static int reset_state(ttt_model* m, hipStream_t st) {
     for (int s = 0; s < B; ++s) {
       ck(hipMemcpyAsync(off(m->f_gu[j], s * ngu, m->es), m->i_gu[j], ngu * m->es, hipMemcpyDeviceToDevice, st));
       ck(hipMemcpyAsync(off(m->f_d[j], s * nd, m->es), m->i_d[j], nd * m->es, hipMemcpyDeviceToDevice, st));
+      ck(hipMemcpyAsync(off(m->fb_gu[j], s * ngu, m->es), m->ib_gu[j], ngu * m->es, hipMemcpyDeviceToDevice, st));
+      ck(hipMemcpyAsync(off(m->fb_d[j], s * nd, m->es), m->ib_d[j], nd * m->es, hipMemcpyDeviceToDevice, st));
       if (m->dt == 1) {
         const int64_t mgu = (int64_t)m->mg * m->ht * m->d, md = (int64_t)m->d * m->ht;
         ck(hipMemcpyAsync(m->m_gu[j] + s * mgu, m->im_gu[j], mgu * 4, hipMemcpyDeviceToDevice, st));
@@ -517,8 +541,10 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   m->embed = A.el((int64_t)V * d);
   m->gfin = A.el(d);
   m->wout_t = A.el((int64_t)V * d);
+  m->wout_b = A.el((int64_t)V * d);
   m->g_attn.resize(L); m->g_mlp.resize(L); m->wqkv_t.resize(L); m->wo_t.resize(L);
   m->wgu_t.assign(L, nullptr); m->wd_t.assign(L, nullptr);
+  m->wqkv_b.assign(L, nullptr); m->wo_b.assign(L, nullptr);
   for (int l = 0; l < L; ++l) {
     m->g_attn[l] = A.el(d);
     m->g_mlp[l] = A.el(d);
@@ -528,15 +554,24 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
       m->wgu_t[l] = A.el((int64_t)mg * h * d);
       m->wd_t[l] = A.el((int64_t)d * h);
     }
+    if (l > t0) {
+      m->wqkv_b[l] = A.el((int64_t)3 * HD * d);
+      m->wo_b[l] = A.el((int64_t)d * HD);
+    }
   }
   m->f_gu.resize(m->nt); m->f_d.resize(m->nt); m->i_gu.resize(m->nt); m->i_d.resize(m->nt);
+  m->fb_gu.resize(m->nt); m->fb_d.resize(m->nt); m->ib_gu.resize(m->nt); m->ib_d.resize(m->nt);
   m->m_gu.assign(m->nt, nullptr); m->m_d.assign(m->nt, nullptr);
   m->im_gu.assign(m->nt, nullptr); m->im_d.assign(m->nt, nullptr);
   for (int j = 0; j < m->nt; ++j) {
     m->f_gu[j] = A.el((int64_t)B * mg * hf * d);
     m->f_d[j] = A.el((int64_t)B * d * hf);
+    m->fb_gu[j] = A.el((int64_t)B * mg * hf * d);
+    m->fb_d[j] = A.el((int64_t)B * d * hf);
     m->i_gu[j] = A.el((int64_t)mg * hf * d);
     m->i_d[j] = A.el((int64_t)d * hf);
+    m->ib_gu[j] = A.el((int64_t)mg * hf * d);
+    m->ib_d[j] = A.el((int64_t)d * hf);
     if (m->dt == 1) {
       m->m_gu[j] = A.f32((int64_t)B * mg * ht * d);
       m->m_d[j] = A.f32((int64_t)B * d * ht);
@@ -580,6 +615,9 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   m->dres = A.f32(Rt * d); m->dn = A.f32(Rt * d); m->dA = A.f32(Rt * hf); m->delta = A.f32(Rt * m->H);
   m->dq = A.f32(Rt * HD); m->dk = A.f32(Rt * HD); m->dv = A.f32(Rt * HD);
   m->dres_c = A.el(Rt * d); m->dZ = A.el(Rt * mg * hf); m->dO = A.el(Rt * HD); m->dqkv = A.el(Rt * 3 * HD);
+  m->Tdres = A.el(Rt * d); m->Ta = A.el(Rt * ht); m->Tdz = A.el(Rt * mg * ht); m->Tn = A.el(Rt * d);
+  m->ws_elems = std::min<int64_t>((int64_t)1 << 26, 8 * Rt * std::max({d, 3 * HD, hf}));
+  m->ws = A.f32(m->ws_elems);
   if (!A.ok) {
     rc = fail(TTT_ENOMEM, A.why);
     ttt_model_destroy(m);
@@ -593,6 +631,7 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   ck(hipMemcpyAsync(m->embed, w->embed, (int64_t)V * d * es, hipMemcpyDeviceToDevice, st));
   ck(hipMemcpyAsync(m->gfin, w->final_norm, d * es, hipMemcpyDeviceToDevice, st));
   ck(put_t(w->lm_head, d, V, m->wout_t, d, dt, dt, st));
+  ck(hipMemcpyAsync(m->wout_b, w->lm_head, (int64_t)V * d * es, hipMemcpyDeviceToDevice, st));
   for (int l = 0; l < L; ++l) {
     ck(hipMemcpyAsync(m->g_attn[l], w->attn_norm[l], d * es, hipMemcpyDeviceToDevice, st));
     ck(hipMemcpyAsync(m->g_mlp[l], w->mlp_norm[l], d * es, hipMemcpyDeviceToDevice, st));
@@ -600,6 +639,13 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
     ck(put_t(w->wk[l], d, HD, off(m->wqkv_t[l], (int64_t)HD * d, es), d, dt, dt, st));
     ck(put_t(w->wv[l], d, HD, off(m->wqkv_t[l], (int64_t)2 * HD * d, es), d, dt, dt, st));
     ck(put_t(w->wo[l], HD, d, m->wo_t[l], HD, dt, dt, st));
+    if (l > t0) {
+      const void* qkv[3] = {w->wq[l], w->wk[l], w->wv[l]};
+      for (int i = 0; i < 3; ++i)
+        ck(hipMemcpy2DAsync(off(m->wqkv_b[l], (int64_t)i * HD, es), 3 * HD * es, qkv[i], HD * es, HD * es, d,
+                            hipMemcpyDeviceToDevice, st));
+      ck(hipMemcpyAsync(m->wo_b[l], w->wo[l], (int64_t)HD * d * es, hipMemcpyDeviceToDevice, st));
+    }
     if (l < t0) {
       if (glu) {
         ck(put_t(w->w_gate[l], d, h, m->wgu_t[l], d, dt, dt, st));
@@ -613,14 +659,24 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
       // concatenated [gate_t | gate_s | up_t | up_s] rows (SwiGLU) or [up_t | up_s]
       const void* tr[2] = {glu ? w->w_gate[l] : w->w_up[l], w->w_up[l]};
       const void* sr[2] = {glu ? w->s_gate[l] : (hs ? w->s_up[l] : nullptr), hs ? w->s_up[l] : nullptr};
+      const int zw = mg * hf;
       for (int part = 0; part < mg; ++part) {
         void* base = off(m->i_gu[j], (int64_t)part * hf * d, es);
         ck(put_t(tr[part], d, ht, base, d, dt, dt, st));
         if (hs) ck(put_t(sr[part], d, hs, off(base, (int64_t)ht * d, es), d, dt, dt, st));
         if (dt == 1) ck(put_t(tr[part], d, ht, m->im_gu[j] + (int64_t)part * ht * d, d, dt, 0, st));
+        // input-grad layout [d][zw]: columns [part*hf, part*hf + ht) trainable, then static
+        void* bb = off(m->ib_gu[j], (int64_t)part * hf, es);
+        ck(hipMemcpy2DAsync(bb, zw * es, tr[part], ht * es, ht * es, d, hipMemcpyDeviceToDevice, st));
+        if (hs)
+          ck(hipMemcpy2DAsync(off(bb, ht, es), zw * es, sr[part], hs * es, hs * es, d, hipMemcpyDeviceToDevice, st));
       }
       ck(put_t(w->w_down[l], ht, d, m->i_d[j], hf, dt, dt, st));
       if (hs) ck(put_t(w->s_down[l], hs, d, off(m->i_d[j], ht, es), hf, dt, dt, st));
+      ck(hipMemcpyAsync(m->ib_d[j], w->w_down[l], (int64_t)ht * d * es, hipMemcpyDeviceToDevice, st));
+      if (hs)
+        ck(hipMemcpyAsync(off(m->ib_d[j], (int64_t)ht * d, es), w->s_down[l], (int64_t)hs * d * es,
+                          hipMemcpyDeviceToDevice, st));
       if (dt == 1) ck(put_t(w->w_down[l], ht, d, m->im_d[j], ht, dt, 0, st));
     }
   }

@@ -27,18 +27,13 @@ def sync():
 
 # ------------------------------- GEMM ---------------------------------------
 
-def run_gemm(dtype, layout, epi, M, N, K, batch=1, out_f32=True, lr=0.0):
+def run_gemm(dtype, epi, M, N, K, batch=1, out_f32=True, lr=0.0, tile=0, ws_elems=0):
+    """C = A . B^T with both operands K-contiguous, against fp64 numpy."""
     lib = bd.load()
     A, Ad = rnd((batch, M, K), 1, dtype)
     Bm, Bd = rnd((batch, N, K), 2, dtype)
-    if layout >= 2:
-        Ad = Ad.transpose(1, 2).contiguous()
-    if layout >= 1:
-        Bd = Bd.transpose(1, 2).contiguous()
-    lda = K if layout < 2 else M
-    ldb = K if layout == 0 else N
     ref = np.einsum("zmk,znk->zmn", A, Bm)
-    R = Rd = Wm = Wd = None
+    R = Rd = Wm = Wd = C2 = None
     cdt = torch.float32 if (out_f32 or epi == 1) else dtype
     C = torch.zeros((batch, M, N), dtype=cdt, device="cuda")
     if epi == 1:
@@ -48,49 +43,65 @@ def run_gemm(dtype, layout, epi, M, N, K, batch=1, out_f32=True, lr=0.0):
         Wm, Wd = rnd((batch, M, N), 4, torch.float32)
         ref = Wm - lr * ref
         C = torch.zeros((batch, M, N), dtype=dtype, device="cuda")
-    rc = lib.ttt_k_gemm(kdt(dtype), layout, epi, int(out_f32), M, N, K, bd.ptr(Ad), lda, M * K, bd.ptr(Bd),
-                        ldb, N * K, bd.ptr(C), N, M * N, bd.ptr(Rd), N, M * N, bd.ptr(Wd), N, M * N,
-                        lr, batch, bd.stream_ptr())
-    bd.check(rc, kernel=True)
-    sync()
-    return ref, C.float().cpu().numpy(), (Wd.cpu().numpy() if Wd is not None else None)
+        C2 = torch.zeros((batch, N, M), dtype=dtype, device="cuda")
+    ws = torch.zeros(max(ws_elems, 1), device="cuda") if ws_elems else None
+    lib.ttt_k_gemm_tile(tile)
+    try:
+        rc = lib.ttt_k_gemm(kdt(dtype), epi, int(out_f32), M, N, K, bd.ptr(Ad), K, M * K, bd.ptr(Bd), K, N * K,
+                            bd.ptr(C), N, M * N, bd.ptr(C2), M, M * N, bd.ptr(Rd), N, M * N, bd.ptr(Wd), N, M * N,
+                            lr, batch, bd.ptr(ws), ws_elems, bd.stream_ptr())
+        bd.check(rc, kernel=True)
+        sync()
+    finally:
+        lib.ttt_k_gemm_tile(0)
+    return (ref, C.float().cpu().numpy(), (Wd.cpu().numpy() if Wd is not None else None),
+            (C2.float().cpu().numpy() if C2 is not None else None))
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("layout", [0, 1, 2])
-@pytest.mark.parametrize("shape", [(200, 136, 72), (1, 64, 96), (256, 256, 512), (72, 328, 1000)])
-def test_gemm_store(dtype, layout, shape):
+@pytest.mark.parametrize("tile", [0, 1, 3])
+@pytest.mark.parametrize("shape", [(200, 136, 72), (1, 64, 96), (256, 256, 512), (300, 328, 1000)])
+def test_gemm_store(dtype, tile, shape):
     M, N, K = shape
-    if layout == 2 and M % 8:
-        M = 8
-    ref, got, _ = run_gemm(dtype, layout, 0, M, N, K, batch=2)
-    tol = 1e-5 if dtype == torch.float32 else 1e-5
+    ref, got, _, _ = run_gemm(dtype, 0, M, N, K, batch=2, tile=tile)
     err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
-    assert err < tol * math.sqrt(K) * 4, err
+    assert err < 4e-5 * math.sqrt(K), err
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", [(130, 136, 4096), (1, 3072, 3072), (64, 256, 8192)])
+def test_gemm_split_k(dtype, shape):
+    """Few output tiles and a long K: the 128x128 tile splits K (fixed-order sum)."""
+    M, N, K = shape
+    ref, got, _, _ = run_gemm(dtype, 1, M, N, K, tile=3, ws_elems=1 << 24)
+    err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err < 4e-5 * math.sqrt(K), err
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_gemm_store_compute_dtype(dtype):
-    ref, got, _ = run_gemm(dtype, 0, 0, 130, 64, 64, out_f32=False)
+    ref, got, _, _ = run_gemm(dtype, 0, 130, 64, 64, out_f32=False)
     rt = 1e-6 if dtype == torch.float32 else 2 ** -8
     np.testing.assert_allclose(got, ref, rtol=rt, atol=rt * np.abs(ref).max())
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("layout", [0, 1])
-def test_gemm_residual_add(dtype, layout):
-    ref, got, _ = run_gemm(dtype, layout, 1, 150, 96, 200)
+@pytest.mark.parametrize("tile", [0, 1, 3])
+def test_gemm_residual_add(dtype, tile):
+    ref, got, _, _ = run_gemm(dtype, 1, 150, 96, 200, tile=tile)
     np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-4)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_gemm_sgd_epilogue(dtype):
-    """W <- W - lr * (A^T-contracted gradient); compute copy = cast(W)."""
+@pytest.mark.parametrize("tile,ws", [(0, 0), (1, 0), (3, 1 << 22)])
+def test_gemm_sgd_epilogue(dtype, tile, ws):
+    """W <- W - lr * (gradient); both compute copies = cast(W)."""
     lr = 0.37
-    ref, got_c, got_w = run_gemm(dtype, 2, 2, 96, 136, 300, batch=2, lr=lr)
+    ref, got_c, got_w, got_c2 = run_gemm(dtype, 2, 96, 136, 1024, batch=2, lr=lr, tile=tile, ws_elems=ws)
     np.testing.assert_allclose(got_w, ref, rtol=1e-5, atol=1e-4)
     rt = 1e-7 if dtype == torch.float32 else 2 ** -8
     np.testing.assert_allclose(got_c, got_w, rtol=rt, atol=0)
+    np.testing.assert_allclose(got_c2, got_w.transpose(0, 2, 1), rtol=rt, atol=0)
 
 
 # ---------------------------- attention --------------------------------------
