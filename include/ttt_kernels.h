@@ -40,18 +40,24 @@ void ttt_k_gemm_tile(int32_t cfg);
  * p-window < j <= p; technical review section 2.1 Eq. 1 and section 5).
  * q, o: [B*M][H*hd] rows (row s*M+i = position pos0+i of sequence s);
  * kc, vc: [B][cap][H*hd], key position j at slot j % cap (cap multiple of 64);
- * lse: fp32 [B][H][M] natural-log sum of exp of the scaled scores. */
+ * lse: fp32 [B][H][M] natural-log sum of exp of the scaled scores.
+ * nsplit (1..8) splits each query block's key range over workgroups; with
+ * nsplit > 1, ws is an fp32 workspace of nsplit*B*M*(H*hd + 2*H) elements. */
 int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
                    float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
-                   float scale, void* stream);
+                   float scale, int32_t nsplit, float* ws, void* stream);
 
-/* Backward of ttt_k_attn_fwd: dq (fp32, rows like q) over each query's whole
- * window; dk, dv (fp32 [B*M][H*hd]) for the keys at positions pos0..pos0+M-1
- * only (earlier cached keys are constants). dout like q; delta = fp32
- * [B][H][M] row sums of dout * o (see ttt_k_attn_delta). */
+/* Backward of ttt_k_attn_fwd: dq (fp32, nsplit slices of [B*M][H*hd] whose
+ * sum is the gradient; each query's window split as in the forward); dk, dv
+ * (fp32 [B*M][H*hd]) for the keys at positions pos0..pos0+M-1 only (earlier
+ * cached keys are constants). dout like q; delta = fp32 [B][H][M] row sums
+ * of dout * o (see ttt_k_attn_delta). */
 int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, const float* lse,
                    const void* dout, const float* delta, float* dq, float* dk, float* dv, int32_t B, int32_t M,
-                   int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, void* stream);
+                   int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, int32_t nsplit, void* stream);
+
+/* The library's choice of key-range splits for M queries per sequence. */
+int32_t ttt_k_attn_splits(int32_t M, int32_t H, int32_t B, int64_t keys_per_query);
 int ttt_k_attn_delta(int32_t dtype, const void* o, const void* dout, int32_t B, int32_t M, int32_t H, int32_t hd,
                      float* delta, void* stream);
 

@@ -81,9 +81,10 @@ def load():
     lib.ttt_k_gemm_tile.argtypes = [c_i32]
     lib.ttt_k_gemm_tile.restype = None
     lib.ttt_k_attn_fwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
-                                   c_i64, c_i32, c_f32, c_vp]
+                                   c_i64, c_i32, c_f32, c_i32, c_vp, c_vp]
     lib.ttt_k_attn_bwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
-                                   c_i32, c_i32, c_i32, c_i64, c_i32, c_f32, c_vp]
+                                   c_i32, c_i32, c_i32, c_i64, c_i32, c_f32, c_i32, c_vp]
+    lib.ttt_k_attn_splits.argtypes = [c_i32, c_i32, c_i32, c_i64]
     lib.ttt_k_attn_delta.argtypes = [c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
     lib.ttt_k_ce.argtypes = [c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp, c_vp, c_vp]
     lib.ttt_k_rmsnorm_fwd.argtypes = [c_i32, c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp, c_vp]

@@ -10,13 +10,17 @@
 // rows before attention runs.
 //
 // Every product is an MFMA 32x32 tile with the query index on the lanes:
-//   S^T[key][q] = K . Q^T     (K tile from LDS, Q fragments held in registers)
-//   O^T[d][q]  += V^T . P^T   (V staged transposed in LDS, P from registers)
+//   S^T[key][q] = K . Q^T     (K fragments from LDS, Q fragments in registers)
+//   O^T[d][q]  += V^T . P^T   (V^T fragments from LDS, P from registers)
 // so each lane owns one query's softmax row (two half-waves split the keys):
-// the online-softmax max and sum need only one cross-half shuffle. The P
-// fragments are fed to the second MFMA straight from the first one's
-// accumulator registers; the keys of the 16-wide contraction are permuted
-// consistently on both operands, which the sum over keys does not see.
+// the online-softmax max and sum need one cross-half shuffle. P is fed to the
+// second MFMA straight from the first one's accumulator registers; the keys
+// of the 16-wide contraction are permuted consistently on both operands,
+// which the sum over keys does not see. All tiles sit in LDS row-major
+// (copied with 16-byte loads and stores, double-buffered so the next tile's
+// global loads overlap the current tile's MFMAs); operands that need the
+// transposed view (V^T, K^T, Q^T, dO^T) are read with gfx950's transposing
+// LDS read ds_read_b64_tr_b16 (fp32: plain reads, one element per lane).
 //
 // Backward (only the gradients the inner loop needs): dQ for every query over
 // its whole window; dK and dV only for keys of the current chunk (cached keys
@@ -25,6 +29,9 @@
 //                               dQ^T += K^T . dS^T
 //   dkdv kernel (key-owned):    S = Q . K^T, P, dV^T += dO^T . P,
 //                               dP = dO . V^T, dK^T += Q^T . dS
+// When few queries are in flight (a chunk of b rows), the forward and the dq
+// kernel split each query block's key range over several workgroups
+// ("splits"); partial results are merged in a fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,16 +42,29 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr int NT = 256;
 constexpr int BKEY = 64;  // key tile
 constexpr int WQ = 32;    // queries (or keys) per wave
+constexpr int QB = 4 * WQ;  // queries per workgroup
 constexpr float NEG_BIG = -1e30f;
+// The running row max of the online softmax is raised only when a tile's max
+// exceeds it by more than RESCALE_SLACK (log2 units): probabilities are then
+// bounded by 2^RESCALE_SLACK and the O accumulators are rescaled rarely.
+constexpr float RESCALE_SLACK = 8.f;
+
+// 2^x with the hardware instruction (flushes results below 2^-126 to zero,
+// which a softmax weight never needs)
+TTT_DEV float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T> struct AT;
+// Row padding of the LDS tiles: PADR for tiles read only row-wise (16-byte
+// fragment reads, conflict-free at a stride of 4 mod 64 dwords), PADT for
+// tiles also read transposed (a 16-lane transposing read touches 4 rows, which
+// a stride of 8 mod 64 dwords spreads over distinct banks).
 template <> struct AT<bf16> {
-  static constexpr int KS = 16, PAD = 8, VEC = 8;
+  static constexpr int KS = 16, PADR = 8, PADT = 16, VEC = 8;
   typedef bf16x8 frag;
   typedef bf16x8 vec;
 };
 template <> struct AT<float> {
-  static constexpr int KS = 2, PAD = 1, VEC = 4;
+  static constexpr int KS = 2, PADR = 1, PADT = 1, VEC = 4;
   typedef float frag;
   typedef f32x4 vec;
 };
@@ -56,40 +76,53 @@ TTT_DEV f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Number of MFMA k-steps that cover 32 keys, and the key index (0..31 in a
-// 32-key accumulator tile) of fragment element e at k-step u for half-wave h.
-template <typename T> struct KeyPerm;
-template <> struct KeyPerm<bf16> {
-  static constexpr int STEPS = 2;
-  TTT_DEV static int key(int u, int h, int e) { return u * 16 + (e >> 2) * 8 + h * 4 + (e & 3); }
-};
-template <> struct KeyPerm<float> {
-  static constexpr int STEPS = 16;
-  TTT_DEV static int key(int u, int h, int) { return (u >> 2) * 8 + h * 4 + (u & 3); }
-};
+// Number of MFMA k-steps that cover 32 keys.
+template <typename T> struct KSteps;
+template <> struct KSteps<bf16> { static constexpr int N = 2; };
+template <> struct KSteps<float> { static constexpr int N = 16; };
 
 // accumulator register r of a 32x32 tile -> row within the tile (lane half h)
 TTT_DEV int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
 
-// fragment of a row-major LDS tile s[row][ld] at (row, k..): rows on lanes
+// fragment (rows on lanes, KS consecutive k) of a row-major LDS tile s[row][ld]
 template <typename T>
 TTT_DEV typename AT<T>::frag lds_frag(const T* s, int ld, int row, int k) {
   return *reinterpret_cast<const typename AT<T>::frag*>(s + row * ld + k);
 }
 
-// Build the fragment of a transposed LDS tile st[d][key] for MFMA A-operand
-// rows d, keys permuted as KeyPerm for the 32-key group g and step u.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Fragment of the TRANSPOSED view of a row-major LDS tile s[key][d]: MFMA
+// operand rows = d (d0 .. d0+31 on the lanes), contraction over the 32 keys
+// of group g at k-step u, in the key order of the accumulator registers
+// (key(u, h, e) = 16u + 8*(e/4) + 4h + e%4 for bf16; (u/4)*8 + 4h + u%4 fp32).
+// bf16: two ds_read_b64_tr_b16. Within a 16-lane group a transposing read
+// returns to lane i element e the (i%4)-th 16-bit value at the address of
+// lane i/4 + 4e, so lane X supplies the 4 values of key row
+// (base + 8r + (X%16)/4), columns d0 + 16*((X/16)%2) + 4*(X%4) .. +3.
 template <typename T>
-TTT_DEV typename AT<T>::frag lds_frag_perm(const T* st, int ld, int d, int g, int u, int h) {
+TTT_DEV typename AT<T>::frag lds_frag_tr(const T* s, int ld, int d0, int g, int u, int lane, int dmax) {
   typename AT<T>::frag f;
   if constexpr (sizeof(T) == 2) {
-    const T* p = st + d * ld + g * 32 + u * 16 + h * 4;
-    bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-    bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
-    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    const int h = lane >> 5;
+    const int key = g * 32 + u * 16 + h * 4 + ((lane & 15) >> 2);
+    const int col = d0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    typedef __attribute__((address_space(3))) s16x4 lds_v4;
+    // generic -> LDS address-space casts (the tiles live in __shared__ memory)
+    lds_v4* p0 = (lds_v4*)(T*)(s + key * ld + col);
+    lds_v4* p1 = (lds_v4*)(T*)(s + (key + 8) * ld + col);
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    f = __builtin_bit_cast(bf16x8, v);
   } else {
-    f = st[d * ld + g * 32 + KeyPerm<float>::key(u, h, 0)];
+    const int h = lane >> 5;
+    const int key = g * 32 + (u >> 2) * 8 + h * 4 + (u & 3);
+    const int d = d0 + (lane & 31);
+    f = d < dmax ? s[key * ld + d] : 0.f;
   }
   return f;
 }
@@ -107,25 +140,43 @@ TTT_DEV typename AT<T>::frag acc_frag(const f32x16& acc, int u) {
   return f;
 }
 
-// Cooperative copy of `rows` rows (rows of length HD, global row stride ld)
-// into LDS as row-major [rows][HD+PAD] and/or transposed [HD][rows+PAD].
-// Global rows come from row_ptr(i) (nullptr = zero row).
-template <typename T, int HD, int ROWS, bool ROWMAJ, bool TRANS, typename F>
-TTT_DEV void stage_rows(T* s_row, T* s_tr, F row_ptr) {
+// Registers holding one ROWS x HD tile between its global load and its LDS
+// store (LDS row stride LD). Rows r < nvalid come from base + r*ld, the others
+// are zero.
+template <typename T, int HD, int ROWS, int LD>
+struct Stage {
   typedef AT<T> A;
   typedef typename A::vec V;
-  constexpr int VPR = HD / A::VEC;
-  constexpr int NV = ROWS * VPR;
-  for (int vi = threadIdx.x; vi < NV; vi += NT) {
-    const int r = vi / VPR, c = (vi % VPR) * A::VEC;
-    const T* src = row_ptr(r);
-    V v = src ? *reinterpret_cast<const V*>(src + c) : V{};
-    if constexpr (ROWMAJ) *reinterpret_cast<V*>(s_row + r * (HD + A::PAD) + c) = v;
-    if constexpr (TRANS) {
+  static constexpr int VPR = HD / A::VEC;
+  static constexpr int NV = (ROWS * VPR + NT - 1) / NT;
+  V v[NV];
+  TTT_DEV void load(const T* base, int64_t ld, int nvalid) {
 #pragma unroll
-      for (int e = 0; e < A::VEC; ++e) s_tr[(c + e) * (ROWS + A::PAD) + r] = v[e];
+    for (int i = 0; i < NV; ++i) {
+      const int vi = i * NT + threadIdx.x;
+      if (vi < ROWS * VPR) {
+        const int r = vi / VPR;
+        v[i] = r < nvalid ? *reinterpret_cast<const V*>(base + r * ld + (vi % VPR) * A::VEC) : V{};
+      }
     }
   }
+  TTT_DEV void store(T* s) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = i * NT + threadIdx.x;
+      if (vi < ROWS * VPR)
+        *reinterpret_cast<V*>(s + (vi / VPR) * LD + (vi % VPR) * A::VEC) = v[i];
+    }
+  }
+};
+
+// key-tile range [jb, je) (positions, multiples of BKEY) of split `sp`
+TTT_DEV void split_range(int j_start, int hi, int nsplit, int sp, int* jb, int* je) {
+  const int ntiles = (hi - j_start) / BKEY + 1;
+  const int per = (ntiles + nsplit - 1) / nsplit;
+  const int t0 = min(ntiles, per * sp), t1 = min(ntiles, per * (sp + 1));
+  *jb = j_start + t0 * BKEY;
+  *je = j_start + t1 * BKEY;  // exclusive
 }
 
 // ============================== forward ==============================
@@ -133,46 +184,46 @@ TTT_DEV void stage_rows(T* s_row, T* s_tr, F row_ptr) {
 template <typename T, int HD>
 __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnArgs a) {
   typedef AT<T> A;
-  constexpr int LDK = HD + A::PAD, LDV = BKEY + A::PAD;
+  constexpr int LDK = HD + A::PADR, LDV = HD + A::PADT;
   constexpr int NKS = HD / A::KS;               // k-steps over the head dim
   constexpr int DB = HD >= 32 ? HD / 32 : 1;    // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) T sK[BKEY * LDK];
-  __shared__ __attribute__((aligned(16))) T sVt[HD * LDV];
+  __shared__ __attribute__((aligned(16))) T sK[2][BKEY * LDK];
+  __shared__ __attribute__((aligned(16))) T sV[2][BKEY * LDV];
 
-  const int s = blockIdx.z, h = blockIdx.y;
+  const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
+  const int s = blockIdx.z / nsplit, sp = blockIdx.z % nsplit, h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hl = lane >> 5;
   const int M = a.M;
-  const int qb0 = blockIdx.x * (4 * WQ);
+  const int qb0 = blockIdx.x * QB;
   const int qw0 = qb0 + w * WQ;
   const int q = qw0 + (lane & 31);
   const bool qvalid = q < M;
-  const int64_t pq = a.pos0 + (qvalid ? q : M - 1);
-  const int64_t win = a.window;
-  const T* Q = reinterpret_cast<const T*>(a.q);
+  const int pos0 = (int)a.pos0;                // positions fit in 31 bits
+  const int pq = pos0 + (qvalid ? q : M - 1);
+  const int win = a.window;
   const T* Kc = reinterpret_cast<const T*>(a.kc) + s * a.seq_stride + h * a.hd;
   const T* Vc = reinterpret_cast<const T*>(a.vc) + s * a.seq_stride + h * a.hd;
 
-  // Q fragments (B operand: query on lanes)
   typename A::frag qf[NKS];
   {
-    const T* qrow = Q + ((int64_t)s * M + (qvalid ? q : 0)) * a.ldq + h * a.hd;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)s * M + (qvalid ? q : 0)) * a.ldq + h * a.hd;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (sizeof(T) == 2)
         qf[ks] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hl * 8) : bf16x8{};
-      } else {
+      else
         qf[ks] = qvalid ? qrow[ks * 2 + hl] : 0.f;
-      }
     }
   }
 
-  const int qlast_blk = min(qb0 + 4 * WQ, M) - 1;
-  const int64_t lo = max((int64_t)0, a.pos0 + qb0 - win + 1);
-  const int64_t hi = a.pos0 + qlast_blk;
-  const int64_t j_start = lo & ~(int64_t)(BKEY - 1);
+  const int qlast_blk = min(qb0 + QB, M) - 1;
+  const int lo = max(0, pos0 + qb0 - win + 1);
+  const int hi = pos0 + qlast_blk;
+  int jb, je;
+  split_range(lo & ~(BKEY - 1), hi, nsplit, sp, &jb, &je);
   const bool wactive = qw0 < M;
-  const int64_t wfirst = a.pos0 + qw0;
-  const int64_t wlast = a.pos0 + min(qw0 + WQ, M) - 1;
+  const int wfirst = pos0 + qw0;
+  const int wlast = pos0 + min(qw0 + WQ, M) - 1;
 
   const float c2 = a.scale * LOG2E;
   float m_i = NEG_BIG, l_i = 0.f;
@@ -180,92 +231,147 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
 
-  for (int64_t j0 = j_start; j0 <= hi; j0 += BKEY) {
-    __syncthreads();
-    {
-      auto rp = [&](int r) -> const T* {
-        const int64_t j = j0 + r;
-        if (j < 0 || j > hi) return nullptr;
-        return Kc + (j % a.cap) * a.ldk;
-      };
-      stage_rows<T, HD, BKEY, true, false>(sK, nullptr, rp);
-      auto rv = [&](int r) -> const T* {
-        const int64_t j = j0 + r;
-        if (j < 0 || j > hi) return nullptr;
-        return Vc + (j % a.cap) * a.ldk;
-      };
-      stage_rows<T, HD, BKEY, false, true>(nullptr, sVt, rv);
-    }
-    __syncthreads();
-    if (!wactive) continue;
-    if (j0 > wlast || j0 + BKEY - 1 <= wfirst - win) continue;
-    const bool full = (j0 + BKEY - 1 <= wfirst) && (j0 > wlast - win);
+  Stage<T, HD, BKEY, LDK> stK;
+  Stage<T, HD, BKEY, LDV> stV;
+  // a 64-aligned key tile occupies consecutive ring slots (cap % 64 == 0)
+  auto load_tile = [&](int j0) {
+    const int64_t off = (int64_t)(j0 % a.cap) * a.ldk;
+    const int nvalid = min(BKEY, hi - j0 + 1);
+    stK.load(Kc + off, a.ldk, nvalid);
+    stV.load(Vc + off, a.ldk, nvalid);
+  };
+  if (jb < je) {
+    load_tile(jb);
+    stK.store(sK[0]);
+    stV.store(sV[0]);
+  }
+  __syncthreads();
 
-    f32x16 st[2];
+  int buf = 0;
+  for (int j0 = jb; j0 < je; j0 += BKEY, buf ^= 1) {
+    const bool more = j0 + BKEY < je;
+    if (more) load_tile(j0 + BKEY);
+    const T* cK = sK[buf];
+    const T* cV = sV[buf];
+    if (wactive && !(j0 > wlast || j0 + BKEY - 1 <= wfirst - win)) {
+      const bool full = (j0 + BKEY - 1 <= wfirst) && (j0 > wlast - win);
+      f32x16 st[2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      st[g] = f32x16{};
+      for (int g = 0; g < 2; ++g) {
+        st[g] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        typename A::frag kf = lds_frag<T>(sK, LDK, g * 32 + (lane & 31), ks * A::KS + hl * (A::KS / 2));
-        st[g] = mfma(kf, qf[ks], st[g]);
+        for (int ks = 0; ks < NKS; ++ks)
+          st[g] = mfma(lds_frag<T>(cK, LDK, g * 32 + (lane & 31), ks * A::KS + hl * (A::KS / 2)), qf[ks], st[g]);
       }
+      if (!full) {
+        // visible iff pq - win < j <= pq, i.e. 0 <= pq - j < win
+        const int dj = pq - (j0 + hl * 4);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned t = (unsigned)(dj - g * 32 - (r >> 2) * 8 - (r & 3));
+            if (t >= (unsigned)win) st[g][r] = -INFINITY;
+          }
+      }
+      // max of the raw scores, then one fma per score into exp2
+      float mx = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[g][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+      if (__any(mx > m_i + RESCALE_SLACK)) {   // wave-uniform branch
+        const float m_new = fmaxf(m_i, mx);
+        const float alpha = ex2(m_i - m_new);
+        l_i *= alpha;
+        m_i = m_new;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[i] *= alpha;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = ex2(fmaf(st[g][r], c2, -m_i));
+          st[g][r] = pv;
+          rs += pv;
+        }
+      l_i += rs;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int u = 0; u < KSteps<T>::N; ++u) {
+          typename A::frag pf = acc_frag<T>(st[g], u);
+#pragma unroll
+          for (int i = 0; i < DB; ++i) {
+            typename A::frag vf = (i * 32 < HD) ? lds_frag_tr<T>(cV, LDV, i * 32, g, u, lane, HD) : typename A::frag{};
+            o[i] = mfma(vf, pf, o[i]);
+          }
+        }
     }
-    float mx = NEG_BIG;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = st[g][r] * c2;
-        if (!full) {
-          const int64_t j = j0 + g * 32 + acc_row(r, hl);
-          if (!(j <= pq && j > pq - win)) v = -INFINITY;
-        }
-        st[g][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_i, mx);
-    const float alpha = exp2f(m_i - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = exp2f(st[g][r] - m_new);
-        st[g][r] = pv;
-        rs += pv;
-      }
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] *= alpha;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int u = 0; u < KeyPerm<T>::STEPS; ++u) {
-        typename A::frag pf = acc_frag<T>(st[g], u);
-#pragma unroll
-        for (int i = 0; i < DB; ++i) {
-          const int d = i * 32 + (lane & 31);
-          typename A::frag vf = d < HD ? lds_frag_perm<T>(sVt, LDV, d, g, u, hl) : typename A::frag{};
-          o[i] = mfma(vf, pf, o[i]);
-        }
-      }
+    if (more) {
+      stK.store(sK[buf ^ 1]);
+      stV.store(sV[buf ^ 1]);
+    }
+    __syncthreads();
   }
 
   if (!wactive || !qvalid) return;
   const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
-  const float inv = 1.f / l_tot;
-  T* O = reinterpret_cast<T*>(a.o) + ((int64_t)s * M + q) * a.ldo + h * a.hd;
+  if (nsplit == 1) {
+    const float inv = 1.f / l_tot;
+    T* O = reinterpret_cast<T*>(a.o) + ((int64_t)s * M + q) * a.ldo + h * a.hd;
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d = i * 32 + acc_row(r, hl);
-      if (d < HD) O[d] = from_f32<T>(o[i][r] * inv);
+      for (int r = 0; r < 16; ++r) {
+        const int d = i * 32 + acc_row(r, hl);
+        if (d < HD) O[d] = from_f32<T>(o[i][r] * inv);
+      }
+    if (hl == 0) a.lse[((int64_t)s * a.H + h) * M + q] = m_i * LN2 + logf(l_tot);
+  } else {
+    // partial: normalized O_s (fp32), row max (log2 units) and row sum
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t row = (int64_t)s * M + q;
+    float* O = a.part_o + ((int64_t)sp * a.B * M + row) * a.ldo + h * a.hd;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = i * 32 + acc_row(r, hl);
+        if (d < HD) O[d] = o[i][r] * inv;
+      }
+    if (hl == 0) {
+      const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * M + q;
+      a.part_m[li] = m_i;
+      a.part_l[li] = l_tot;
     }
-  if (hl == 0) a.lse[((int64_t)s * a.H + h) * M + q] = m_i * LN2 + logf(l_tot);
+  }
+}
+
+// merge split partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - m)
+template <typename T>
+__global__ void attn_combine_kernel(AttnArgs a) {
+  const int64_t row = blockIdx.x;  // s*M + q
+  const int s = row / a.M, q = row % a.M;
+  const int HD = a.H * a.hd;
+  for (int c = threadIdx.x; c < HD; c += blockDim.x) {
+    const int h = c / a.hd;
+    float m = NEG_BIG;
+    for (int sp = 0; sp < a.nsplit; ++sp)
+      m = fmaxf(m, a.part_m[(((int64_t)sp * a.B + s) * a.H + h) * a.M + q]);
+    float wsum = 0.f, acc = 0.f;
+    for (int sp = 0; sp < a.nsplit; ++sp) {
+      const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * a.M + q;
+      const float wgt = a.part_l[li] * ex2(a.part_m[li] - m);
+      wsum += wgt;
+      acc += wgt * a.part_o[((int64_t)sp * a.B * a.M + row) * a.ldo + c];
+    }
+    reinterpret_cast<T*>(a.o)[row * a.ldo + c] = from_f32<T>(acc / wsum);
+    if (c % a.hd == 0) a.lse[((int64_t)s * a.H + h) * a.M + q] = m * LN2 + logf(wsum);
+  }
 }
 
 // ============================== backward: dQ ==============================
@@ -273,22 +379,23 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnArgs a) {
 template <typename T, int HD>
 __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(AttnArgs a) {
   typedef AT<T> A;
-  constexpr int LDK = HD + A::PAD, LDT = BKEY + A::PAD;
+  constexpr int LDK = HD + A::PADT, LDV = HD + A::PADR;
   constexpr int NKS = HD / A::KS;
   constexpr int DB = HD >= 32 ? HD / 32 : 1;
-  __shared__ __attribute__((aligned(16))) T sK[BKEY * LDK];
-  __shared__ __attribute__((aligned(16))) T sV[BKEY * LDK];
-  __shared__ __attribute__((aligned(16))) T sKt[HD * LDT];
+  __shared__ __attribute__((aligned(16))) T sK[2][BKEY * LDK];
+  __shared__ __attribute__((aligned(16))) T sV[2][BKEY * LDV];
 
-  const int s = blockIdx.z, h = blockIdx.y;
+  const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
+  const int s = blockIdx.z / nsplit, sp = blockIdx.z % nsplit, h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hl = lane >> 5;
   const int M = a.M;
-  const int qb0 = blockIdx.x * (4 * WQ);
+  const int qb0 = blockIdx.x * QB;
   const int qw0 = qb0 + w * WQ;
   const int q = qw0 + (lane & 31);
   const bool qvalid = q < M;
-  const int64_t pq = a.pos0 + (qvalid ? q : M - 1);
-  const int64_t win = a.window;
+  const int pos0 = (int)a.pos0;
+  const int pq = pos0 + (qvalid ? q : M - 1);
+  const int win = a.window;
   const T* Kc = reinterpret_cast<const T*>(a.kc) + s * a.seq_stride + h * a.hd;
   const T* Vc = reinterpret_cast<const T*>(a.vc) + s * a.seq_stride + h * a.hd;
 
@@ -311,77 +418,83 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(AttnArgs a) {
   const float lse2 = qvalid ? a.lse[li] * LOG2E : 0.f;
   const float dlt = qvalid ? a.delta[li] : 0.f;
 
-  const int qlast_blk = min(qb0 + 4 * WQ, M) - 1;
-  const int64_t lo = max((int64_t)0, a.pos0 + qb0 - win + 1);
-  const int64_t hi = a.pos0 + qlast_blk;
-  const int64_t j_start = lo & ~(int64_t)(BKEY - 1);
+  const int qlast_blk = min(qb0 + QB, M) - 1;
+  const int lo = max(0, pos0 + qb0 - win + 1);
+  const int hi = pos0 + qlast_blk;
+  int jb, je;
+  split_range(lo & ~(BKEY - 1), hi, nsplit, sp, &jb, &je);
   const bool wactive = qw0 < M;
-  const int64_t wfirst = a.pos0 + qw0;
-  const int64_t wlast = a.pos0 + min(qw0 + WQ, M) - 1;
+  const int wfirst = pos0 + qw0;
+  const int wlast = pos0 + min(qw0 + WQ, M) - 1;
   const float c2 = a.scale * LOG2E;
 
   f32x16 dq[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
 
-  for (int64_t j0 = j_start; j0 <= hi; j0 += BKEY) {
-    __syncthreads();
-    {
-      auto rk = [&](int r) -> const T* {
-        const int64_t j = j0 + r;
-        if (j < 0 || j > hi) return nullptr;
-        return Kc + (j % a.cap) * a.ldk;
-      };
-      stage_rows<T, HD, BKEY, true, true>(sK, sKt, rk);
-      auto rv = [&](int r) -> const T* {
-        const int64_t j = j0 + r;
-        if (j < 0 || j > hi) return nullptr;
-        return Vc + (j % a.cap) * a.ldk;
-      };
-      stage_rows<T, HD, BKEY, true, false>(sV, nullptr, rv);
-    }
-    __syncthreads();
-    if (!wactive) continue;
-    if (j0 > wlast || j0 + BKEY - 1 <= wfirst - win) continue;
-    const bool full = (j0 + BKEY - 1 <= wfirst) && (j0 > wlast - win);
+  Stage<T, HD, BKEY, LDK> stK;
+  Stage<T, HD, BKEY, LDV> stV;
+  auto load_tile = [&](int j0) {
+    const int64_t off = (int64_t)(j0 % a.cap) * a.ldk;
+    const int nvalid = min(BKEY, hi - j0 + 1);
+    stK.load(Kc + off, a.ldk, nvalid);
+    stV.load(Vc + off, a.ldk, nvalid);
+  };
+  if (jb < je) {
+    load_tile(jb);
+    stK.store(sK[0]);
+    stV.store(sV[0]);
+  }
+  __syncthreads();
 
-    f32x16 p[2], dp[2];
+  int buf = 0;
+  for (int j0 = jb; j0 < je; j0 += BKEY, buf ^= 1) {
+    const bool more = j0 + BKEY < je;
+    if (more) load_tile(j0 + BKEY);
+    const T* cK = sK[buf];
+    const T* cV = sV[buf];
+    if (wactive && !(j0 > wlast || j0 + BKEY - 1 <= wfirst - win)) {
+      const bool full = (j0 + BKEY - 1 <= wfirst) && (j0 > wlast - win);
+      f32x16 p[2], dp[2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      p[g] = f32x16{};
-      dp[g] = f32x16{};
+      for (int g = 0; g < 2; ++g) {
+        p[g] = f32x16{};
+        dp[g] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int row = g * 32 + (lane & 31), kk = ks * A::KS + hl * (A::KS / 2);
-        p[g] = mfma(lds_frag<T>(sK, LDK, row, kk), qf[ks], p[g]);
-        dp[g] = mfma(lds_frag<T>(sV, LDK, row, kk), df[ks], dp[g]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = p[g][r] * c2;
-        if (!full) {
-          const int64_t j = j0 + g * 32 + acc_row(r, hl);
-          if (!(j <= pq && j > pq - win)) sv = -INFINITY;
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int row = g * 32 + (lane & 31), kk = ks * A::KS + hl * (A::KS / 2);
+          p[g] = mfma(lds_frag<T>(cK, LDK, row, kk), qf[ks], p[g]);
+          dp[g] = mfma(lds_frag<T>(cV, LDV, row, kk), df[ks], dp[g]);
         }
-        const float pr = exp2f(sv - lse2);
-        p[g][r] = pr * (dp[g][r] - dlt);  // dS
+        const int dj = pq - (j0 + g * 32 + hl * 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = ex2(fmaf(p[g][r], c2, -lse2));
+          if (!full && (unsigned)(dj - (r >> 2) * 8 - (r & 3)) >= (unsigned)win) pr = 0.f;
+          p[g][r] = pr * (dp[g][r] - dlt);  // dS
+        }
       }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int u = 0; u < KSteps<T>::N; ++u) {
+          typename A::frag sf = acc_frag<T>(p[g], u);
+#pragma unroll
+          for (int i = 0; i < DB; ++i) {
+            typename A::frag kf = (i * 32 < HD) ? lds_frag_tr<T>(cK, LDK, i * 32, g, u, lane, HD) : typename A::frag{};
+            dq[i] = mfma(kf, sf, dq[i]);
+          }
+        }
     }
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int u = 0; u < KeyPerm<T>::STEPS; ++u) {
-        typename A::frag sf = acc_frag<T>(p[g], u);
-#pragma unroll
-        for (int i = 0; i < DB; ++i) {
-          const int d = i * 32 + (lane & 31);
-          typename A::frag kf = d < HD ? lds_frag_perm<T>(sKt, LDT, d, g, u, hl) : typename A::frag{};
-          dq[i] = mfma(kf, sf, dq[i]);
-        }
-      }
+    if (more) {
+      stK.store(sK[buf ^ 1]);
+      stV.store(sV[buf ^ 1]);
+    }
+    __syncthreads();
   }
   if (!wactive || !qvalid) return;
-  float* out = a.dq + ((int64_t)s * M + q) * a.lddq + h * a.hd;
+  // split sp writes its own slice of dq (the slices are summed by the caller's pack)
+  float* out = a.dq + (int64_t)sp * a.B * M * a.lddq + ((int64_t)s * M + q) * a.lddq + h * a.hd;
 #pragma unroll
   for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -398,28 +511,29 @@ constexpr int BQT = 64;  // query tile of the key-owned kernel
 template <typename T, int HD>
 __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(AttnArgs a) {
   typedef AT<T> A;
-  constexpr int LDR = HD + A::PAD, LDT = BQT + A::PAD;
+  constexpr int LD = HD + A::PADT;
   constexpr int NKS = HD / A::KS;
   constexpr int DB = HD >= 32 ? HD / 32 : 1;
-  __shared__ __attribute__((aligned(16))) T sQ[BQT * LDR];
-  __shared__ __attribute__((aligned(16))) T sD[BQT * LDR];
-  __shared__ __attribute__((aligned(16))) T sQt[HD * LDT];
-  __shared__ __attribute__((aligned(16))) T sDt[HD * LDT];
-  __shared__ float sL[BQT], sDl[BQT];
+  __shared__ __attribute__((aligned(16))) T sQ[2][BQT * LD];
+  __shared__ __attribute__((aligned(16))) T sD[2][BQT * LD];
+  __shared__ float sL[2][BQT], sDl[2][BQT];
 
   const int s = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hl = lane >> 5;
   const int M = a.M;
-  const int kb0 = blockIdx.x * (4 * WQ);
+  const int kb0 = blockIdx.x * QB;
   const int kw0 = kb0 + w * WQ;
   const int kr = kw0 + (lane & 31);     // key row within the chunk
   const bool kvalid = kr < M;
-  const int64_t pk = a.pos0 + (kvalid ? kr : M - 1);
-  const int64_t win = a.window;
+  const int pos0 = (int)a.pos0;
+  const int pk = pos0 + (kvalid ? kr : M - 1);
+  const int win = a.window;
   const T* Kc = reinterpret_cast<const T*>(a.kc) + s * a.seq_stride + h * a.hd;
   const T* Vc = reinterpret_cast<const T*>(a.vc) + s * a.seq_stride + h * a.hd;
   const T* Q = reinterpret_cast<const T*>(a.q) + (int64_t)s * M * a.ldq + h * a.hd;
   const T* DO = reinterpret_cast<const T*>(a.dout) + (int64_t)s * M * a.lddo + h * a.hd;
+  const float* LSE = a.lse + ((int64_t)s * a.H + h) * M;
+  const float* DLT = a.delta + ((int64_t)s * a.H + h) * M;
 
   typename A::frag kf[NKS], vf[NKS];
   {
@@ -437,80 +551,94 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
   }
   const float c2 = a.scale * LOG2E;
-  const int klast_blk = min(kb0 + 4 * WQ, M) - 1;
+  const int klast_blk = min(kb0 + QB, M) - 1;
   const bool wactive = kw0 < M;
   const int wk_first = kw0, wk_last = min(kw0 + WQ, M) - 1;
   // queries (rows) that can see keys of this block: [kb0, klast_blk + win - 1]
-  const int q_end = (int)min((int64_t)M, (int64_t)klast_blk + win);
+  const int q_end = min(M, klast_blk + win);
   const int q_start = kb0 & ~(BQT - 1);
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
-  for (int q0 = q_start; q0 < q_end; q0 += BQT) {
-    __syncthreads();
-    {
-      auto rq = [&](int r) -> const T* {
-        const int qi = q0 + r;
-        return qi < M ? Q + (int64_t)qi * a.ldq : nullptr;
-      };
-      stage_rows<T, HD, BQT, true, true>(sQ, sQt, rq);
-      auto rd = [&](int r) -> const T* {
-        const int qi = q0 + r;
-        return qi < M ? DO + (int64_t)qi * a.lddo : nullptr;
-      };
-      stage_rows<T, HD, BQT, true, true>(sD, sDt, rd);
-      for (int r = threadIdx.x; r < BQT; r += NT) {
-        const int qi = q0 + r;
-        const int64_t li = ((int64_t)s * a.H + h) * M + qi;
-        sL[r] = qi < M ? a.lse[li] * LOG2E : 0.f;
-        sDl[r] = qi < M ? a.delta[li] : 0.f;
-      }
-    }
-    __syncthreads();
-    if (!wactive) continue;
-    // does any (query in tile, key in wave) pair satisfy pk <= pq < pk + win ?
-    if (q0 + BQT - 1 < wk_first || q0 > wk_last + win - 1) continue;
+  Stage<T, HD, BQT, LD> stQ, stD;
+  float nl = 0.f, nd = 0.f;
 
-    f32x16 p[2], dp[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {   // 32-query groups of the tile
-      p[g] = f32x16{};
-      dp[g] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int row = g * 32 + (lane & 31), kk = ks * A::KS + hl * (A::KS / 2);
-        p[g] = mfma(lds_frag<T>(sQ, LDR, row, kk), kf[ks], p[g]);
-        dp[g] = mfma(lds_frag<T>(sD, LDR, row, kk), vf[ks], dp[g]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = g * 32 + acc_row(r, hl);
-        const int qi = q0 + qr;
-        const int64_t pq = a.pos0 + qi;
-        float sv = p[g][r] * c2;
-        if (!(kvalid && qi < M && pk <= pq && pk > pq - win)) sv = -INFINITY;
-        const float pr = exp2f(sv - sL[qr]);
-        p[g][r] = pr;
-        dp[g][r] = pr * (dp[g][r] - sDl[qr]);  // dS
-      }
+  auto ld_stats = [&](int q0) {
+    const int r = threadIdx.x, qi = q0 + r;
+    if (r < BQT) {
+      nl = qi < M ? LSE[qi] * LOG2E : 0.f;
+      nd = qi < M ? DLT[qi] : 0.f;
     }
+  };
+  auto st_stats = [&](int b) {
+    if (threadIdx.x < BQT) { sL[b][threadIdx.x] = nl; sDl[b][threadIdx.x] = nd; }
+  };
+  if (q_start < q_end) {
+    stQ.load(Q + (int64_t)q_start * a.ldq, a.ldq, M - q_start);
+    stD.load(DO + (int64_t)q_start * a.lddo, a.lddo, M - q_start);
+    ld_stats(q_start);
+    stQ.store(sQ[0]);
+    stD.store(sD[0]);
+    st_stats(0);
+  }
+  __syncthreads();
+
+  int buf = 0;
+  for (int q0 = q_start; q0 < q_end; q0 += BQT, buf ^= 1) {
+    const bool more = q0 + BQT < q_end;
+    if (more) {
+      stQ.load(Q + (int64_t)(q0 + BQT) * a.ldq, a.ldq, M - q0 - BQT);
+      stD.load(DO + (int64_t)(q0 + BQT) * a.lddo, a.lddo, M - q0 - BQT);
+      ld_stats(q0 + BQT);
+    }
+    const T* cQ = sQ[buf];
+    const T* cD = sD[buf];
+    // does any (query in tile, key in wave) pair satisfy pk <= pq < pk + win ?
+    if (wactive && !(q0 + BQT - 1 < wk_first || q0 > wk_last + win - 1)) {
+      f32x16 p[2], dp[2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < 2; ++g) {   // 32-query groups of the tile
+        p[g] = f32x16{};
+        dp[g] = f32x16{};
 #pragma unroll
-      for (int u = 0; u < KeyPerm<T>::STEPS; ++u) {
-        typename A::frag pf = acc_frag<T>(p[g], u);
-        typename A::frag sf = acc_frag<T>(dp[g], u);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int row = g * 32 + (lane & 31), kk = ks * A::KS + hl * (A::KS / 2);
+          p[g] = mfma(lds_frag<T>(cQ, LD, row, kk), kf[ks], p[g]);
+          dp[g] = mfma(lds_frag<T>(cD, LD, row, kk), vf[ks], dp[g]);
+        }
+        // visible iff 0 <= pq - pk < win, pq = pos0 + q0 + qr, and the query row exists
+        const int dq0 = pos0 + q0 + g * 32 + hl * 4 - pk;
 #pragma unroll
-        for (int i = 0; i < DB; ++i) {
-          const int d = i * 32 + (lane & 31);
-          typename A::frag dof = d < HD ? lds_frag_perm<T>(sDt, LDT, d, g, u, hl) : typename A::frag{};
-          typename A::frag qtf = d < HD ? lds_frag_perm<T>(sQt, LDT, d, g, u, hl) : typename A::frag{};
-          dv[i] = mfma(dof, pf, dv[i]);
-          dk[i] = mfma(qtf, sf, dk[i]);
+        for (int r = 0; r < 16; ++r) {
+          const int qr = g * 32 + acc_row(r, hl);
+          float pr = ex2(fmaf(p[g][r], c2, -sL[buf][qr]));
+          if ((unsigned)(dq0 + (r >> 2) * 8 + (r & 3)) >= (unsigned)win || q0 + qr >= M || !kvalid) pr = 0.f;
+          p[g][r] = pr;
+          dp[g][r] = pr * (dp[g][r] - sDl[buf][qr]);  // dS
         }
       }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int u = 0; u < KSteps<T>::N; ++u) {
+          typename A::frag pf = acc_frag<T>(p[g], u);
+          typename A::frag sf = acc_frag<T>(dp[g], u);
+#pragma unroll
+          for (int i = 0; i < DB; ++i) {
+            if (i * 32 >= HD) continue;
+            dv[i] = mfma(lds_frag_tr<T>(cD, LD, i * 32, g, u, lane, HD), pf, dv[i]);
+            dk[i] = mfma(lds_frag_tr<T>(cQ, LD, i * 32, g, u, lane, HD), sf, dk[i]);
+          }
+        }
+    }
+    if (more) {
+      stQ.store(sQ[buf ^ 1]);
+      stD.store(sD[buf ^ 1]);
+      st_stats(buf ^ 1);
+    }
+    __syncthreads();
   }
   if (!wactive || !kvalid) return;
   float* dko = a.dk + ((int64_t)s * M + kr) * a.lddk + h * a.hd;
@@ -529,17 +657,23 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(AttnArgs a) {
 
 template <typename T, int HD>
 hipError_t fwd_t(const AttnArgs& a, hipStream_t st) {
-  dim3 grid((a.M + 4 * WQ - 1) / (4 * WQ), a.H, a.B);
+  const int ns = a.nsplit > 0 ? a.nsplit : 1;
+  dim3 grid((a.M + QB - 1) / QB, a.H, a.B * ns);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<T>), dim3(a.B * a.M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 template <typename T, int HD>
 hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
-  dim3 grid((a.M + 4 * WQ - 1) / (4 * WQ), a.H, a.B);
+  const int ns = a.nsplit > 0 ? a.nsplit : 1;
+  dim3 grid((a.M + QB - 1) / QB, a.H, a.B * ns);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  dim3 grid2((a.M + QB - 1) / QB, a.H, a.B);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid2, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -563,8 +697,17 @@ hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
   }                                                                         \
   return hipErrorInvalidValue;
 
+int attn_splits(int M, int H, int B, int64_t keys_per_query) {
+  // enough waves to cover the CUs twice, each split keeping >= 8 key tiles
+  const int64_t waves = (int64_t)((M + WQ - 1) / WQ) * H * B;
+  int ns = 1;
+  while (waves * ns < 2048 && keys_per_query / (BKEY * ns * 2) >= 8 && ns < 8) ns *= 2;
+  return ns;
+}
+
 hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
+  if (a.nsplit > 1 && (!a.part_o || !a.part_m || !a.part_l)) return hipErrorInvalidValue;
   TTT_HD_SWITCH(fwd_t)
 }
 

@@ -111,8 +111,8 @@ __global__ void rope_split_kernel(const T* qkv, int S, int H, int hd, int64_t p0
 
 // inverse rotation of dq, dk (fp32 rows [rows][H*hd]); pack [dq | dk | dv] in T
 template <typename T>
-__global__ void rope_bwd_pack_kernel(const float* dq, const float* dk, const float* dv, int S, int H,
-                                     int hd, int64_t p0, const float2* tab, T* out) {
+__global__ void rope_bwd_pack_kernel(const float* dq, int nsplit, int64_t rows, const float* dk, const float* dv,
+                                     int S, int H, int hd, int64_t p0, const float2* tab, T* out) {
   const int64_t r = blockIdx.x;
   const int i = r % S;
   const int64_t pos = p0 + i;
@@ -121,14 +121,19 @@ __global__ void rope_bwd_pack_kernel(const float* dq, const float* dk, const flo
   const float* b = dk + r * HD;
   const float* v = dv + r * HD;
   T* o = out + r * 3 * HD;
+  auto dqv = [&](int c) {
+    float t = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) t += a[sp * rows * HD + c];
+    return t;
+  };
   for (int c = threadIdx.x; c < HD; c += blockDim.x) {
     const int hh = c / hd, e = c % hd;
-    float x = a[c], y = b[c];
+    float x = dqv(c), y = b[c];
     if (tab) {
       const int pe = e < half ? e : e - half;
       const float2 cs = tab[pos * half + pe];
       const int partner = hh * hd + (e < half ? e + half : e - half);
-      const float xp = a[partner], yp = b[partner];
+      const float xp = dqv(partner), yp = b[partner];
       if (e < half) {
         x = x * cs.x + xp * cs.y;
         y = y * cs.x + yp * cs.y;
@@ -390,12 +395,13 @@ hipError_t rope_split_launch(const void* qkv, int rows, int S, int H, int hd, in
   return hipGetLastError();
 }
 
-hipError_t rope_bwd_pack_launch(const float* dq, const float* dk, const float* dv, int rows, int S, int H,
-                                int hd, int64_t p0, const float2* tab, void* dqkv, int dt, hipStream_t st) {
+hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, const float* dv, int rows, int S,
+                                int H, int hd, int64_t p0, const float2* tab, void* dqkv, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  const int64_t R = rows;
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(rope_bwd_pack_kernel<bf16>, dim3(rows), dim3(NT), 0, st, dq, dk, dv, S, H, hd, p0, tab, mp<bf16>(dqkv)),
-      hipLaunchKernelGGL(rope_bwd_pack_kernel<float>, dim3(rows), dim3(NT), 0, st, dq, dk, dv, S, H, hd, p0, tab, mp<float>(dqkv)));
+      hipLaunchKernelGGL(rope_bwd_pack_kernel<bf16>, dim3(rows), dim3(NT), 0, st, dq, nsplit, R, dk, dv, S, H, hd, p0, tab, mp<bf16>(dqkv)),
+      hipLaunchKernelGGL(rope_bwd_pack_kernel<float>, dim3(rows), dim3(NT), 0, st, dq, nsplit, R, dk, dv, S, H, hd, p0, tab, mp<float>(dqkv)));
   return hipGetLastError();
 }
 

@@ -57,24 +57,37 @@ static AttnArgs mk(const void* q, const void* kc, const void* vc, int32_t cap, i
 
 int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
                    float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
-                   float scale, void* stream) {
+                   float scale, int32_t nsplit, float* ws, void* stream) {
   if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
     return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
+  if (nsplit < 1 || nsplit > 8 || (nsplit > 1 && !ws)) return kfail(TTT_EINVAL, "nsplit in 1..8, ws for > 1");
   AttnArgs a = mk(q, kc, vc, cap, B, M, H, hd, pos0, window, scale);
   a.o = o; a.ldo = (int64_t)H * hd; a.lse = lse;
+  a.nsplit = nsplit;
+  if (nsplit > 1) {
+    a.part_o = ws;
+    a.part_m = ws + (int64_t)nsplit * B * M * H * hd;
+    a.part_l = a.part_m + (int64_t)nsplit * B * H * M;
+  }
   return kdone(attn_fwd_launch(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, const float* lse,
                    const void* dout, const float* delta, float* dq, float* dk, float* dv, int32_t B, int32_t M,
-                   int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, void* stream) {
+                   int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, int32_t nsplit, void* stream) {
   if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
     return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
+  if (nsplit < 1 || nsplit > 8) return kfail(TTT_EINVAL, "nsplit in 1..8");
   AttnArgs a = mk(q, kc, vc, cap, B, M, H, hd, pos0, window, scale);
   const int64_t HD = (int64_t)H * hd;
   a.lse = const_cast<float*>(lse); a.dout = dout; a.lddo = HD; a.delta = delta;
   a.dq = dq; a.lddq = HD; a.dk = dk; a.dv = dv; a.lddk = HD;
+  a.nsplit = nsplit;
   return kdone(attn_bwd_launch(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int32_t ttt_k_attn_splits(int32_t M, int32_t H, int32_t B, int64_t keys_per_query) {
+  return attn_splits(M, H, B, keys_per_query);
 }
 
 int ttt_k_attn_delta(int32_t dtype, const void* o, const void* dout, int32_t B, int32_t M, int32_t H, int32_t hd,

@@ -43,12 +43,18 @@ struct AttnArgs {
   // backward
   const void* dout; int64_t lddo;   // dO rows like q
   const float* delta;               // [B][H][M] rowsum(dO * O)
-  float* dq; int64_t lddq;          // fp32 rows like q
+  float* dq; int64_t lddq;          // fp32 rows like q, nsplit slices of B*M rows (summed by the caller)
   float* dk; float* dv; int64_t lddk;  // fp32 [B*M][H*hd] for keys at pos0..pos0+M-1
+  // key-range splits (forward and dq): partial outputs of the forward
+  int nsplit;
+  float* part_o;                    // [nsplit][B*M][ldo]
+  float* part_m; float* part_l;     // [nsplit][B][H][M]
 };
 
 hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st);
 hipError_t attn_bwd_launch(const AttnArgs& a, int dt, hipStream_t st);
+// number of key-range splits that keeps the CUs busy for M queries per sequence
+int attn_splits(int M, int H, int B, int64_t keys_per_query);
 
 // elementwise / row kernels
 hipError_t embed_launch(const int32_t* ids, int64_t ids_seq_stride, int64_t p0, int S, int B,
@@ -61,7 +67,8 @@ hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, 
 hipError_t rope_split_launch(const void* qkv, int rows, int S, int H, int hd, int64_t p0,
                              const float2* rope_tab, void* q, void* kc, void* vc, int cap,
                              int64_t seq_stride, int dt, hipStream_t st);
-hipError_t rope_bwd_pack_launch(const float* dq, const float* dk, const float* dv, int rows, int S,
+// dq holds nsplit slices of rows x H*hd (summed here)
+hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, const float* dv, int rows, int S,
                                 int H, int hd, int64_t p0, const float2* rope_tab, void* dqkv,
                                 int dt, hipStream_t st);
 hipError_t act_fwd_launch(const void* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,

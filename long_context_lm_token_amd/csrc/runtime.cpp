@@ -106,6 +106,9 @@ struct ttt_model {
   void *Tdres = nullptr, *Ta = nullptr, *Tdz = nullptr, *Tn = nullptr;
   float* ws = nullptr;  // split-K partials
   int64_t ws_elems = 0;
+  // key-range splits of the chunk attention: forward partials (dq slices use dq)
+  static constexpr int kMaxSplit = 8;
+  float *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
 
   bool poisoned = false;
   int64_t bytes = 0;
@@ -278,6 +281,9 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       a.seq_stride = (int64_t)m->cap_t * HD; a.cap = m->cap_t; a.o = m->to[j]; a.ldo = HD;
       a.lse = m->tlse[j]; a.M = M; a.H = m->H; a.hd = m->hd; a.B = B; a.pos0 = P0;
       a.window = m->cfg.window; a.scale = m->scale;
+      a.nsplit = std::min(ttt_model::kMaxSplit,
+                          attn_splits(M, m->H, B, std::min<int64_t>(m->cfg.window, P0 + M)));
+      a.part_o = m->part_o; a.part_m = m->part_m; a.part_l = m->part_l;
       hipEvent_t e0;
       prof_begin(m, TTT_PROF_ATTN_FWD, c.st, &e0);
       c.chk(attn_fwd_launch(a, m->dt, c.st), "attn_fwd");
@@ -379,6 +385,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     a.window = m->cfg.window; a.scale = m->scale;
     a.dout = m->dO; a.lddo = HD; a.delta = m->delta; a.dq = m->dq; a.lddq = HD;
     a.dk = m->dk; a.dv = m->dv; a.lddk = HD;
+    a.nsplit = std::min(ttt_model::kMaxSplit, attn_splits(M, m->H, B, std::min<int64_t>(m->cfg.window, P0 + M)));
     {
       hipEvent_t e0;
       prof_begin(m, TTT_PROF_ATTN_BWD, c.st, &e0);
@@ -388,8 +395,8 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       const double inchunk = (double)M * (M + 1) / 2.0;
       prof_end(m, TTT_PROF_ATTN_BWD, c.st, e0, (4.0 * pairs + 4.0 * inchunk) * m->hd * m->H * B);
     }
-    c.chk(rope_bwd_pack_launch(m->dq, m->dk, m->dv, R, M, m->H, m->hd, P0, m->cfg.rope ? m->rope : nullptr,
-                               m->dqkv, m->dt, c.st),
+    c.chk(rope_bwd_pack_launch(m->dq, a.nsplit, m->dk, m->dv, R, M, m->H, m->hd, P0,
+                               m->cfg.rope ? m->rope : nullptr, m->dqkv, m->dt, c.st),
           "rope_bwd");
     c.gemm(EPI_STORE, true, ga(m->dqkv, 3 * HD, m->wqkv_b[l], 3 * HD, m->dn, d, R, d, 3 * HD));
     c.chk(rmsnorm_bwd_launch(m->tx[j], m->tr1[j], m->g_attn[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
@@ -613,7 +620,10 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   m->txL = A.f32(Rt * d); m->trf = A.f32(Rt); m->tlog = A.f32(Rt * V);
   m->tf = A.el(Rt * d); m->tdz = A.el(Rt * V); m->tU = A.el(Rt * d); m->tQKV = A.el(Rt * 3 * HD);
   m->dres = A.f32(Rt * d); m->dn = A.f32(Rt * d); m->dA = A.f32(Rt * hf); m->delta = A.f32(Rt * m->H);
-  m->dq = A.f32(Rt * HD); m->dk = A.f32(Rt * HD); m->dv = A.f32(Rt * HD);
+  m->dq = A.f32(ttt_model::kMaxSplit * Rt * HD); m->dk = A.f32(Rt * HD); m->dv = A.f32(Rt * HD);
+  m->part_o = A.f32(ttt_model::kMaxSplit * Rt * HD);
+  m->part_m = A.f32(ttt_model::kMaxSplit * Rt * m->H);
+  m->part_l = A.f32(ttt_model::kMaxSplit * Rt * m->H);
   m->dres_c = A.el(Rt * d); m->dZ = A.el(Rt * mg * hf); m->dO = A.el(Rt * HD); m->dqkv = A.el(Rt * 3 * HD);
   m->Tdres = A.el(Rt * d); m->Ta = A.el(Rt * ht); m->Tdz = A.el(Rt * mg * ht); m->Tn = A.el(Rt * d);
   m->ws_elems = std::min<int64_t>((int64_t)1 << 26, 8 * Rt * std::max({d, 3 * HD, hf}));

@@ -125,30 +125,35 @@ def attn_case(dtype, B, M, H, hd, pos0, window, seed=0):
 
 @pytest.mark.parametrize("dtype,hd", [(torch.float32, 16), (torch.float32, 64), (torch.bfloat16, 64),
                                       (torch.bfloat16, 128)])
-@pytest.mark.parametrize("B,M,H,pos0,window", [(1, 100, 2, 0, 128), (2, 64, 3, 300, 96),
-                                               (1, 200, 2, 1000, 64), (1, 1, 2, 517, 256)])
-def test_attention_fwd_bwd(dtype, hd, B, M, H, pos0, window):
+@pytest.mark.parametrize("B,M,H,pos0,window,nsplit", [(1, 100, 2, 0, 128, 1), (2, 64, 3, 300, 96, 1),
+                                                      (1, 200, 2, 1000, 64, 1), (1, 1, 2, 517, 256, 1),
+                                                      (1, 130, 2, 900, 512, 4), (2, 64, 3, 1500, 1024, 8),
+                                                      (1, 1, 2, 2000, 1024, 8), (1, 100, 2, 0, 128, 2)])
+def test_attention_fwd_bwd(dtype, hd, B, M, H, pos0, window, nsplit):
     lib = bd.load()
     c = attn_case(dtype, B, M, H, hd, pos0, window)
     HD = H * hd
     scale = 1.0 / math.sqrt(hd)
     o = torch.zeros((B * M, HD), dtype=dtype, device="cuda")
     lse = torch.zeros((B, H, M), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(nsplit * B * M * (HD + 2 * H), device="cuda")
     bd.check(lib.ttt_k_attn_fwd(kdt(dtype), bd.ptr(c["qd"]), bd.ptr(c["kcd"]), bd.ptr(c["vcd"]), c["cap"],
-                                bd.ptr(o), bd.ptr(lse), B, M, H, hd, pos0, window, scale, bd.stream_ptr()),
+                                bd.ptr(o), bd.ptr(lse), B, M, H, hd, pos0, window, scale, nsplit, bd.ptr(ws),
+                                bd.stream_ptr()),
              kernel=True)
     do, dod = rnd((B, M, H, hd), 9, dtype)
     dod = dod.reshape(B * M, HD).contiguous()
     delta = torch.zeros((B, H, M), dtype=torch.float32, device="cuda")
     bd.check(lib.ttt_k_attn_delta(kdt(dtype), bd.ptr(o), bd.ptr(dod), B, M, H, hd, bd.ptr(delta),
                                   bd.stream_ptr()), kernel=True)
-    dq = torch.zeros((B * M, HD), dtype=torch.float32, device="cuda")
-    dk = torch.zeros_like(dq)
-    dv = torch.zeros_like(dq)
+    dqs = torch.zeros((nsplit, B * M, HD), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((B * M, HD), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
     bd.check(lib.ttt_k_attn_bwd(kdt(dtype), bd.ptr(c["qd"]), bd.ptr(c["kcd"]), bd.ptr(c["vcd"]), c["cap"],
-                                bd.ptr(lse), bd.ptr(dod), bd.ptr(delta), bd.ptr(dq), bd.ptr(dk), bd.ptr(dv),
-                                B, M, H, hd, pos0, window, scale, bd.stream_ptr()), kernel=True)
+                                bd.ptr(lse), bd.ptr(dod), bd.ptr(delta), bd.ptr(dqs), bd.ptr(dk), bd.ptr(dv),
+                                B, M, H, hd, pos0, window, scale, nsplit, bd.stream_ptr()), kernel=True)
     sync()
+    dq = dqs.sum(0)
     qpos = np.arange(pos0, pos0 + M)
     kpos = np.arange(c["lo"], pos0 + M)
     o_g = o.float().cpu().numpy().reshape(B, M, H, hd)
