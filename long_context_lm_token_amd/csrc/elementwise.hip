@@ -155,40 +155,81 @@ TTT_DEV float gelu_g(float x) {
 }
 TTT_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
 
-// GELU: a = gelu(z[:, j]); SwiGLU: a = silu(z[:, j]) * z[:, h + j]
+// GELU: a = gelu(z[:, j]); SwiGLU: a = silu(z[:, j]) * z[:, h + j].
+// Each thread handles 8 consecutive columns (16-byte bf16 / 2x16-byte fp32 accesses).
+template <typename T> struct V8;
+template <> struct V8<bf16> {
+  typedef bf16x8 type;
+  TTT_DEV static type load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  TTT_DEV static void store(bf16* p, const float (&v)[8]) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(p) = o;
+  }
+  TTT_DEV static void get(const bf16* p, float (&v)[8]) {
+    const bf16x8 x = load(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+  }
+};
+template <> struct V8<float> {
+  TTT_DEV static void store(float* p, const float (&v)[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  TTT_DEV static void get(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 template <typename T>
 __global__ void act_fwd_kernel(const T* z, int h, int64_t ldz, int glu, T* a, int64_t lda) {
   const int64_t r = blockIdx.y;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int j = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (j >= h) return;
   const T* zr = z + r * ldz;
-  float v;
+  float g[8], o[8];
+  V8<T>::get(zr + j, g);
   if (glu) {
-    const float g = to_f32(zr[j]), u = to_f32(zr[h + j]);
-    v = g * sigm(g) * u;
+    float u[8];
+    V8<T>::get(zr + h + j, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = g[e] * sigm(g[e]) * u[e];
   } else {
-    v = gelu_f(to_f32(zr[j]));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = gelu_f(g[e]);
   }
-  a[r * lda + j] = from_f32<T>(v);
+  V8<T>::store(a + r * lda + j, o);
 }
 
 template <typename T>
 __global__ void act_bwd_kernel(const T* z, const float* da, int hcols, int64_t ldz, int64_t ldda,
                                int64_t up_off, int glu, T* dz, int64_t lddz) {
   const int64_t r = blockIdx.y;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int j = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (j >= hcols) return;
   const T* zr = z + r * ldz;
-  const float g = da[r * ldda + j];
-  T* o = dz + r * lddz;
+  float g[8], zg[8], o1[8];
+  V8<float>::get(da + r * ldda + j, g);
+  V8<T>::get(zr + j, zg);
+  T* out = dz + r * lddz;
   if (glu) {
-    const float zg = to_f32(zr[j]), zu = to_f32(zr[up_off + j]);
-    const float sg = sigm(zg);
-    o[j] = from_f32<T>(g * zu * sg * (1.f + zg * (1.f - sg)));
-    o[up_off + j] = from_f32<T>(g * zg * sg);
+    float zu[8], o2[8];
+    V8<T>::get(zr + up_off + j, zu);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sg = sigm(zg[e]);
+      o1[e] = g[e] * zu[e] * sg * (1.f + zg[e] * (1.f - sg));
+      o2[e] = g[e] * zg[e] * sg;
+    }
+    V8<T>::store(out + up_off + j, o2);
   } else {
-    o[j] = from_f32<T>(g * gelu_g(to_f32(zr[j])));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o1[e] = g[e] * gelu_g(zg[e]);
   }
+  V8<T>::store(out + j, o1);
 }
 
 // delta[s][h][i] = sum_d dO * O for row s*S+i, head h
@@ -408,7 +449,8 @@ hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, co
 hipError_t act_fwd_launch(const void* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
                           int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  dim3 g((h + NT - 1) / NT, rows);
+  if (h % 8 || ldz % 8 || lda % 8) return hipErrorInvalidValue;
+  dim3 g((h / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(act_fwd_kernel<bf16>, g, dim3(NT), 0, st, cp<bf16>(z), h, ldz, glu, mp<bf16>(a), lda),
       hipLaunchKernelGGL(act_fwd_kernel<float>, g, dim3(NT), 0, st, cp<float>(z), h, ldz, glu, mp<float>(a), lda));
@@ -418,7 +460,8 @@ hipError_t act_fwd_launch(const void* z, int rows, int h, int64_t ldz, int glu, 
 hipError_t act_bwd_launch(const void* z, const float* da, int rows, int hcols, int64_t ldz, int64_t ldda,
                           int64_t up_off, int glu, void* dz, int64_t lddz, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  dim3 g((hcols + NT - 1) / NT, rows);
+  if (hcols % 8 || ldz % 8 || ldda % 8 || up_off % 8 || lddz % 8) return hipErrorInvalidValue;
+  dim3 g((hcols / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(act_bwd_kernel<bf16>, g, dim3(NT), 0, st, cp<bf16>(z), da, hcols, ldz, ldda, up_off, glu, mp<bf16>(dz), lddz),
       hipLaunchKernelGGL(act_bwd_kernel<float>, g, dim3(NT), 0, st, cp<float>(z), da, hcols, ldz, ldda, up_off, glu, mp<float>(dz), lddz));

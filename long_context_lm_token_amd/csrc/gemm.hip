@@ -121,6 +121,63 @@ TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
   }
 }
 
+// SGD epilogue with the transposed compute copy written through LDS: the
+// tile's new weights go to LDS as [col][row] (4 consecutive rows per 8-byte
+// store), then each [col] row segment leaves in 16-byte stores. The fp32
+// master and the row-major copy are updated directly (lanes along columns).
+template <typename T, int BM, int BN, int WGM, int WGN>
+TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                 T* lds) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN, TI = WTM / 32, TJ = WTN / 32;
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int LT = BM + 8;  // row stride of the [col][row] staging tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN, hl = lane >> 5;
+  float* Wm = p.Wm + z * p.sW;
+  T* C = p.C ? reinterpret_cast<T*>(p.C) + z * p.sC : nullptr;
+  __syncthreads();  // the main loop's last reads of the operand tiles are done
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int cl = wn * WTN + j * 32 + (lane & 31);
+      const int col = n0 + cl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rl = wm * WTM + i * 32 + q * 8 + hl * 4;
+        bf16x4 nv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + rl + e;
+          float nw = 0.f;
+          if (row < p.M && col < p.N) {
+            float* wp = Wm + (int64_t)row * p.ldw + col;
+            nw = *wp - p.lr * acc[i][j][q * 4 + e];
+            *wp = nw;
+            if (C) C[(int64_t)row * p.ldc + col] = from_f32<T>(nw);
+          }
+          nv[e] = (bf16)nw;
+        }
+        *reinterpret_cast<bf16x4*>(lds + cl * LT + rl) = nv;
+      }
+    }
+  __syncthreads();
+  T* C2 = reinterpret_cast<T*>(p.C2) + z * p.sC2;
+  constexpr int CH = BM / 8;  // 16-byte chunks per column
+  for (int v = threadIdx.x; v < BN * CH; v += NT) {
+    const int cl = v / CH, r0 = (v % CH) * 8;
+    const int col = n0 + cl, row = m0 + r0;
+    if (col >= p.N || row >= p.M) continue;
+    T* dst = C2 + (int64_t)col * p.ldc2 + row;
+    const T* src = lds + cl * LT + r0;
+    if (row + 8 <= p.M && ((uintptr_t)dst & 15) == 0) {
+      *reinterpret_cast<bf16x8*>(dst) = *reinterpret_cast<const bf16x8*>(src);
+    } else {
+      for (int e = 0; e < 8 && row + e < p.M; ++e) dst[e] = src[e];
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int splits, float* part) {
   typedef GT<T> G;
@@ -194,6 +251,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
   }
 
   // ---- epilogue ----
+  if constexpr (EPI == EPI_SGD && sizeof(T) == 2) {
+    if (splits == 1 && p.C2) {
+      sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, &smem[0][0]);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
