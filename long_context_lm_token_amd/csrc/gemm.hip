@@ -125,6 +125,21 @@ TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
 // tile's new weights go to LDS as [col][row] (4 consecutive rows per 8-byte
 // store), then each [col] row segment leaves in 16-byte stores. The fp32
 // master and the row-major copy are updated directly (lanes along columns).
+// Epilogue store when the operand (residual / master value) is already loaded.
+template <int EPI, typename OutT, typename T>
+TTT_DEV void store_out(const GemmArgs& p, int z, int row, int col, float v, float in) {
+  if constexpr (EPI == EPI_STORE) {
+    reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<OutT>(v);
+  } else if constexpr (EPI == EPI_ADD) {
+    reinterpret_cast<float*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = in + v;
+  } else {
+    const float nw = in - p.lr * v;
+    p.Wm[z * p.sW + (int64_t)row * p.ldw + col] = nw;
+    if (p.C) reinterpret_cast<T*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<T>(nw);
+    if (p.C2) reinterpret_cast<T*>(p.C2)[z * p.sC2 + (int64_t)col * p.ldc2 + row] = from_f32<T>(nw);
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN>
 TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
                                  T* lds) {
@@ -137,7 +152,18 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
   T* C = p.C ? reinterpret_cast<T*>(p.C) + z * p.sC : nullptr;
   __syncthreads();  // the main loop's last reads of the operand tiles are done
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int i = 0; i < TI; ++i) {
+    // all master loads of this row block first, so they are in flight together
+    float mv[TJ][16];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+        mv[j][r] = (row < p.M && col < p.N) ? Wm[(int64_t)row * p.ldw + col] : 0.f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int cl = wn * WTN + j * 32 + (lane & 31);
@@ -149,11 +175,9 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + rl + e;
-          float nw = 0.f;
+          const float nw = mv[j][q * 4 + e] - p.lr * acc[i][j][q * 4 + e];
           if (row < p.M && col < p.N) {
-            float* wp = Wm + (int64_t)row * p.ldw + col;
-            nw = *wp - p.lr * acc[i][j][q * 4 + e];
-            *wp = nw;
+            Wm[(int64_t)row * p.ldw + col] = nw;
             if (C) C[(int64_t)row * p.ldc + col] = from_f32<T>(nw);
           }
           nv[e] = (bf16)nw;
@@ -161,6 +185,7 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
         *reinterpret_cast<bf16x4*>(lds + cl * LT + rl) = nv;
       }
     }
+  }
   __syncthreads();
   T* C2 = reinterpret_cast<T*>(p.C2) + z * p.sC2;
   constexpr int CH = BM / 8;  // 16-byte chunks per column
@@ -258,7 +283,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     }
   }
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int i = 0; i < TI; ++i) {
+    // epilogue operands (residual or master) of this row block loaded first
+    float in[TJ][16];
+    if constexpr (EPI != EPI_STORE) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          in[j][r] = 0.f;
+          if (splits == 1 && row < p.M && col < p.N)
+            in[j][r] = EPI == EPI_ADD ? p.R[z * p.sR + (int64_t)row * p.ldr + col]
+                                      : p.Wm[z * p.sW + (int64_t)row * p.ldw + col];
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int col = n0 + wn * WTN + j * 32 + (lane & 31);
@@ -271,9 +312,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
         if (splits > 1)
           part[(((int64_t)blockIdx.y * gridDim.z + z) * p.M + row) * p.N + col] = v;
         else
-          apply<EPI, OutT, T>(p, z, row, col, v);
+          store_out<EPI, OutT, T>(p, z, row, col, v, in[j][r]);
       }
     }
+  }
 }
 
 // sum split-K partials in order and apply the epilogue
