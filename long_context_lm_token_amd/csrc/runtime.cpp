@@ -102,8 +102,12 @@ struct ttt_model {
   float *dres = nullptr, *dn = nullptr, *dA = nullptr, *delta = nullptr, *dq = nullptr, *dk = nullptr,
         *dv = nullptr;
   void *dres_c = nullptr, *dZ = nullptr, *dO = nullptr, *dqkv = nullptr;
-  // token-contiguous operands of the weight-gradient GEMMs: [B][cols][b]
-  void *Tdres = nullptr, *Ta = nullptr, *Tdz = nullptr, *Tn = nullptr;
+  // token-contiguous operands of the weight-gradient GEMMs, per tail block: [B][cols][b]
+  std::vector<void*> Tdres, Ta, Tdz, Tn;
+  // the weight-gradient + SGD GEMMs run on a second stream (default priority),
+  // ordered after the input-gradient GEMMs that read W_c; joined per chunk
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ev;  // pool of ordering events
   float* ws = nullptr;  // split-K partials
   int64_t ws_elems = 0;
   // key-range splits of the chunk attention: forward partials (dq slices use dq)
@@ -185,15 +189,23 @@ struct Ctx {
     }
   }
   // C = A . B^T-ish per GemmArgs, optionally batched over sequences
-  void gemm(int epi, bool out_f32, const GemmArgs& a, int batch = 1) {
+  void gemm(int epi, bool out_f32, const GemmArgs& a, int batch = 1, hipStream_t on = nullptr) {
     // class of this launch for the timing hooks: every GEMM, or the plain
     // store in the compute dtype (forward projections)
     int cls = TTT_PROF_GEMM;
     if (m->prof.cls == TTT_PROF_GEMM_FWD) cls = (epi == EPI_STORE && !out_f32) ? TTT_PROF_GEMM_FWD : -2;
+    hipStream_t s = on ? on : st;
+    // the split-K workspace belongs to the main stream
+    float* ws = on ? nullptr : m->ws;
     hipEvent_t e0;
-    prof_begin(m, cls, st, &e0);
-    chk(gemm_launch(a, m->dt, epi, out_f32, batch, m->ws, m->ws_elems, st), "gemm");
-    prof_end(m, cls, st, e0, 2.0 * a.M * a.N * (double)a.K * batch);
+    prof_begin(m, cls, s, &e0);
+    chk(gemm_launch(a, m->dt, epi, out_f32, batch, ws, on ? 0 : m->ws_elems, s), "gemm");
+    prof_end(m, cls, s, e0, 2.0 * a.M * a.N * (double)a.K * batch);
+  }
+  // `to` waits for everything enqueued so far on `from`
+  void order(hipStream_t from, hipStream_t to, hipEvent_t e) {
+    chk(hipEventRecord(e, from), "event record");
+    chk(hipStreamWaitEvent(to, e, 0), "stream wait");
   }
   void transpose(const void* src, int rows, int cols, int64_t lds, void* dst, int64_t ldd, int batch,
                  int64_t s_src, int64_t s_dst) {
@@ -338,16 +350,18 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     GemmArgs g = ga(m->dres_c, d, m->fb_d[j], d, m->dA, hf, M, hcols, d);
     g.sA = (int64_t)M * d; g.sB = sbd; g.sC = (int64_t)M * hf;
     c.gemm(EPI_STORE, true, g, B);
-    // W_down trainable columns: W^T[d][ht] -= eta * dres^T . A_t
-    c.transpose(m->dres_c, M, d, d, m->Tdres, M, B, (int64_t)M * d, (int64_t)d * M);
-    c.transpose(m->ta[j], M, ht, hf, m->Ta, M, B, (int64_t)M * hf, (int64_t)ht * M);
-    g = ga(m->Tdres, M, m->Ta, M, master ? m->f_d[j] : nullptr, hf, d, ht, M);
+    // W_down trainable columns: W^T[d][ht] -= eta * dres^T . A_t  (side stream,
+    // after the dA GEMM above has read W_c)
+    c.transpose(m->dres_c, M, d, d, m->Tdres[j], M, B, (int64_t)M * d, (int64_t)d * M);
+    c.transpose(m->ta[j], M, ht, hf, m->Ta[j], M, B, (int64_t)M * hf, (int64_t)ht * M);
+    c.order(c.st, m->side, m->ev[2 * j]);
+    g = ga(m->Tdres[j], M, m->Ta[j], M, master ? m->f_d[j] : nullptr, hf, d, ht, M);
     g.sA = (int64_t)d * M; g.sB = (int64_t)ht * M; g.sC = sd;
     g.Wm = master ? m->m_d[j] : static_cast<float*>(m->f_d[j]);
     g.ldw = master ? ht : hf; g.sW = master ? smd : sd;
     g.C2 = m->fb_d[j]; g.ldc2 = d; g.sC2 = sbd;
     g.lr = m->cfg.lr;
-    c.gemm(EPI_SGD, false, g, B);
+    c.gemm(EPI_SGD, false, g, B, m->side);
     c.chk(act_bwd_launch(m->tz[j], m->dA, R, hcols, zw, hf, hf, mg == 2, m->dZ, zw, m->dt, c.st), "act_bwd");
     if (j >= 1) {
       // dn = dZ . W_gu^T (reads W_c before its update below)
@@ -355,20 +369,24 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       g.sA = (int64_t)M * zw; g.sB = sbgu; g.sC = (int64_t)M * d;
       c.gemm(EPI_STORE, true, g, B);
     }
-    // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ_t^T . n
-    c.transpose(m->tn[j], M, d, d, m->Tn, M, B, (int64_t)M * d, (int64_t)d * M);
+    // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ_t^T . n  (side stream)
+    c.transpose(m->tn[j], M, d, d, m->Tn[j], M, B, (int64_t)M * d, (int64_t)d * M);
+    for (int part = 0; part < mg; ++part) {
+      void* tdz = off(m->Tdz[j], (int64_t)part * B * ht * M, es);
+      c.transpose(off(m->dZ, (int64_t)part * hf, es), M, ht, zw, tdz, M, B, (int64_t)M * zw, (int64_t)ht * M);
+    }
+    c.order(c.st, m->side, m->ev[2 * j + 1]);
     for (int part = 0; part < mg; ++part) {
       const int64_t zoff = (int64_t)part * hf;      // column of dZ / row of the forward copy
       const int64_t moff = (int64_t)part * ht * d;  // row block of the master
-      void* tdz = off(m->Tdz, (int64_t)part * B * ht * M, es);
-      c.transpose(off(m->dZ, zoff, es), M, ht, zw, tdz, M, B, (int64_t)M * zw, (int64_t)ht * M);
-      g = ga(tdz, M, m->Tn, M, master ? off(m->f_gu[j], zoff * d, es) : nullptr, d, ht, d, M);
+      void* tdz = off(m->Tdz[j], (int64_t)part * B * ht * M, es);
+      g = ga(tdz, M, m->Tn[j], M, master ? off(m->f_gu[j], zoff * d, es) : nullptr, d, ht, d, M);
       g.sA = (int64_t)ht * M; g.sB = (int64_t)d * M; g.sC = sgu;
       g.Wm = master ? m->m_gu[j] + moff : reinterpret_cast<float*>(off(m->f_gu[j], zoff * d, es));
       g.ldw = d; g.sW = master ? smgu : sgu;
       g.C2 = off(m->fb_gu[j], zoff, es); g.ldc2 = zw; g.sC2 = sbgu;
       g.lr = m->cfg.lr;
-      c.gemm(EPI_SGD, false, g, B);
+      c.gemm(EPI_SGD, false, g, B, m->side);
     }
     if (j == 0) break;
     c.chk(rmsnorm_bwd_launch(m->ty[j], m->tr2[j], m->g_mlp[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
@@ -403,6 +421,9 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
                              c.st),
           "norm_bwd");
   }
+  // the next use of the fast weights (and of the per-block operand copies) waits
+  // for every SGD step of this chunk
+  c.order(m->side, c.st, m->ev[2 * m->nt]);
 }
 
 int finish(Ctx& c) {
@@ -461,6 +482,8 @@ void ttt_model_destroy(ttt_model* m) {
   (void)hipDeviceSynchronize();
   for (void* p : m->allocs) (void)hipFree(p);
   for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
+  for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
+  if (m->side) (void)hipStreamDestroy(m->side);
   delete m;
 }
 
@@ -625,13 +648,31 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   m->part_m = A.f32(ttt_model::kMaxSplit * Rt * m->H);
   m->part_l = A.f32(ttt_model::kMaxSplit * Rt * m->H);
   m->dres_c = A.el(Rt * d); m->dZ = A.el(Rt * mg * hf); m->dO = A.el(Rt * HD); m->dqkv = A.el(Rt * 3 * HD);
-  m->Tdres = A.el(Rt * d); m->Ta = A.el(Rt * ht); m->Tdz = A.el(Rt * mg * ht); m->Tn = A.el(Rt * d);
+  m->Tdres.resize(nt); m->Ta.resize(nt); m->Tdz.resize(nt); m->Tn.resize(nt);
+  for (int j = 0; j < nt; ++j) {
+    m->Tdres[j] = A.el(Rt * d); m->Ta[j] = A.el(Rt * ht); m->Tdz[j] = A.el(Rt * mg * ht); m->Tn[j] = A.el(Rt * d);
+  }
   m->ws_elems = std::min<int64_t>((int64_t)1 << 26, 8 * Rt * std::max({d, 3 * HD, hf}));
   m->ws = A.f32(m->ws_elems);
   if (!A.ok) {
     rc = fail(TTT_ENOMEM, A.why);
     ttt_model_destroy(m);
     return rc;
+  }
+  if (hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking) != hipSuccess) {
+    m->side = nullptr;
+    rc = fail(TTT_EHIP, "side stream creation failed");
+    ttt_model_destroy(m);
+    return rc;
+  }
+  for (int i = 0; i < 2 * nt + 2; ++i) {
+    hipEvent_t e;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+      rc = fail(TTT_EHIP, "event creation failed");
+      ttt_model_destroy(m);
+      return rc;
+    }
+    m->ev.push_back(e);
   }
 
   // ---- upload: transpose [in][out] -> [out][in] ----
