@@ -42,6 +42,15 @@ Readings of points the pages leave open (each is listed in the design doc):
   * plain SGD (no momentum, decay or clipping), one joint step over all fast
     matrices; a chunk that is not yet complete is scored at the current W and
     never applied.
+
+bf16 operand mode (static_losses(..., operands="bf16")): the bf16 runs compute
+every matrix product from bf16 operands with wider accumulation. In this mode
+the forward rounds each operand that is not a stored weight (normalised
+activations, q / k after RoPE, v, the unnormalised softmax weights, the
+attention output, the MLP activation, the final normalised state) to bf16 -
+an fp32 value rounded to nearest even - and keeps everything else in fp64.
+It isolates what bf16 operands alone do to the losses; it is not used for
+gradients.
 """
 from __future__ import annotations
 
@@ -51,7 +60,7 @@ from scipy.special import erf
 
 __all__ = ["Oracle", "rmsnorm_fwd", "rmsnorm_bwd", "gelu", "gelu_grad", "rope",
            "rope_inv", "window_attention", "window_attention_bwd", "cross_entropy",
-           "sgd_step", "visible_pairs", "prefill"]
+           "sgd_step", "visible_pairs", "prefill", "bf16_round"]
 
 
 # --------------------------------------------------------------------------
@@ -108,6 +117,21 @@ def rope_inv(x, pos, theta):
     return np.concatenate([x1 * c + x2 * s, -x1 * s + x2 * c], axis=-1)
 
 
+def bf16_round(x):
+    """Round to bf16: to fp32 (nearest even), then keep the top 16 bits of the
+    fp32 pattern, rounding the dropped 16 to nearest with ties to even (the
+    bf16 format: fp32's sign and exponent, 7 stored mantissa bits)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    bits = ((bits + 0x7FFF + lsb) >> 16) << 16
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _same(x):
+    return x
+
+
 def window_mask(qpos, kpos, window):
     """Visible iff qpos - window < kpos <= qpos."""
     qp = np.asarray(qpos)[:, None]
@@ -120,10 +144,12 @@ def visible_pairs(T, window):
     return int(sum(min(p + 1, window) for p in range(T)))
 
 
-def window_attention(q, K, V, qpos, kpos, window):
+def window_attention(q, K, V, qpos, kpos, window, rnd=None):
     """Softmax attention per head restricted to the window.
 
     q [m][H][hd], K/V [n][H][hd]; returns o [m][H][hd] and P [H][m][n].
+    With rnd (bf16 operand mode) the product with V takes rnd(exp(s - max))
+    and the normalisation by the exact sum follows it; P is then None.
     """
     hd = q.shape[-1]
     mask = window_mask(qpos, kpos, window)
@@ -132,6 +158,9 @@ def window_attention(q, K, V, qpos, kpos, window):
     s = np.where(mask[None], s, -np.inf)
     s = s - s.max(axis=-1, keepdims=True)
     e = np.exp(s)
+    if rnd is not None:
+        o = ((rnd(e) @ Vh) / e.sum(axis=-1, keepdims=True)).transpose(1, 0, 2)
+        return o, None
     P = e / e.sum(axis=-1, keepdims=True)
     o = (P @ Vh).transpose(1, 0, 2)                           # [m][H][hd]
     return o, P
@@ -209,13 +238,16 @@ class Oracle:
         self.last_logits = None
 
     # ---- forward over positions [p0, p0+m) with the cache for keys < p0 ----
-    def forward(self, ids, p0, W=None, keep=False):
+    def forward(self, ids, p0, W=None, keep=False, rnd=None):
         """Return logits [m][V] and a tape of what the backward needs.
 
         Keys before p0 come from the cache as stored; keys in [p0, p0+m) come
         from this pass. If keep, the tape keeps tail-block intermediates.
+        rnd: operand rounding of the bf16 operand mode (forward only).
         """
         cfg = self.cfg
+        r = _same if rnd is None else rnd
+        assert rnd is None or not keep
         W = self.W if W is None else W
         H, hd, eps = cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"]
         win = cfg["window"]
@@ -228,32 +260,35 @@ class Oracle:
         for l in range(cfg["n_blocks"]):
             pre = f"{l}."
             u, r1 = rmsnorm_fwd(x, self.p(pre + "attn_norm"), eps)
-            q = (u @ self.p(pre + "wq")).reshape(m, H, hd)
-            k = (u @ self.p(pre + "wk")).reshape(m, H, hd)
-            v = (u @ self.p(pre + "wv")).reshape(m, H, hd)
+            ur = r(u)
+            q = (ur @ self.p(pre + "wq")).reshape(m, H, hd)
+            k = (ur @ self.p(pre + "wk")).reshape(m, H, hd)
+            v = r((ur @ self.p(pre + "wv")).reshape(m, H, hd))
             if cfg["rope"]:
                 q = rope(q, pos, cfg["rope_theta"])
                 k = rope(k, pos, cfg["rope_theta"])
+            q, k = r(q), r(k)
             Kw = np.concatenate([self.K[l][lo:p0], k], axis=0)
             Vw = np.concatenate([self.V[l][lo:p0], v], axis=0)
-            o, P = window_attention(q, Kw, Vw, pos, kpos, win)
+            o, P = window_attention(q, Kw, Vw, pos, kpos, win, rnd=rnd)
             a = o.reshape(m, H * hd)
-            y = x + a @ self.p(pre + "wo")
+            y = x + r(a) @ self.p(pre + "wo")
             n, r2 = rmsnorm_fwd(y, self.p(pre + "mlp_norm"), eps)
+            nr = r(n)
             rec = None
             if l >= self.t0:
-                mt, mt_rec = self._mlp(n, W[(l, "w_up")], W.get((l, "w_gate")), W[(l, "w_down")])
-                ms, ms_rec = self._mlp(n, self.p(pre + "s_up"),
+                mt, mt_rec = self._mlp(nr, W[(l, "w_up")], W.get((l, "w_gate")), W[(l, "w_down")], r)
+                ms, ms_rec = self._mlp(nr, self.p(pre + "s_up"),
                                        self.p(pre + "s_gate") if self.glu else None,
-                                       self.p(pre + "s_down"))
+                                       self.p(pre + "s_down"), r)
                 xn = y + mt + ms
                 if keep:
                     rec = dict(x=x, u=u, r1=r1, q=q, Kw=Kw, Vw=Vw, P=None, a=a, y=y, n=n,
                                r2=r2, mt=mt_rec, ms=ms_rec, nk_cache=p0 - lo)
             else:
-                mo, _ = self._mlp(n, self.p(pre + "w_up"),
+                mo, _ = self._mlp(nr, self.p(pre + "w_up"),
                                   self.p(pre + "w_gate") if self.glu else None,
-                                  self.p(pre + "w_down"))
+                                  self.p(pre + "w_down"), r)
                 xn = y + mo
             tape["kv"].append((k, v))
             if rec is not None:
@@ -262,11 +297,11 @@ class Oracle:
             if self.progress:
                 self.progress(f"oracle forward block {l} positions {p0}..{p0 + m - 1}")
         f, rf = rmsnorm_fwd(x, self.p("final_norm"), eps)
-        z = f @ self.p("lm_head")
+        z = r(f) @ self.p("lm_head")
         tape.update(xL=x, rf=rf, f=f)
         return z, tape
 
-    def _mlp(self, n, Wup, Wgate, Wdown):
+    def _mlp(self, n, Wup, Wgate, Wdown, r=_same):
         hu = n @ Wup
         if self.glu:
             hg = n @ Wgate
@@ -274,7 +309,7 @@ class Oracle:
         else:
             hg = None
             act = gelu(hu)
-        return act @ Wdown, dict(hu=hu, hg=hg, act=act)
+        return r(act) @ Wdown, dict(hu=hu, hg=hg, act=act)
 
     def _mlp_bwd(self, n, rec, Wup, Wgate, Wdown, dout, need_dn):
         """Gradients of one MLP branch: (dWup, dWgate, dWdown, dn)."""
@@ -394,15 +429,18 @@ class Oracle:
                 out[i] = loss_at[pos]
         return out
 
-    def static_losses(self, ids):
-        """Losses of a whole stream in one pass at the current W (no updates)."""
+    def static_losses(self, ids, operands=None):
+        """Losses of a whole stream in one pass at the current W (no updates).
+
+        operands="bf16": the bf16 operand mode (module docstring)."""
+        assert operands in (None, "bf16")
         saveK, saveV = self.K, self.V
         L = self.cfg["n_blocks"]
         H, hd = self.cfg["n_heads"], self.cfg["head_dim"]
         self.K = [np.zeros((0, H, hd)) for _ in range(L)]
         self.V = [np.zeros((0, H, hd)) for _ in range(L)]
         try:
-            z, _ = self.forward(list(ids[:-1]), 0)
+            z, _ = self.forward(list(ids[:-1]), 0, rnd=bf16_round if operands else None)
         finally:
             self.K, self.V = saveK, saveV
         loss, _ = cross_entropy(z, np.asarray(ids[1:]))

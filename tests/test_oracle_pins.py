@@ -193,8 +193,13 @@ def test_p9_visible_pairs_eq1():
 # P6: b = T; cross-check against torch autograd on an independent forward
 # --------------------------------------------------------------------------
 
-def torch_forward(cfg, w, ids, p0, Kc, Vc, Wfast):
-    """Independent forward from torch library ops; returns logits, new K/V."""
+def torch_forward(cfg, w, ids, p0, Kc, Vc, Wfast, bf=False):
+    """Independent forward from torch library ops; returns logits, new K/V.
+
+    bf: round every activation operand of a matrix product with torch's own
+    bf16 cast (through fp32), attention written out so that the unnormalised
+    softmax weights can be rounded (forward only)."""
+    rb = (lambda a: a.float().bfloat16().double()) if bf else (lambda a: a)
     d, H, hd, eps, win = cfg["d_model"], cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"], cfg["window"]
     t0 = cfg["n_blocks"] - cfg["n_ttt_blocks"]
     T = lambda a: torch.as_tensor(a, dtype=torch.float64)
@@ -210,8 +215,8 @@ def torch_forward(cfg, w, ids, p0, Kc, Vc, Wfast):
 
     def mlp(n, up, gate, down):
         if cfg["mlp"] == "swiglu":
-            return (F.silu(n @ gate) * (n @ up)) @ down
-        return F.gelu(n @ up) @ down
+            return rb(F.silu(n @ gate) * (n @ up)) @ down
+        return rb(F.gelu(n @ up)) @ down
 
     x = T(w["embed"])[torch.as_tensor(ids, dtype=torch.long)]
     lo = max(0, p0 - win + 1)
@@ -221,27 +226,34 @@ def torch_forward(cfg, w, ids, p0, Kc, Vc, Wfast):
     newK, newV = [], []
     for l in range(cfg["n_blocks"]):
         P = lambda n: T(w[f"{l}.{n}"])
-        u = F.rms_norm(x, (d,), weight=P("attn_norm"), eps=eps)
+        u = rb(F.rms_norm(x, (d,), weight=P("attn_norm"), eps=eps))
         q = (u @ P("wq")).view(m, H, hd)
         k = (u @ P("wk")).view(m, H, hd)
-        v = (u @ P("wv")).view(m, H, hd)
+        v = rb((u @ P("wv")).view(m, H, hd))
         if cfg["rope"]:
             q, k = rot(q), rot(k)
+        q, k = rb(q), rb(k)
         newK.append(k.detach())
         newV.append(v.detach())
         Kw = torch.cat([Kc[l][lo:p0], k], 0)
         Vw = torch.cat([Vc[l][lo:p0], v], 0)
-        a = F.scaled_dot_product_attention(q.transpose(0, 1), Kw.transpose(0, 1), Vw.transpose(0, 1),
-                                           attn_mask=mask)
-        y = x + a.transpose(0, 1).reshape(m, H * hd) @ P("wo")
-        n = F.rms_norm(y, (d,), weight=P("mlp_norm"), eps=eps)
+        if bf:
+            sc = q.transpose(0, 1) @ Kw.transpose(0, 1).transpose(1, 2) / math.sqrt(hd)
+            sc = sc.masked_fill(~mask, float("-inf"))
+            e = torch.exp(sc - sc.amax(-1, keepdim=True))
+            a = (rb(e) @ Vw.transpose(0, 1)) / e.sum(-1, keepdim=True)
+        else:
+            a = F.scaled_dot_product_attention(q.transpose(0, 1), Kw.transpose(0, 1), Vw.transpose(0, 1),
+                                               attn_mask=mask)
+        y = x + rb(a.transpose(0, 1).reshape(m, H * hd)) @ P("wo")
+        n = rb(F.rms_norm(y, (d,), weight=P("mlp_norm"), eps=eps))
         if l >= t0:
             glu = cfg["mlp"] == "swiglu"
             x = y + mlp(n, Wfast[(l, "w_up")], Wfast.get((l, "w_gate")), Wfast[(l, "w_down")]) \
                 + mlp(n, P("s_up"), P("s_gate") if glu else None, P("s_down"))
         else:
             x = y + mlp(n, P("w_up"), P("w_gate") if cfg["mlp"] == "swiglu" else None, P("w_down"))
-    z = F.rms_norm(x, (d,), weight=T(w["final_norm"]), eps=eps) @ T(w["lm_head"])
+    z = rb(F.rms_norm(x, (d,), weight=T(w["final_norm"]), eps=eps)) @ T(w["lm_head"])
     return z, newK, newV
 
 
@@ -269,6 +281,43 @@ def torch_prefill(cfg, w, ids):
         Kc = [torch.cat([Kc[l], nk[l]], 0) for l in range(cfg["n_blocks"])]
         Vc = [torch.cat([Vc[l], nv[l]], 0) for l in range(cfg["n_blocks"])]
     return np.concatenate(losses), {k: v.numpy() for k, v in Wf.items()}
+
+
+@pytest.mark.parametrize("mlp,rope", [("swiglu", True), ("gelu", False)])
+def test_bf16_operand_mode_matches_torch_casts(mlp, rope):
+    """The oracle's bf16 operand mode against the torch forward with torch's
+    bf16 cast at the same operands; it must also differ from fp64 by a bf16-
+    sized amount (so the rounding is applied at all)."""
+    cfg = small_cfg(mlp=mlp, rope=rope, window=64)
+    T = 40
+    w, ids = setup(cfg, T + 1, std=0.3)
+    got = O.Oracle(cfg, w).static_losses(ids, operands="bf16")
+    H, hd = cfg["n_heads"], cfg["head_dim"]
+    L = cfg["n_blocks"]
+    Kc = [torch.zeros(0, H, hd, dtype=torch.float64) for _ in range(L)]
+    Vc = [torch.zeros(0, H, hd, dtype=torch.float64) for _ in range(L)]
+    t0 = L - cfg["n_ttt_blocks"]
+    names = ["w_up", "w_gate", "w_down"] if mlp == "swiglu" else ["w_up", "w_down"]
+    Wf = {(l, n): torch.tensor(w[f"{l}.{n}"], dtype=torch.float64) for l in range(t0, L) for n in names}
+    z, _, _ = torch_forward(cfg, w, ids[:-1], 0, Kc, Vc, Wf, bf=True)
+    ref = F.cross_entropy(z, torch.as_tensor(ids[1:], dtype=torch.long), reduction="none").numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-9)
+    exact = O.Oracle(cfg, w).static_losses(ids)
+    dev = np.abs(got - exact).max()
+    assert 1e-5 < dev < 0.1, dev
+
+
+def test_bf16_round_cases():
+    """Round to nearest, ties to even, at the 8-bit significand of bf16."""
+    u = 2.0 ** -7  # bf16 spacing in [1, 2)
+    cases = [(1.0, 1.0), (1 + u / 2, 1.0), (1 + 3 * u / 2, 1 + 2 * u), (1 + u / 2 + 2 ** -20, 1 + u),
+             (-(1 + 3 * u / 2), -(1 + 2 * u)), (3.0 * 2 ** 100, 3.0 * 2 ** 100), (0.0, 0.0),
+             (1 + u - 2 ** -30, 1 + u)]
+    for x, want in cases:
+        assert O.bf16_round(np.array([x]))[0] == want, (x, want)
+    x = np.random.default_rng(0).standard_normal(20000) * 10.0 ** np.random.default_rng(1).integers(-20, 20, 20000)
+    ref = torch.as_tensor(x.astype(np.float32)).bfloat16().double().numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
 
 
 def test_p6_one_chunk_matches_autograd():
