@@ -27,7 +27,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="3b")
     ap.add_argument("--seq-len", type=int, default=None)
-    ap.add_argument("--prof-class", default="gemm_fwd",
+    ap.add_argument("--prof-class", default="mlp_up",
                     help="kernel class timed with HIP events during the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=None,

@@ -25,12 +25,21 @@ const char* ttt_k_last_error(void);
  *     2: Wm -= lr * acc (fp32 master, ld ldw), then C[m][n] = cast(Wm) if C
  *        and C2[n*ldc2+m] = cast(Wm) if C2 (the inner SGD step, technical
  *        review section 5, Eq. 9, with both compute layouts refreshed).
+ *        For bf16, sr_seed != 0 rounds the copies stochastically (unbiased,
+ *        bits from a hash of (sr_seed, batch, m, n)); 0 rounds to nearest.
+ *     3: SwiGLU MLP up-projection with the activation applied to the fp32
+ *        accumulators: B's rows come in blocks of 64, 32 gate rows then the
+ *        32 up rows of the same hidden units (N a multiple of 64), and
+ *        C[m][u] = silu(gate_u) * up_u for hidden unit u < N/2 (C has N/2
+ *        columns; fp32 if out_f32 else dtype).
+ *     4: C = gelu(acc), exact erf form (fp32 if out_f32 else dtype).
+ *     The activations are the block MLPs of the workloads' configurations.
  * ws: fp32 workspace of ws_elems elements for split-K partial sums (may be
  *     NULL; the kernel then runs without splitting K). */
 int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* A,
                int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc, int64_t sC,
                void* C2, int64_t ldc2, int64_t sC2, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
-               int64_t sW, float lr, int32_t batch, float* ws, int64_t ws_elems, void* stream);
+               int64_t sW, float lr, uint32_t sr_seed, int32_t batch, float* ws, int64_t ws_elems, void* stream);
 
 /* Test hook: force the GEMM block tile (0 automatic, 1 = 256x256, 3 = 128x128
  * with split-K when the tile count is low). Process-wide. */

@@ -9,8 +9,9 @@
  *   TTT_PROF_ATTN_FWD  4*hd*H*(visible query-key pairs) flops per launch
  *   TTT_PROF_ATTN_BWD  4*hd*H*(pairs + in-chunk pairs) flops (dQ, dK, dV)
  *   TTT_PROF_CE        bytes: 4*V read (+ element size * V written) per row
- *   TTT_PROF_GEMM_FWD  2*M*N*K flops, only the forward-layout GEMM that
- *                      stores in the compute dtype (one kernel instance)
+ *   TTT_PROF_MLP_UP    2*M*N*K flops, only the MLP up-projection GEMM with
+ *                      the activation in its epilogue (frozen blocks, one
+ *                      kernel instance)
  * ttt_prof_end waits for the recorded events and returns the summed event
  * time (ms), the launch count and the summed work, then switches timing off.
  * Timing adds event records between launches; leave it off for throughput.
@@ -29,7 +30,7 @@ extern "C" {
 #define TTT_PROF_ATTN_FWD 1
 #define TTT_PROF_ATTN_BWD 2
 #define TTT_PROF_CE 3
-#define TTT_PROF_GEMM_FWD 4
+#define TTT_PROF_MLP_UP 4
 
 struct ttt_model;
 int ttt_prof_begin(struct ttt_model* m, int32_t kernel_class);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libttt.so")
 TTT_FP32, TTT_BF16 = 0, 1
 TTT_GELU, TTT_SWIGLU = 0, 1
 TTT_UP, TTT_GATE, TTT_DOWN = 0, 1, 2
-PROF = {"gemm": 0, "attn_fwd": 1, "attn_bwd": 2, "ce": 3, "gemm_fwd": 4}
+PROF = {"gemm": 0, "attn_fwd": 1, "attn_bwd": 2, "ce": 3, "mlp_up": 4}
 
 c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -77,7 +77,7 @@ def load():
                                  ctypes.POINTER(ctypes.c_double)]
     lib.ttt_k_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
                                c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
-                               c_f32, c_i32, c_vp, c_i64, c_vp]
+                               c_f32, ctypes.c_uint32, c_i32, c_vp, c_i64, c_vp]
     lib.ttt_k_gemm_tile.argtypes = [c_i32]
     lib.ttt_k_gemm_tile.restype = None
     lib.ttt_k_attn_fwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,

@@ -74,27 +74,29 @@ __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g
 }
 
 // ------------------------------- RoPE ------------------------------------
-// qkv rows [rows][3*H*hd] (q | k | v). Row r = s*S + i is position p0 + i.
-// q -> q out (rotated), k (rotated), v -> ring caches at slot pos % cap.
+// fp32 qkv rows [rows][3*H*hd] (q | k | v), as the projection GEMM leaves
+// them, so q and k are rounded to T once, after the rotation. Row r = s*S + i
+// is position p0 + i. q -> q out (rotated), k (rotated), v -> ring caches at
+// slot pos % cap.
 template <typename T>
-__global__ void rope_split_kernel(const T* qkv, int S, int H, int hd, int64_t p0, const float2* tab,
+__global__ void rope_split_kernel(const float* qkv, int S, int H, int hd, int64_t p0, const float2* tab,
                                   T* q, T* kc, T* vc, int cap, int64_t seq_stride) {
   const int64_t r = blockIdx.x;
   const int s = r / S, i = r % S;
   const int64_t pos = p0 + i;
   const int HD = H * hd, half = hd / 2;
-  const T* src = qkv + r * 3 * HD;
+  const float* src = qkv + r * 3 * HD;
   T* kdst = kc + s * seq_stride + (pos % cap) * HD;
   T* vdst = vc + s * seq_stride + (pos % cap) * HD;
   T* qdst = q + r * HD;
   for (int c = threadIdx.x; c < HD; c += blockDim.x) {
     const int hh = c / hd, e = c % hd;
-    float qv = to_f32(src[c]), kv = to_f32(src[HD + c]);
+    float qv = src[c], kv = src[HD + c];
     if (tab) {
       const int pe = e < half ? e : e - half;
       const float2 cs = tab[pos * half + pe];
       const int partner = hh * hd + (e < half ? e + half : e - half);
-      const float qp = to_f32(src[partner]), kp = to_f32(src[HD + partner]);
+      const float qp = src[partner], kp = src[HD + partner];
       if (e < half) {
         qv = qv * cs.x - qp * cs.y;
         kv = kv * cs.x - kp * cs.y;
@@ -105,7 +107,7 @@ __global__ void rope_split_kernel(const T* qkv, int S, int H, int hd, int64_t p0
     }
     qdst[c] = from_f32<T>(qv);
     kdst[c] = from_f32<T>(kv);
-    vdst[c] = src[2 * HD + c];
+    vdst[c] = from_f32<T>(src[2 * HD + c]);
   }
 }
 
@@ -155,8 +157,9 @@ TTT_DEV float gelu_g(float x) {
 }
 TTT_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
 
-// GELU: a = gelu(z[:, j]); SwiGLU: a = silu(z[:, j]) * z[:, h + j].
-// Each thread handles 8 consecutive columns (16-byte bf16 / 2x16-byte fp32 accesses).
+// GELU: a = gelu(z[:, j]); SwiGLU: a = silu(z[:, j]) * z[:, h + j], z in fp32
+// (the pre-activations kept for the backward). Each thread handles 8
+// consecutive columns (16-byte bf16 / 2x16-byte fp32 accesses).
 template <typename T> struct V8;
 template <> struct V8<bf16> {
   typedef bf16x8 type;
@@ -185,16 +188,16 @@ template <> struct V8<float> {
 };
 
 template <typename T>
-__global__ void act_fwd_kernel(const T* z, int h, int64_t ldz, int glu, T* a, int64_t lda) {
+__global__ void act_fwd_kernel(const float* z, int h, int64_t ldz, int glu, T* a, int64_t lda) {
   const int64_t r = blockIdx.y;
   const int j = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (j >= h) return;
-  const T* zr = z + r * ldz;
+  const float* zr = z + r * ldz;
   float g[8], o[8];
-  V8<T>::get(zr + j, g);
+  V8<float>::get(zr + j, g);
   if (glu) {
     float u[8];
-    V8<T>::get(zr + h + j, u);
+    V8<float>::get(zr + h + j, u);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = g[e] * sigm(g[e]) * u[e];
   } else {
@@ -205,19 +208,19 @@ __global__ void act_fwd_kernel(const T* z, int h, int64_t ldz, int glu, T* a, in
 }
 
 template <typename T>
-__global__ void act_bwd_kernel(const T* z, const float* da, int hcols, int64_t ldz, int64_t ldda,
+__global__ void act_bwd_kernel(const float* z, const float* da, int hcols, int64_t ldz, int64_t ldda,
                                int64_t up_off, int glu, T* dz, int64_t lddz) {
   const int64_t r = blockIdx.y;
   const int j = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (j >= hcols) return;
-  const T* zr = z + r * ldz;
+  const float* zr = z + r * ldz;
   float g[8], zg[8], o1[8];
   V8<float>::get(da + r * ldda + j, g);
-  V8<T>::get(zr + j, zg);
+  V8<float>::get(zr + j, zg);
   T* out = dz + r * lddz;
   if (glu) {
     float zu[8], o2[8];
-    V8<T>::get(zr + up_off + j, zu);
+    V8<float>::get(zr + up_off + j, zu);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float sg = sigm(zg[e]);
@@ -426,13 +429,13 @@ hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, 
   return hipGetLastError();
 }
 
-hipError_t rope_split_launch(const void* qkv, int rows, int S, int H, int hd, int64_t p0,
+hipError_t rope_split_launch(const float* qkv, int rows, int S, int H, int hd, int64_t p0,
                              const float2* tab, void* q, void* kc, void* vc, int cap,
                              int64_t seq_stride, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(rope_split_kernel<bf16>, dim3(rows), dim3(NT), 0, st, cp<bf16>(qkv), S, H, hd, p0, tab, mp<bf16>(q), mp<bf16>(kc), mp<bf16>(vc), cap, seq_stride),
-      hipLaunchKernelGGL(rope_split_kernel<float>, dim3(rows), dim3(NT), 0, st, cp<float>(qkv), S, H, hd, p0, tab, mp<float>(q), mp<float>(kc), mp<float>(vc), cap, seq_stride));
+      hipLaunchKernelGGL(rope_split_kernel<bf16>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<bf16>(q), mp<bf16>(kc), mp<bf16>(vc), cap, seq_stride),
+      hipLaunchKernelGGL(rope_split_kernel<float>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<float>(q), mp<float>(kc), mp<float>(vc), cap, seq_stride));
   return hipGetLastError();
 }
 
@@ -446,25 +449,25 @@ hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, co
   return hipGetLastError();
 }
 
-hipError_t act_fwd_launch(const void* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
+hipError_t act_fwd_launch(const float* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
                           int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (h % 8 || ldz % 8 || lda % 8) return hipErrorInvalidValue;
   dim3 g((h / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(act_fwd_kernel<bf16>, g, dim3(NT), 0, st, cp<bf16>(z), h, ldz, glu, mp<bf16>(a), lda),
-      hipLaunchKernelGGL(act_fwd_kernel<float>, g, dim3(NT), 0, st, cp<float>(z), h, ldz, glu, mp<float>(a), lda));
+      hipLaunchKernelGGL(act_fwd_kernel<bf16>, g, dim3(NT), 0, st, z, h, ldz, glu, mp<bf16>(a), lda),
+      hipLaunchKernelGGL(act_fwd_kernel<float>, g, dim3(NT), 0, st, z, h, ldz, glu, mp<float>(a), lda));
   return hipGetLastError();
 }
 
-hipError_t act_bwd_launch(const void* z, const float* da, int rows, int hcols, int64_t ldz, int64_t ldda,
+hipError_t act_bwd_launch(const float* z, const float* da, int rows, int hcols, int64_t ldz, int64_t ldda,
                           int64_t up_off, int glu, void* dz, int64_t lddz, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (hcols % 8 || ldz % 8 || ldda % 8 || up_off % 8 || lddz % 8) return hipErrorInvalidValue;
   dim3 g((hcols / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(act_bwd_kernel<bf16>, g, dim3(NT), 0, st, cp<bf16>(z), da, hcols, ldz, ldda, up_off, glu, mp<bf16>(dz), lddz),
-      hipLaunchKernelGGL(act_bwd_kernel<float>, g, dim3(NT), 0, st, cp<float>(z), da, hcols, ldz, ldda, up_off, glu, mp<float>(dz), lddz));
+      hipLaunchKernelGGL(act_bwd_kernel<bf16>, g, dim3(NT), 0, st, z, da, hcols, ldz, ldda, up_off, glu, mp<bf16>(dz), lddz),
+      hipLaunchKernelGGL(act_bwd_kernel<float>, g, dim3(NT), 0, st, z, da, hcols, ldz, ldda, up_off, glu, mp<float>(dz), lddz));
   return hipGetLastError();
 }
 

@@ -8,14 +8,19 @@
 // (the weight grad reduces over the tokens of a chunk). The weight-grad
 // epilogue applies the inner SGD step W <- W - eta * G to the fp32 master
 // and refreshes the compute copies (technical review "TTT-E2E: Learning a
-// Long Context into Weights", section 5, Eq. 9).
+// Long Context into Weights", section 5, Eq. 9). The MLP up-projection
+// epilogues apply the activation to the fp32 accumulators (GELU, or SwiGLU
+// with gate and up columns interleaved in 32-column blocks so that a lane
+// holds both operands of a hidden unit), so the pre-activation never makes a
+// round trip through HBM or a bf16 rounding.
 //
 // Tiling: block tile BM x BN computed by a WGM x WGN grid of wave64s, each
 // owning a (BM/WGM) x (BN/WGN) tile of 32x32 MFMA tiles (bf16:
 // v_mfma_f32_32x32x16_bf16, fp32: v_mfma_f32_32x32x2f32), fp32 accumulation.
 // Configurations: 256x256 with 8 waves (128x64 wave tiles, two waves per
-// SIMD) for large M*N, 128x128 with 4 waves (64x64 wave tiles) otherwise. Larger wave tiles reuse each LDS
-// fragment for more MFMAs (LDS bandwidth is the limit of 64x64 wave tiles). Operands are
+// SIMD) for large M*N, 128x128 with 4 waves (64x64 wave tiles) otherwise.
+// Larger wave tiles reuse each LDS fragment for more MFMAs (LDS bandwidth is
+// the limit of 64x64 wave tiles). Operands are
 // staged global -> registers -> LDS (two stages, loads of tile k+1 in flight
 // during the MFMAs of tile k) with a padded row stride that keeps the 16-byte
 // fragment reads conflict-free. Block ids are remapped so that each XCD runs
@@ -102,10 +107,42 @@ TTT_DEV void tile_coords(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
   *tn = (t % (GROUP * tiles_n)) / gsz;
 }
 
-// Apply the epilogue to one element (row, col) of batch z.
+// Unbiased (stochastic) rounding of the fp32 master to the bf16 compute copy.
+// A fast weight starts exactly on the bf16 grid and an inner step moves it by
+// less than half a bf16 ulp, so round-to-nearest would return it to W_0 and the
+// forward would never see the update; stochastic rounding keeps the copy an
+// unbiased estimate of W. The random bits come from a counter-based hash.
+TTT_DEV uint32_t mix32(uint32_t h) {
+  h ^= h >> 16; h *= 0x7feb352du; h ^= h >> 15; h *= 0x846ca68bu; h ^= h >> 16;
+  return h;
+}
+template <typename T>
+TTT_DEV T round_copy(float x, uint32_t seed, int z, int row, int col) {
+  if constexpr (sizeof(T) == 2) {
+    if (seed) {
+      const uint32_t h = mix32(seed * 0x9E3779B1u ^ mix32((uint32_t)row * 0x85EBCA77u ^ (uint32_t)col * 0xC2B2AE3Du
+                                                          ^ (uint32_t)z * 0x27D4EB2Fu));
+      const uint32_t u = (__float_as_uint(x) + (h & 0xFFFFu)) & 0xFFFF0000u;
+      return __builtin_bit_cast(bf16, (uint16_t)(u >> 16));
+    }
+  }
+  return from_f32<T>(x);
+}
+
+// MLP activations applied to fp32 accumulators (exact GELU; SiLU gate)
+TTT_DEV float gelu_acc(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+TTT_DEV float swiglu_acc(float g, float u) { return g / (1.f + __expf(-g)) * u; }
+
+// interleaved column of hidden unit u's gate (its up column is 32 further)
+TTT_DEV int gate_col(int u) { return (u >> 5) * 64 + (u & 31); }
+
+// Apply the epilogue to one element (row, col) of batch z (not EPI_SWIGLU).
 template <int EPI, typename OutT, typename T>
 TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_GELU) {
+    OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+    C[(int64_t)row * p.ldc + col] = from_f32<OutT>(gelu_acc(v));
+  } else if constexpr (EPI == EPI_STORE) {
     OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
     C[(int64_t)row * p.ldc + col] = from_f32<OutT>(v);
   } else if constexpr (EPI == EPI_ADD) {
@@ -116,8 +153,27 @@ TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
     float* wp = p.Wm + z * p.sW + (int64_t)row * p.ldw + col;
     const float nw = *wp - p.lr * v;
     *wp = nw;
-    if (p.C) reinterpret_cast<T*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<T>(nw);
-    if (p.C2) reinterpret_cast<T*>(p.C2)[z * p.sC2 + (int64_t)col * p.ldc2 + row] = from_f32<T>(nw);
+    const T cv = round_copy<T>(nw, p.sr_seed, z, row, col);
+    if (p.C) reinterpret_cast<T*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = cv;
+    if (p.C2) reinterpret_cast<T*>(p.C2)[z * p.sC2 + (int64_t)col * p.ldc2 + row] = cv;
+  }
+}
+
+// Epilogue store when the operand (residual / master value) is already loaded.
+template <int EPI, typename OutT, typename T>
+TTT_DEV void store_out(const GemmArgs& p, int z, int row, int col, float v, float in) {
+  if constexpr (EPI == EPI_GELU) {
+    reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<OutT>(gelu_acc(v));
+  } else if constexpr (EPI == EPI_STORE) {
+    reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<OutT>(v);
+  } else if constexpr (EPI == EPI_ADD) {
+    reinterpret_cast<float*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = in + v;
+  } else {
+    const float nw = in - p.lr * v;
+    p.Wm[z * p.sW + (int64_t)row * p.ldw + col] = nw;
+    const T cv = round_copy<T>(nw, p.sr_seed, z, row, col);
+    if (p.C) reinterpret_cast<T*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = cv;
+    if (p.C2) reinterpret_cast<T*>(p.C2)[z * p.sC2 + (int64_t)col * p.ldc2 + row] = cv;
   }
 }
 
@@ -125,21 +181,6 @@ TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
 // tile's new weights go to LDS as [col][row] (4 consecutive rows per 8-byte
 // store), then each [col] row segment leaves in 16-byte stores. The fp32
 // master and the row-major copy are updated directly (lanes along columns).
-// Epilogue store when the operand (residual / master value) is already loaded.
-template <int EPI, typename OutT, typename T>
-TTT_DEV void store_out(const GemmArgs& p, int z, int row, int col, float v, float in) {
-  if constexpr (EPI == EPI_STORE) {
-    reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<OutT>(v);
-  } else if constexpr (EPI == EPI_ADD) {
-    reinterpret_cast<float*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = in + v;
-  } else {
-    const float nw = in - p.lr * v;
-    p.Wm[z * p.sW + (int64_t)row * p.ldw + col] = nw;
-    if (p.C) reinterpret_cast<T*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<T>(nw);
-    if (p.C2) reinterpret_cast<T*>(p.C2)[z * p.sC2 + (int64_t)col * p.ldc2 + row] = from_f32<T>(nw);
-  }
-}
-
 template <typename T, int BM, int BN, int WGM, int WGN>
 TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
                                  T* lds) {
@@ -176,11 +217,12 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + rl + e;
           const float nw = mv[j][q * 4 + e] - p.lr * acc[i][j][q * 4 + e];
+          const T cv = round_copy<T>(nw, p.sr_seed, z, row, col);
           if (row < p.M && col < p.N) {
             Wm[(int64_t)row * p.ldw + col] = nw;
-            if (C) C[(int64_t)row * p.ldc + col] = from_f32<T>(nw);
+            if (C) C[(int64_t)row * p.ldc + col] = cv;
           }
-          nv[e] = (bf16)nw;
+          nv[e] = cv;
         }
         *reinterpret_cast<bf16x4*>(lds + cl * LT + rl) = nv;
       }
@@ -282,11 +324,33 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
       return;
     }
   }
+  if constexpr (EPI == EPI_SWIGLU) {
+    // acc[i][2jj] holds gate columns and acc[i][2jj+1] the matching up columns
+    static_assert(TJ % 2 == 0, "SwiGLU epilogue pairs 32-column blocks");
+    if (splits == 1) {
+      OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TJ / 2; ++jj) {
+          const int cb = n0 + wn * WTN + jj * 64;  // multiple of 64
+          if (cb >= p.N) continue;
+          const int u = cb / 2 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            if (row < p.M)
+              C[(int64_t)row * p.ldc + u] = from_f32<OutT>(swiglu_acc(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]));
+          }
+        }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     // epilogue operands (residual or master) of this row block loaded first
     float in[TJ][16];
-    if constexpr (EPI != EPI_STORE) {
+    if constexpr (EPI == EPI_ADD || EPI == EPI_SGD) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int col = n0 + wn * WTN + j * 32 + (lane & 31);
@@ -323,10 +387,27 @@ template <typename T, int EPI, typename OutT>
 __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __restrict__ part) {
   const int64_t MN = (int64_t)p.M * p.N;
   const int z = blockIdx.y;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[((int64_t)s * batch + z) * MN + e];
-    apply<EPI, OutT, T>(p, z, (int)(e / p.N), (int)(e % p.N), v);
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int H = p.N / 2;
+    OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < (int64_t)p.M * H;
+         e += (int64_t)gridDim.x * blockDim.x) {
+      const int row = (int)(e / H), u = (int)(e % H);
+      const int64_t gi = (int64_t)row * p.N + gate_col(u);
+      float g = 0.f, up = 0.f;
+      for (int s = 0; s < splits; ++s) {
+        g += part[((int64_t)s * batch + z) * MN + gi];
+        up += part[((int64_t)s * batch + z) * MN + gi + 32];
+      }
+      C[(int64_t)row * p.ldc + u] = from_f32<OutT>(swiglu_acc(g, up));
+    }
+    return;
+  } else {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
+      float v = 0.f;
+      for (int s = 0; s < splits; ++s) v += part[((int64_t)s * batch + z) * MN + e];
+      apply<EPI, OutT, T>(p, z, (int)(e / p.N), (int)(e % p.N), v);
+    }
   }
 }
 
@@ -371,6 +452,12 @@ hipError_t dispatch(const GemmArgs& p, int epi, bool out_f32, int batch, float* 
                    : pick<T, EPI_STORE, T>(p, batch, ws, ws_elems, st);
   if (epi == EPI_ADD) return pick<T, EPI_ADD, float>(p, batch, ws, ws_elems, st);
   if (epi == EPI_SGD) return pick<T, EPI_SGD, T>(p, batch, ws, ws_elems, st);
+  if (epi == EPI_SWIGLU)
+    return out_f32 ? pick<T, EPI_SWIGLU, float>(p, batch, ws, ws_elems, st)
+                   : pick<T, EPI_SWIGLU, T>(p, batch, ws, ws_elems, st);
+  if (epi == EPI_GELU)
+    return out_f32 ? pick<T, EPI_GELU, float>(p, batch, ws, ws_elems, st)
+                   : pick<T, EPI_GELU, T>(p, batch, ws, ws_elems, st);
   return hipErrorInvalidValue;
 }
 
@@ -382,6 +469,7 @@ hipError_t gemm_launch(const GemmArgs& p, int dtype, int epi, bool out_f32, int 
                        hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
   if (p.K % (dtype == 1 ? 8 : 4)) return hipErrorInvalidValue;
+  if (epi == EPI_SWIGLU && p.N % 64) return hipErrorInvalidValue;
   if (dtype == 1) return dispatch<bf16>(p, epi, out_f32, batch, ws, ws_elems, st);
   return dispatch<float>(p, epi, out_f32, batch, ws, ws_elems, st);
 }

@@ -29,17 +29,19 @@ const char* ttt_k_last_error(void) { return k_err.c_str(); }
 int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N, int32_t K, const void* A,
                int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C, int64_t ldc, int64_t sC,
                void* C2, int64_t ldc2, int64_t sC2, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
-               int64_t sW, float lr, int32_t batch, float* ws, int64_t ws_elems, void* stream) {
-  if (epi < 0 || epi > 2 || M < 0 || N < 0 || K < 0 || batch < 1) return kfail(TTT_EINVAL, "bad gemm arguments");
+               int64_t sW, float lr, uint32_t sr_seed, int32_t batch, float* ws, int64_t ws_elems, void* stream) {
+  if (epi < 0 || epi > 4 || M < 0 || N < 0 || K < 0 || batch < 1) return kfail(TTT_EINVAL, "bad gemm arguments");
   const int v = dtype == 1 ? 8 : 4;
   if (K % v) return kfail(TTT_EINVAL, "K must be a multiple of the vector width");
   if (epi == 1 && !R) return kfail(TTT_EINVAL, "EPI_ADD needs R");
   if (epi == 2 && !Wm) return kfail(TTT_EINVAL, "EPI_SGD needs Wm");
+  if (epi == 3 && N % 64) return kfail(TTT_EINVAL, "EPI_SWIGLU needs N a multiple of 64");
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.A = A; g.lda = lda; g.sA = sA; g.B = B; g.ldb = ldb; g.sB = sB; g.C = C; g.ldc = ldc; g.sC = sC;
   g.C2 = C2; g.ldc2 = ldc2; g.sC2 = sC2;
   g.M = M; g.N = N; g.K = K; g.R = R; g.ldr = ldr; g.sR = sR; g.Wm = Wm; g.ldw = ldw; g.sW = sW; g.lr = lr;
+  g.sr_seed = sr_seed;
   return kdone(gemm_launch(g, dtype, epi, out_f32 != 0, batch, ws, ws_elems, static_cast<hipStream_t>(stream)));
 }
 

@@ -4,7 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SGD = 2 };
+// EPI_SWIGLU: B's rows (output columns) come in blocks of 32 gate / 32 up
+// columns; C[m][u] = silu(gate_u) * up_u for hidden unit u, C has N/2 columns.
+// EPI_GELU: C = gelu(acc).
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SGD = 2, EPI_SWIGLU = 3, EPI_GELU = 4 };
 
 // C[m][n] (epilogue)= sum_k A[m*lda + k] * B[n*ldb + k], batched over z.
 struct GemmArgs {
@@ -21,6 +24,10 @@ struct GemmArgs {
   void* C2;
   int64_t ldc2, sC2;
   float lr;
+  // EPI_SGD with a bf16 compute copy: if nonzero, the copies are rounded
+  // stochastically from the fp32 master with a counter-based hash of
+  // (sr_seed, batch, row, col); 0 = round to nearest even
+  uint32_t sr_seed;
 };
 
 // ws: fp32 split-K workspace of ws_elems elements (may be null: no split)
@@ -64,16 +71,16 @@ hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, fl
 hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, const float* dn,
                               int rows, int d, float* dres, void* dres_c, bool accumulate, int dt,
                               hipStream_t st);
-hipError_t rope_split_launch(const void* qkv, int rows, int S, int H, int hd, int64_t p0,
+hipError_t rope_split_launch(const float* qkv, int rows, int S, int H, int hd, int64_t p0,
                              const float2* rope_tab, void* q, void* kc, void* vc, int cap,
                              int64_t seq_stride, int dt, hipStream_t st);
 // dq holds nsplit slices of rows x H*hd (summed here)
 hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, const float* dv, int rows, int S,
                                 int H, int hd, int64_t p0, const float2* rope_tab, void* dqkv,
                                 int dt, hipStream_t st);
-hipError_t act_fwd_launch(const void* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
+hipError_t act_fwd_launch(const float* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
                           int dt, hipStream_t st);
-hipError_t act_bwd_launch(const void* z, const float* da, int rows, int hcols, int64_t ldz,
+hipError_t act_bwd_launch(const float* z, const float* da, int rows, int hcols, int64_t ldz,
                           int64_t ldda, int64_t up_off, int glu, void* dz, int64_t lddz, int dt,
                           hipStream_t st);
 hipError_t attn_delta_launch(const void* o, const void* dout, int rows, int H, int hd, int64_t ld,

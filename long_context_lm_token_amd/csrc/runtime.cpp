@@ -92,13 +92,16 @@ struct ttt_model {
 
   // span-pass workspace (rows = B * span)
   float *sX = nullptr, *sR = nullptr, *sL = nullptr;
-  void *sU = nullptr, *sQKV = nullptr, *sQ = nullptr, *sO = nullptr, *sZ = nullptr, *sA = nullptr;
+  void *sU = nullptr, *sQ = nullptr, *sO = nullptr, *sA = nullptr;
+  float* sQKV = nullptr;
 
   // tail workspace (rows = B * b), per tail block where saved for the backward
   std::vector<float*> tx, ty, tr1, tr2, tlse;
-  std::vector<void*> tn, tq, to, tz, ta;
+  std::vector<void*> tn, tq, to, ta;
+  std::vector<float*> tz;  // fp32 pre-activations of the tail MLPs (kept for the backward)
   float *txL = nullptr, *trf = nullptr, *tlog = nullptr;
-  void *tf = nullptr, *tdz = nullptr, *tU = nullptr, *tQKV = nullptr;
+  void *tf = nullptr, *tdz = nullptr, *tU = nullptr;
+  float* tQKV = nullptr;
   float *dres = nullptr, *dn = nullptr, *dA = nullptr, *delta = nullptr, *dq = nullptr, *dk = nullptr,
         *dv = nullptr;
   void *dres_c = nullptr, *dZ = nullptr, *dO = nullptr, *dqkv = nullptr;
@@ -190,10 +193,10 @@ struct Ctx {
   }
   // C = A . B^T-ish per GemmArgs, optionally batched over sequences
   void gemm(int epi, bool out_f32, const GemmArgs& a, int batch = 1, hipStream_t on = nullptr) {
-    // class of this launch for the timing hooks: every GEMM, or the plain
-    // store in the compute dtype (forward projections)
+    // class of this launch for the timing hooks: every GEMM, or only the MLP
+    // up-projection with the activation fused
     int cls = TTT_PROF_GEMM;
-    if (m->prof.cls == TTT_PROF_GEMM_FWD) cls = (epi == EPI_STORE && !out_f32) ? TTT_PROF_GEMM_FWD : -2;
+    if (m->prof.cls == TTT_PROF_MLP_UP) cls = (epi == EPI_SWIGLU || epi == EPI_GELU) ? TTT_PROF_MLP_UP : -2;
     hipStream_t s = on ? on : st;
     // the split-K workspace belongs to the main stream
     float* ws = on ? nullptr : m->ws;
@@ -224,6 +227,11 @@ GemmArgs ga(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int
 
 inline char* off(void* p, int64_t elems, size_t es) { return static_cast<char*>(p) + elems * (int64_t)es; }
 
+// nonzero seed of the stochastic rounding of one update (chunk, tail block, matrix)
+inline uint32_t sr_seed(int64_t chunk, int j, int mat) {
+  return (uint32_t)(chunk * 64 + j * 4 + mat) * 2654435761u | 1u;
+}
+
 // ---------- the span pass: frozen prefix over positions [p0, p0+S) ----------
 void span_pass(Ctx& c, int64_t p0, int S) {
   ttt_model* m = c.m;
@@ -232,7 +240,7 @@ void span_pass(Ctx& c, int64_t p0, int S) {
   c.chk(embed_launch(m->ids, m->maxpos, p0, S, B, m->embed, d, m->V, m->sX, m->dt, c.st), "embed");
   for (int l = 0; l <= m->t0; ++l) {
     c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_attn[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
-    c.gemm(EPI_STORE, false, ga(m->sU, d, m->wqkv_t[l], d, m->sQKV, 3 * HD, R, 3 * HD, d));
+    c.gemm(EPI_STORE, true, ga(m->sU, d, m->wqkv_t[l], d, m->sQKV, 3 * HD, R, 3 * HD, d));
     c.chk(rope_split_launch(m->sQKV, R, S, m->H, m->hd, p0, m->cfg.rope ? m->rope : nullptr, m->sQ,
                             m->kc[l], m->vc[l], m->cap_s, (int64_t)m->cap_s * HD, m->dt, c.st),
           "rope");
@@ -254,9 +262,10 @@ void span_pass(Ctx& c, int64_t p0, int S) {
     c.gemm(EPI_ADD, true, g);
     if (l == m->t0) break;
     c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_mlp[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
+    // up-projection with the activation in its epilogue (SwiGLU weights are
+    // stored with gate / up rows interleaved in blocks of 32)
     const int h = m->h, zw = m->mg * h;
-    c.gemm(EPI_STORE, false, ga(m->sU, d, m->wgu_t[l], d, m->sZ, zw, R, zw, d));
-    c.chk(act_fwd_launch(m->sZ, R, h, zw, m->mg == 2, m->sA, h, m->dt, c.st), "act");
+    c.gemm(m->mg == 2 ? EPI_SWIGLU : EPI_GELU, false, ga(m->sU, d, m->wgu_t[l], d, m->sA, h, R, zw, d));
     g = ga(m->sA, h, m->wd_t[l], h, m->sX, d, R, d, h);
     g.R = m->sX; g.ldr = d;
     c.gemm(EPI_ADD, true, g);
@@ -283,7 +292,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     if (j >= 1) {
       y = m->ty[j];
       c.chk(rmsnorm_fwd_launch(m->tx[j], R, d, m->g_attn[l], eps, m->tU, m->tr1[j], m->dt, c.st), "norm");
-      c.gemm(EPI_STORE, false, ga(m->tU, d, m->wqkv_t[l], d, m->tQKV, 3 * HD, R, 3 * HD, d));
+      c.gemm(EPI_STORE, true, ga(m->tU, d, m->wqkv_t[l], d, m->tQKV, 3 * HD, R, 3 * HD, d));
       c.chk(rope_split_launch(m->tQKV, R, M, m->H, m->hd, P0, m->cfg.rope ? m->rope : nullptr, m->tq[j],
                               m->kc[l], m->vc[l], m->cap_t, (int64_t)m->cap_t * HD, m->dt, c.st),
             "rope");
@@ -309,7 +318,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     c.chk(rmsnorm_fwd_launch(y, R, d, m->g_mlp[l], eps, m->tn[j], m->tr2[j], m->dt, c.st), "norm");
     GemmArgs g = ga(m->tn[j], d, m->f_gu[j], d, m->tz[j], zw, M, zw, d);
     g.sA = (int64_t)M * d; g.sB = sgu; g.sC = (int64_t)M * zw;
-    c.gemm(EPI_STORE, false, g, B);
+    c.gemm(EPI_STORE, true, g, B);
     c.chk(act_fwd_launch(m->tz[j], R, hf, zw, mg == 2, m->ta[j], hf, m->dt, c.st), "act");
     float* xo = (j + 1 < m->nt) ? m->tx[j + 1] : m->txL;
     g = ga(m->ta[j], hf, m->f_d[j], hf, xo, d, M, d, hf);
@@ -361,6 +370,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     g.ldw = master ? ht : hf; g.sW = master ? smd : sd;
     g.C2 = m->fb_d[j]; g.ldc2 = d; g.sC2 = sbd;
     g.lr = m->cfg.lr;
+    g.sr_seed = sr_seed(P0 / m->cfg.mini_batch, j, 2);
     c.gemm(EPI_SGD, false, g, B, m->side);
     c.chk(act_bwd_launch(m->tz[j], m->dA, R, hcols, zw, hf, hf, mg == 2, m->dZ, zw, m->dt, c.st), "act_bwd");
     if (j >= 1) {
@@ -386,6 +396,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       g.ldw = d; g.sW = master ? smgu : sgu;
       g.C2 = off(m->fb_gu[j], zoff, es); g.ldc2 = zw; g.sC2 = sbgu;
       g.lr = m->cfg.lr;
+      g.sr_seed = sr_seed(P0 / m->cfg.mini_batch, j, part);
       c.gemm(EPI_SGD, false, g, B, m->side);
     }
     if (j == 0) break;
@@ -455,6 +466,8 @@ int validate(const ttt_config* c) {
   if (c->d_model % vec || (c->n_heads * hd) % vec || c->vocab % vec || c->mlp_hidden % vec ||
       c->ttt_hidden % vec || c->static_hidden < 0 || tail_h % vec)
     return fail(TTT_EINVAL, "d_model, n_heads*head_dim, vocab and hidden sizes must be multiples of 8");
+  if (c->mlp_kind == TTT_SWIGLU && c->mlp_hidden % 32)
+    return fail(TTT_EINVAL, "mlp_hidden must be a multiple of 32 for SwiGLU");
   if (c->vocab > 32768) return fail(TTT_EINVAL, "vocab above 32768 is not supported");
   if (c->ttt_hidden < 8) return fail(TTT_EINVAL, "ttt_hidden must be >= 8");
   return TTT_OK;
@@ -623,8 +636,8 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   // span workspace
   const int64_t Rs = (int64_t)B * span;
   m->sX = A.f32(Rs * d); m->sR = A.f32(Rs); m->sL = A.f32(Rs * m->H);
-  m->sU = A.el(Rs * d); m->sQKV = A.el(Rs * 3 * HD); m->sQ = A.el(Rs * HD); m->sO = A.el(Rs * HD);
-  m->sZ = A.el(Rs * mg * h); m->sA = A.el(Rs * h);
+  m->sU = A.el(Rs * d); m->sQKV = A.f32(Rs * 3 * HD); m->sQ = A.el(Rs * HD); m->sO = A.el(Rs * HD);
+  m->sA = A.el(Rs * h);
   // tail workspace
   const int64_t Rt = (int64_t)B * b;
   const int nt = m->nt;
@@ -638,10 +651,10 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
       m->tq[j] = A.el(Rt * HD); m->to[j] = A.el(Rt * HD);
     }
     m->tr2[j] = A.f32(Rt); m->tn[j] = A.el(Rt * d);
-    m->tz[j] = A.el(Rt * mg * hf); m->ta[j] = A.el(Rt * hf);
+    m->tz[j] = A.f32(Rt * mg * hf); m->ta[j] = A.el(Rt * hf);
   }
   m->txL = A.f32(Rt * d); m->trf = A.f32(Rt); m->tlog = A.f32(Rt * V);
-  m->tf = A.el(Rt * d); m->tdz = A.el(Rt * V); m->tU = A.el(Rt * d); m->tQKV = A.el(Rt * 3 * HD);
+  m->tf = A.el(Rt * d); m->tdz = A.el(Rt * V); m->tU = A.el(Rt * d); m->tQKV = A.f32(Rt * 3 * HD);
   m->dres = A.f32(Rt * d); m->dn = A.f32(Rt * d); m->dA = A.f32(Rt * hf); m->delta = A.f32(Rt * m->H);
   m->dq = A.f32(ttt_model::kMaxSplit * Rt * HD); m->dk = A.f32(Rt * HD); m->dv = A.f32(Rt * HD);
   m->part_o = A.f32(ttt_model::kMaxSplit * Rt * HD);
@@ -699,8 +712,10 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
     }
     if (l < t0) {
       if (glu) {
-        ck(put_t(w->w_gate[l], d, h, m->wgu_t[l], d, dt, dt, st));
-        ck(put_t(w->w_up[l], d, h, off(m->wgu_t[l], (int64_t)h * d, es), d, dt, dt, st));
+        // rows 64c .. 64c+31: gate units 32c .. 32c+31; rows 64c+32 .. 64c+63: up units
+        for (int i = 0; i < 2; ++i)
+          ck(transpose_launch(i ? w->w_up[l] : w->w_gate[l], d, 32, h, dt, off(m->wgu_t[l], (int64_t)i * 32 * d, es),
+                              d, dt, st, h / 32, 32, (int64_t)64 * d));
       } else {
         ck(put_t(w->w_up[l], d, h, m->wgu_t[l], d, dt, dt, st));
       }
@@ -853,7 +868,7 @@ int ttt_get_weights(const ttt_model* m, int32_t seq, int32_t block, int32_t mat,
 // ---- kernel timing (HIP events around each launch of one kernel class) ----
 int ttt_prof_begin(ttt_model* m, int32_t kernel_class) {
   if (!m) return fail(TTT_EINVAL, "model is NULL");
-  if (kernel_class < TTT_PROF_GEMM || kernel_class > TTT_PROF_GEMM_FWD) return fail(TTT_EINVAL, "kernel_class");
+  if (kernel_class < TTT_PROF_GEMM || kernel_class > TTT_PROF_MLP_UP) return fail(TTT_EINVAL, "kernel_class");
   m->prof.cls = kernel_class;
   m->prof.used = 0;
   m->prof.work.clear();

@@ -27,7 +27,7 @@ def sync():
 
 # ------------------------------- GEMM ---------------------------------------
 
-def run_gemm(dtype, epi, M, N, K, batch=1, out_f32=True, lr=0.0, tile=0, ws_elems=0):
+def run_gemm(dtype, epi, M, N, K, batch=1, out_f32=True, lr=0.0, tile=0, ws_elems=0, sr_seed=0):
     """C = A . B^T with both operands K-contiguous, against fp64 numpy."""
     lib = bd.load()
     A, Ad = rnd((batch, M, K), 1, dtype)
@@ -49,7 +49,7 @@ def run_gemm(dtype, epi, M, N, K, batch=1, out_f32=True, lr=0.0, tile=0, ws_elem
     try:
         rc = lib.ttt_k_gemm(kdt(dtype), epi, int(out_f32), M, N, K, bd.ptr(Ad), K, M * K, bd.ptr(Bd), K, N * K,
                             bd.ptr(C), N, M * N, bd.ptr(C2), M, M * N, bd.ptr(Rd), N, M * N, bd.ptr(Wd), N, M * N,
-                            lr, batch, bd.ptr(ws), ws_elems, bd.stream_ptr())
+                            lr, sr_seed, batch, bd.ptr(ws), ws_elems, bd.stream_ptr())
         bd.check(rc, kernel=True)
         sync()
     finally:
@@ -94,14 +94,97 @@ def test_gemm_residual_add(dtype, tile):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("tile,ws", [(0, 0), (1, 0), (3, 1 << 22)])
-def test_gemm_sgd_epilogue(dtype, tile, ws):
-    """W <- W - lr * (gradient); both compute copies = cast(W)."""
+@pytest.mark.parametrize("sr_seed", [0, 12345])
+def test_gemm_sgd_epilogue(dtype, tile, ws, sr_seed):
+    """W <- W - lr * (gradient); both compute copies = the same rounding of W."""
     lr = 0.37
-    ref, got_c, got_w, got_c2 = run_gemm(dtype, 2, 96, 136, 1024, batch=2, lr=lr, tile=tile, ws_elems=ws)
+    ref, got_c, got_w, got_c2 = run_gemm(dtype, 2, 96, 136, 1024, batch=2, lr=lr, tile=tile, ws_elems=ws,
+                                         sr_seed=sr_seed)
     np.testing.assert_allclose(got_w, ref, rtol=1e-5, atol=1e-4)
-    rt = 1e-7 if dtype == torch.float32 else 2 ** -8
-    np.testing.assert_allclose(got_c, got_w, rtol=rt, atol=0)
-    np.testing.assert_allclose(got_c2, got_w.transpose(0, 2, 1), rtol=rt, atol=0)
+    np.testing.assert_array_equal(got_c2, got_c.transpose(0, 2, 1))
+    if dtype == torch.float32:
+        np.testing.assert_allclose(got_c, got_w, rtol=1e-7, atol=0)
+    elif sr_seed == 0:
+        np.testing.assert_allclose(got_c, got_w, rtol=2 ** -8, atol=0)
+    else:
+        # stochastic rounding: within one bf16 ulp, to one of the two neighbours, unbiased
+        np.testing.assert_allclose(got_c, got_w, rtol=2 ** -7, atol=0)
+        err = (got_c - got_w) / np.abs(got_w)
+        assert abs(err.mean()) < 0.05 * np.abs(err).mean()
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def _gelu(x):
+    from scipy.special import erf
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("epi", [3, 4])
+@pytest.mark.parametrize("tile,ws,shape", [(0, 0, (200, 384, 264)), (1, 0, (300, 640, 200)),
+                                           (3, 1 << 24, (130, 128, 4096)), (3, 0, (70, 192, 96))])
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_gemm_activation_epilogue(dtype, epi, tile, ws, shape, out_f32):
+    """Up-projection with the MLP activation in the epilogue (SwiGLU: gate/up
+    columns interleaved in blocks of 32; GELU: elementwise), incl. split-K."""
+    lib = bd.load()
+    M, N, K = shape
+    batch = 2
+    A, Ad = rnd((batch, M, K), 1, dtype)
+    Bm, Bd = rnd((batch, N, K), 2, dtype)
+    z = np.einsum("zmk,znk->zmn", A, Bm)
+    if epi == 3:
+        u = np.arange(N // 2)
+        gc = (u // 32) * 64 + u % 32
+        ref = _silu(z[:, :, gc]) * z[:, :, gc + 32]
+    else:
+        ref = _gelu(z)
+    NO = ref.shape[2]
+    C = torch.zeros((batch, M, NO), dtype=torch.float32 if out_f32 else dtype, device="cuda")
+    wsb = torch.zeros(ws, device="cuda") if ws else None
+    lib.ttt_k_gemm_tile(tile)
+    try:
+        bd.check(lib.ttt_k_gemm(kdt(dtype), epi, int(out_f32), M, N, K, bd.ptr(Ad), K, M * K, bd.ptr(Bd), K, N * K,
+                                bd.ptr(C), NO, M * NO, None, 0, 0, None, 0, 0, None, 0, 0, 0.0, 0, batch,
+                                bd.ptr(wsb), ws, bd.stream_ptr()), kernel=True)
+        sync()
+    finally:
+        lib.ttt_k_gemm_tile(0)
+    got = C.float().cpu().numpy()
+    scale = np.abs(ref).max()
+    if out_f32:
+        tol = (4e-5 * math.sqrt(K) if dtype == torch.float32 else 2e-3) * max(scale, 1.0)
+    else:
+        tol = (1e-4 if dtype == torch.float32 else 2 ** -8) * max(scale, 1.0) * 2
+    err = np.abs(got - ref).max()
+    assert err <= tol, (err, tol)
+
+
+def test_swiglu_epilogue_rejects_ragged_n():
+    lib = bd.load()
+    rc = lib.ttt_k_gemm(1, 3, 1, 64, 96, 64, None, 64, 0, None, 64, 0, None, 48, 0, None, 0, 0, None, 0, 0,
+                        None, 0, 0, 0.0, 0, 1, None, 0, bd.stream_ptr())
+    assert rc != 0
+
+
+def test_stochastic_rounding_is_unbiased():
+    """Equal masters 1 + 2^-10, an eighth of a bf16 ulp (2^-7 at 1.0) above 1, round up 1/8 of the time."""
+    lib = bd.load()
+    M, N, K = 64, 512, 8
+    A = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+    W = torch.full((M, N), 1.0 + 2.0 ** -10, device="cuda")
+    C = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    bd.check(lib.ttt_k_gemm(1, 2, 0, M, N, K, bd.ptr(A), K, 0, bd.ptr(B), K, 0, bd.ptr(C), N, 0, None, 0, 0,
+                            None, 0, 0, bd.ptr(W), N, 0, 0.0, 777, 1, None, 0, bd.stream_ptr()), kernel=True)
+    sync()
+    c = C.float().cpu().numpy()
+    up = np.mean(c > 1.0)
+    assert set(np.unique(c)) <= {1.0, 1.0 + 2.0 ** -7}
+    assert abs(up - 0.125) < 0.01, up
 
 
 # ---------------------------- attention --------------------------------------
