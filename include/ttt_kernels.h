@@ -41,8 +41,9 @@ int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N
                void* C2, int64_t ldc2, int64_t sC2, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
                int64_t sW, float lr, uint32_t sr_seed, int32_t batch, float* ws, int64_t ws_elems, void* stream);
 
-/* Test hook: force the GEMM block tile (0 automatic, 1 = 256x256, 3 = 128x128
- * with split-K when the tile count is low). Process-wide. */
+/* Test hook: force the GEMM block tile (0 automatic, 1 = 256x256, 2 = 256x128,
+ * 3 = 128x128; each splits K when the tile count is low and a workspace is
+ * given). Process-wide. */
 void ttt_k_gemm_tile(int32_t cfg);
 
 /* Sliding-window attention forward over a ring cache (query p sees keys
@@ -51,7 +52,8 @@ void ttt_k_gemm_tile(int32_t cfg);
  * kc, vc: [B][cap][H*hd], key position j at slot j % cap (cap multiple of 64);
  * lse: fp32 [B][H][M] natural-log sum of exp of the scaled scores.
  * nsplit (1..8) splits each query block's key range over workgroups; with
- * nsplit > 1, ws is an fp32 workspace of nsplit*B*M*(H*hd + 2*H) elements. */
+ * nsplit > 1, H <= 64 and ws is an fp32 workspace of nsplit*B*M*(H*hd + 2*H)
+ * elements. */
 int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
                    float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
                    float scale, int32_t nsplit, float* ws, void* stream);

@@ -10,8 +10,9 @@
  *   TTT_PROF_ATTN_BWD  4*hd*H*(pairs + in-chunk pairs) flops (dQ, dK, dV)
  *   TTT_PROF_CE        bytes: 4*V read (+ element size * V written) per row
  *   TTT_PROF_MLP_UP    2*M*N*K flops, only the MLP up-projection GEMM with
- *                      the activation in its epilogue (frozen blocks, one
- *                      kernel instance)
+ *                      the activation in its epilogue over a full prefill
+ *                      span (frozen blocks, M = batch * span: one kernel
+ *                      instance)
  * ttt_prof_end waits for the recorded events and returns the summed event
  * time (ms), the launch count and the summed work, then switches timing off.
  * Timing adds event records between launches; leave it off for throughput.

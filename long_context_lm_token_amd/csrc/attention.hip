@@ -351,26 +351,42 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-// merge split partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - m)
+// merge split partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - m).
+// One workgroup per row: the normalised weights of every (split, head) go to
+// LDS first, then each thread combines 4 consecutive columns.
+constexpr int COMBINE_MAX_H = 64;
 template <typename T>
 __global__ void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wgt[8][COMBINE_MAX_H];
   const int64_t row = blockIdx.x;  // s*M + q
   const int s = row / a.M, q = row % a.M;
   const int HD = a.H * a.hd;
-  for (int c = threadIdx.x; c < HD; c += blockDim.x) {
-    const int h = c / a.hd;
+  for (int h = threadIdx.x; h < a.H; h += blockDim.x) {
     float m = NEG_BIG;
-    for (int sp = 0; sp < a.nsplit; ++sp)
-      m = fmaxf(m, a.part_m[(((int64_t)sp * a.B + s) * a.H + h) * a.M + q]);
-    float wsum = 0.f, acc = 0.f;
+    for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part_m[(((int64_t)sp * a.B + s) * a.H + h) * a.M + q]);
+    float wsum = 0.f;
     for (int sp = 0; sp < a.nsplit; ++sp) {
       const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * a.M + q;
-      const float wgt = a.part_l[li] * ex2(a.part_m[li] - m);
-      wsum += wgt;
-      acc += wgt * a.part_o[((int64_t)sp * a.B * a.M + row) * a.ldo + c];
+      const float w = a.part_l[li] * ex2(a.part_m[li] - m);
+      wgt[sp][h] = w;
+      wsum += w;
     }
-    reinterpret_cast<T*>(a.o)[row * a.ldo + c] = from_f32<T>(acc / wsum);
-    if (c % a.hd == 0) a.lse[((int64_t)s * a.H + h) * a.M + q] = m * LN2 + logf(wsum);
+    const float inv = 1.f / wsum;
+    for (int sp = 0; sp < a.nsplit; ++sp) wgt[sp][h] *= inv;
+    a.lse[((int64_t)s * a.H + h) * a.M + q] = m * LN2 + logf(wsum);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 4; c < HD; c += blockDim.x * 4) {
+    const int h = c / a.hd;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < a.nsplit; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((int64_t)sp * a.B * a.M + row) * a.ldo + c);
+      const float w = wgt[sp][h];
+      acc[0] += w * v.x; acc[1] += w * v.y; acc[2] += w * v.z; acc[3] += w * v.w;
+    }
+    T* o = reinterpret_cast<T*>(a.o) + row * a.ldo + c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = from_f32<T>(acc[k]);
   }
 }
 
@@ -708,6 +724,7 @@ int attn_splits(int M, int H, int B, int64_t keys_per_query) {
 hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
   if (a.nsplit > 1 && (!a.part_o || !a.part_m || !a.part_l)) return hipErrorInvalidValue;
+  if (a.nsplit > 8 || (a.nsplit > 1 && (a.H > COMBINE_MAX_H || a.ldo % 4))) return hipErrorInvalidValue;
   TTT_HD_SWITCH(fwd_t)
 }
 

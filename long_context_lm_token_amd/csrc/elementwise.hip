@@ -13,6 +13,52 @@ constexpr int NT = 256;
 template <typename T> __host__ __device__ inline const T* cp(const void* p) { return reinterpret_cast<const T*>(p); }
 template <typename T> __host__ __device__ inline T* mp(void* p) { return reinterpret_cast<T*>(p); }
 
+template <typename T> struct V8;
+template <> struct V8<bf16> {
+  typedef bf16x8 type;
+  TTT_DEV static type load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  TTT_DEV static void store(bf16* p, const float (&v)[8]) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(p) = o;
+  }
+  TTT_DEV static void get(const bf16* p, float (&v)[8]) {
+    const bf16x8 x = load(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+  }
+};
+template <> struct V8<float> {
+  TTT_DEV static void store(float* p, const float (&v)[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  TTT_DEV static void get(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+
+// 4 consecutive values of T as floats (8-byte bf16 / 16-byte fp32 accesses)
+TTT_DEV void get4(const bf16* p, float (&v)[4]) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (float)x[e];
+}
+TTT_DEV void get4(const float* p, float (&v)[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+TTT_DEV void put4(bf16* p, const float (&v)[4]) {
+  bf16x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+TTT_DEV void put4(float* p, const float (&v)[4]) { *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]); }
+
 // ------------------------------- embedding -------------------------------
 template <typename T>
 __global__ void embed_kernel(const int32_t* ids, int64_t ids_ss, int64_t p0, int S, const T* E,
@@ -41,16 +87,18 @@ __global__ void rmsnorm_fwd_kernel(const float* x, int d, const T* g, float eps,
   const float rs = rsqrtf(ss / d + eps);
   T* yr = y + r * d;
   for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    yr[c] = from_f32<T>(v.x * rs * to_f32(g[c]));
-    yr[c + 1] = from_f32<T>(v.y * rs * to_f32(g[c + 1]));
-    yr[c + 2] = from_f32<T>(v.z * rs * to_f32(g[c + 2]));
-    yr[c + 3] = from_f32<T>(v.w * rs * to_f32(g[c + 3]));
+    float v[4], gg[4];
+    get4(xr + c, v);
+    get4(g + c, gg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= rs * gg[e];
+    put4(yr + c, v);
   }
   if (threadIdx.x == 0) rstd[r] = rs;
 }
 
 // dx = r*g*dn - x * r^3 * mean(x*g*dn); dres (+)= dx; optional compute copy.
+// Four consecutive columns per thread (d % 4 == 0).
 template <typename T>
 __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g, const float* dn,
                                    int d, float* dres, T* dres_c, bool accumulate) {
@@ -59,17 +107,29 @@ __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g
   const float* xr = x + r * d;
   const float* dr = dn + r * d;
   float dot = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) dot += xr[c] * to_f32(g[c]) * dr[c];
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    float xv[4], gv[4], dv[4];
+    get4(xr + c, xv);
+    get4(g + c, gv);
+    get4(dr + c, dv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot += xv[e] * gv[e] * dv[e];
+  }
   dot = block_sum(dot, red);
   const float rs = rstd[r];
   const float k = rs * rs * rs * dot / d;
   float* o = dres + r * d;
   T* oc = dres_c ? dres_c + r * d : nullptr;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float v = rs * to_f32(g[c]) * dr[c] - xr[c] * k;
-    if (accumulate) v += o[c];
-    o[c] = v;
-    if (oc) oc[c] = from_f32<T>(v);
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    float xv[4], gv[4], dv[4], v[4];
+    get4(xr + c, xv);
+    get4(g + c, gv);
+    get4(dr + c, dv);
+    if (accumulate) get4(o + c, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = rs * gv[e] * dv[e] - xv[e] * k + (accumulate ? v[e] : 0.f);
+    put4(o + c, v);
+    if (oc) put4(oc + c, v);
   }
 }
 
@@ -78,6 +138,7 @@ __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g
 // them, so q and k are rounded to T once, after the rotation. Row r = s*S + i
 // is position p0 + i. q -> q out (rotated), k (rotated), v -> ring caches at
 // slot pos % cap.
+// Each thread rotates 4 consecutive pairs (e, e + hd/2), e = 4t .. 4t+3.
 template <typename T>
 __global__ void rope_split_kernel(const float* qkv, int S, int H, int hd, int64_t p0, const float2* tab,
                                   T* q, T* kc, T* vc, int cap, int64_t seq_stride) {
@@ -89,29 +150,32 @@ __global__ void rope_split_kernel(const float* qkv, int S, int H, int hd, int64_
   T* kdst = kc + s * seq_stride + (pos % cap) * HD;
   T* vdst = vc + s * seq_stride + (pos % cap) * HD;
   T* qdst = q + r * HD;
-  for (int c = threadIdx.x; c < HD; c += blockDim.x) {
-    const int hh = c / hd, e = c % hd;
-    float qv = src[c], kv = src[HD + c];
+  for (int t = threadIdx.x; t < HD / 8; t += blockDim.x) {
+    const int hh = (t * 4) / half, e = (t * 4) % half;
+    const int c1 = hh * hd + e, c2 = c1 + half;
+    float q1[4], q2[4], k1[4], k2[4], v1[4], v2[4];
+    get4(src + c1, q1); get4(src + c2, q2);
+    get4(src + HD + c1, k1); get4(src + HD + c2, k2);
+    get4(src + 2 * HD + c1, v1); get4(src + 2 * HD + c2, v2);
     if (tab) {
-      const int pe = e < half ? e : e - half;
-      const float2 cs = tab[pos * half + pe];
-      const int partner = hh * hd + (e < half ? e + half : e - half);
-      const float qp = src[partner], kp = src[HD + partner];
-      if (e < half) {
-        qv = qv * cs.x - qp * cs.y;
-        kv = kv * cs.x - kp * cs.y;
-      } else {
-        qv = qp * cs.y + qv * cs.x;
-        kv = kp * cs.y + kv * cs.x;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float2 cs = tab[pos * half + e + u];
+        const float a = q1[u], b = q2[u], ka = k1[u], kb = k2[u];
+        q1[u] = a * cs.x - b * cs.y;
+        q2[u] = a * cs.y + b * cs.x;
+        k1[u] = ka * cs.x - kb * cs.y;
+        k2[u] = ka * cs.y + kb * cs.x;
       }
     }
-    qdst[c] = from_f32<T>(qv);
-    kdst[c] = from_f32<T>(kv);
-    vdst[c] = from_f32<T>(src[2 * HD + c]);
+    put4(qdst + c1, q1); put4(qdst + c2, q2);
+    put4(kdst + c1, k1); put4(kdst + c2, k2);
+    put4(vdst + c1, v1); put4(vdst + c2, v2);
   }
 }
 
-// inverse rotation of dq, dk (fp32 rows [rows][H*hd]); pack [dq | dk | dv] in T
+// inverse rotation of dq (sum of nsplit slices), dk (fp32 rows [rows][H*hd]);
+// pack [dq | dk | dv] in T. Each thread handles 4 consecutive pairs.
 template <typename T>
 __global__ void rope_bwd_pack_kernel(const float* dq, int nsplit, int64_t rows, const float* dk, const float* dv,
                                      int S, int H, int hd, int64_t p0, const float2* tab, T* out) {
@@ -123,30 +187,34 @@ __global__ void rope_bwd_pack_kernel(const float* dq, int nsplit, int64_t rows, 
   const float* b = dk + r * HD;
   const float* v = dv + r * HD;
   T* o = out + r * 3 * HD;
-  auto dqv = [&](int c) {
-    float t = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) t += a[sp * rows * HD + c];
-    return t;
-  };
-  for (int c = threadIdx.x; c < HD; c += blockDim.x) {
-    const int hh = c / hd, e = c % hd;
-    float x = dqv(c), y = b[c];
+  for (int t = threadIdx.x; t < HD / 8; t += blockDim.x) {
+    const int hh = (t * 4) / half, e = (t * 4) % half;
+    const int c1 = hh * hd + e, c2 = c1 + half;
+    float x1[4], x2[4], y1[4], y2[4], v1[4], v2[4];
+    get4(a + c1, x1); get4(a + c2, x2);
+    for (int sp = 1; sp < nsplit; ++sp) {
+      float t1[4], t2[4];
+      get4(a + sp * rows * HD + c1, t1);
+      get4(a + sp * rows * HD + c2, t2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { x1[u] += t1[u]; x2[u] += t2[u]; }
+    }
+    get4(b + c1, y1); get4(b + c2, y2);
+    get4(v + c1, v1); get4(v + c2, v2);
     if (tab) {
-      const int pe = e < half ? e : e - half;
-      const float2 cs = tab[pos * half + pe];
-      const int partner = hh * hd + (e < half ? e + half : e - half);
-      const float xp = dqv(partner), yp = b[partner];
-      if (e < half) {
-        x = x * cs.x + xp * cs.y;
-        y = y * cs.x + yp * cs.y;
-      } else {
-        x = -xp * cs.y + x * cs.x;
-        y = -yp * cs.y + y * cs.x;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float2 cs = tab[pos * half + e + u];
+        const float xa = x1[u], xb = x2[u], ya = y1[u], yb = y2[u];
+        x1[u] = xa * cs.x + xb * cs.y;
+        x2[u] = -xa * cs.y + xb * cs.x;
+        y1[u] = ya * cs.x + yb * cs.y;
+        y2[u] = -ya * cs.y + yb * cs.x;
       }
     }
-    o[c] = from_f32<T>(x);
-    o[HD + c] = from_f32<T>(y);
-    o[2 * HD + c] = from_f32<T>(v[c]);
+    put4(o + c1, x1); put4(o + c2, x2);
+    put4(o + HD + c1, y1); put4(o + HD + c2, y2);
+    put4(o + 2 * HD + c1, v1); put4(o + 2 * HD + c2, v2);
   }
 }
 
@@ -160,33 +228,6 @@ TTT_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
 // GELU: a = gelu(z[:, j]); SwiGLU: a = silu(z[:, j]) * z[:, h + j], z in fp32
 // (the pre-activations kept for the backward). Each thread handles 8
 // consecutive columns (16-byte bf16 / 2x16-byte fp32 accesses).
-template <typename T> struct V8;
-template <> struct V8<bf16> {
-  typedef bf16x8 type;
-  TTT_DEV static type load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-  TTT_DEV static void store(bf16* p, const float (&v)[8]) {
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
-    *reinterpret_cast<bf16x8*>(p) = o;
-  }
-  TTT_DEV static void get(const bf16* p, float (&v)[8]) {
-    const bf16x8 x = load(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-  }
-};
-template <> struct V8<float> {
-  TTT_DEV static void store(float* p, const float (&v)[8]) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
-  }
-  TTT_DEV static void get(const float* p, float (&v)[8]) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
-
 template <typename T>
 __global__ void act_fwd_kernel(const float* z, int h, int64_t ldz, int glu, T* a, int64_t lda) {
   const int64_t r = blockIdx.y;
@@ -236,18 +277,27 @@ __global__ void act_bwd_kernel(const float* z, const float* da, int hcols, int64
 }
 
 // delta[s][h][i] = sum_d dO * O for row s*S+i, head h
+// 8 consecutive elements per thread; the hd/8 lanes of a head (2..16, a
+// power of two) reduce with butterflies. Whole waves iterate together.
 template <typename T>
 __global__ void attn_delta_kernel(const T* o, const T* dout, int H, int hd, int64_t ld, int S,
                                   float* delta) {
   const int64_t r = blockIdx.x;
   const int s = r / S, i = r % S;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int h = w; h < H; h += nw) {
+  const int nv = H * hd / 8, g = hd / 8;
+  const int iters = (nv + blockDim.x - 1) / blockDim.x;
+  for (int it = 0; it < iters; ++it) {
+    const int t = it * blockDim.x + threadIdx.x;
     float acc = 0.f;
-    for (int e = lane; e < hd; e += 64)
-      acc += to_f32(o[r * ld + h * hd + e]) * to_f32(dout[r * ld + h * hd + e]);
-    acc = wave_sum(acc);
-    if (lane == 0) delta[((int64_t)s * H + h) * S + i] = acc;
+    if (t < nv) {
+      float a[8], b[8];
+      V8<T>::get(o + r * ld + t * 8, a);
+      V8<T>::get(dout + r * ld + t * 8, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += a[e] * b[e];
+    }
+    for (int off = g >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (t < nv && t % g == 0) delta[((int64_t)s * H + t / g) * S + i] = acc;
   }
 }
 
@@ -369,6 +419,39 @@ __global__ void transpose_kernel(const S* src, int rows, int cols, int64_t lds, 
   }
 }
 
+// 8-element vectors along the source rows and along the destination rows
+// (rows, cols, strides multiples of 8, 16-byte aligned bases).
+template <typename S, typename D>
+__global__ void transpose8_kernel(const S* src, int rows, int cols, int64_t lds, D* dst, int64_t ldd, int64_t s_src,
+                                  int64_t s_dst) {
+  __shared__ float tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  src += blockIdx.z * s_src;
+  dst += blockIdx.z * s_dst;
+  for (int v = threadIdx.x; v < 512; v += blockDim.x) {
+    const int r = v >> 3, cv = (v & 7) * 8;
+    float x[8];
+    if (r0 + r < rows && c0 + cv < cols) {
+      V8<S>::get(src + (int64_t)(r0 + r) * lds + c0 + cv, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][cv + e] = x[e];
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < 512; v += blockDim.x) {
+    const int c = v >> 3, rv = (v & 7) * 8;
+    if (c0 + c < cols && r0 + rv < rows) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = tile[rv + e][c];
+      V8<D>::store(dst + (int64_t)(c0 + c) * ldd + r0 + rv, x);
+    }
+  }
+}
+
 __global__ void copy_rows_kernel(const float* src, int64_t sss, float* dst, int64_t dss, int S, int d) {
   const int i = blockIdx.x, s = blockIdx.y;
   const float* a = src + s * sss + (int64_t)i * d;
@@ -423,6 +506,7 @@ hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, fl
 hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, const float* dn, int rows,
                               int d, float* dres, void* dres_c, bool accumulate, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (d % 4) return hipErrorInvalidValue;
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<bf16>(g), dn, d, dres, mp<bf16>(dres_c), accumulate),
       hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<float>(g), dn, d, dres, mp<float>(dres_c), accumulate));
@@ -433,6 +517,7 @@ hipError_t rope_split_launch(const float* qkv, int rows, int S, int H, int hd, i
                              const float2* tab, void* q, void* kc, void* vc, int cap,
                              int64_t seq_stride, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (hd % 8) return hipErrorInvalidValue;
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(rope_split_kernel<bf16>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<bf16>(q), mp<bf16>(kc), mp<bf16>(vc), cap, seq_stride),
       hipLaunchKernelGGL(rope_split_kernel<float>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<float>(q), mp<float>(kc), mp<float>(vc), cap, seq_stride));
@@ -442,6 +527,7 @@ hipError_t rope_split_launch(const float* qkv, int rows, int S, int H, int hd, i
 hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, const float* dv, int rows, int S,
                                 int H, int hd, int64_t p0, const float2* tab, void* dqkv, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (hd % 8) return hipErrorInvalidValue;
   const int64_t R = rows;
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(rope_bwd_pack_kernel<bf16>, dim3(rows), dim3(NT), 0, st, dq, nsplit, R, dk, dv, S, H, hd, p0, tab, mp<bf16>(dqkv)),
@@ -474,6 +560,7 @@ hipError_t act_bwd_launch(const float* z, const float* da, int rows, int hcols, 
 hipError_t attn_delta_launch(const void* o, const void* dout, int rows, int H, int hd, int64_t ld, int S,
                              float* delta, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (hd % 8 || hd / 8 > 64 || ((hd / 8) & (hd / 8 - 1))) return hipErrorInvalidValue;
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(rows), dim3(NT), 0, st, cp<bf16>(o), cp<bf16>(dout), H, hd, ld, S, delta),
       hipLaunchKernelGGL(attn_delta_kernel<float>, dim3(rows), dim3(NT), 0, st, cp<float>(o), cp<float>(dout), H, hd, ld, S, delta));
@@ -493,6 +580,20 @@ hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, in
                             int ddt, hipStream_t st, int batch, int64_t s_src, int64_t s_dst) {
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
   dim3 g((cols + 63) / 64, (rows + 63) / 64, batch);
+  const bool v8 = rows % 8 == 0 && cols % 8 == 0 && lds % 8 == 0 && ldd % 8 == 0 && s_src % 8 == 0 &&
+                  s_dst % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+  if (v8) {
+    if (sdt == 1 && ddt == 1)
+      hipLaunchKernelGGL((transpose8_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
+    else if (sdt == 1 && ddt == 0)
+      hipLaunchKernelGGL((transpose8_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
+    else if (sdt == 0 && ddt == 1)
+      hipLaunchKernelGGL((transpose8_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
+    else
+      hipLaunchKernelGGL((transpose8_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
+    return hipGetLastError();
+  }
   if (sdt == 1 && ddt == 1)
     hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
   else if (sdt == 1 && ddt == 0)

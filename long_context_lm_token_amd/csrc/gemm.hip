@@ -402,6 +402,35 @@ __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __re
       C[(int64_t)row * p.ldc + u] = from_f32<OutT>(swiglu_acc(g, up));
     }
     return;
+  } else if constexpr (EPI != EPI_SGD) {
+    // four consecutive columns per thread (the launcher checks alignment)
+    const int N4 = p.N / 4;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < MN / 4;
+         e += (int64_t)gridDim.x * blockDim.x) {
+      float4 v = reinterpret_cast<const float4*>(part + (int64_t)z * MN)[e];
+      for (int s = 1; s < splits; ++s) {
+        const float4 t = reinterpret_cast<const float4*>(part + ((int64_t)s * batch + z) * MN)[e];
+        v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+      }
+      const int row = (int)(e / N4), col = (int)(e % N4) * 4;
+      float o[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (EPI == EPI_ADD) {
+        const float4 r = *reinterpret_cast<const float4*>(p.R + z * p.sR + (int64_t)row * p.ldr + col);
+        o[0] += r.x; o[1] += r.y; o[2] += r.z; o[3] += r.w;
+      } else if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = gelu_acc(o[k]);
+      }
+      OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC + (int64_t)row * p.ldc + col;
+      if constexpr (sizeof(OutT) == 4) {
+        *reinterpret_cast<float4*>(C) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        bf16x4 b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) b[k] = (bf16)o[k];
+        *reinterpret_cast<bf16x4*>(C) = b;
+      }
+    }
   } else {
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
       float v = 0.f;
@@ -411,7 +440,7 @@ __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __re
   }
 }
 
-int g_force_tile = 0;  // test hook: 0 auto, 1 = 256x256, 3 = 128x128 (+ split-K)
+int g_force_tile = 0;  // test hook: 0 auto, 1 = 256x256, 2 = 256x128, 3 = 128x128 (each + split-K)
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
 hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
@@ -426,22 +455,45 @@ hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStre
   return hipGetLastError();
 }
 
-template <typename T, int EPI, typename OutT>
-hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipStream_t st) {
-  // 256x256 tiles when they give >= 2 blocks per CU; otherwise 128x128,
-  // split along K when even that leaves CUs idle
-  constexpr int CUS = 256;
-  const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * batch;
-  const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
-  if (g_force_tile == 1 || (!g_force_tile && t256 >= 2 * CUS))
-    return launch_t<T, 256, 256, 2, 4, EPI, OutT>(p, batch, 1, nullptr, st);
+// K splits that bring `tiles` blocks up to `target` (at least 8 K tiles per split)
+template <typename T>
+int k_splits(const GemmArgs& p, int batch, int64_t tiles, int64_t target, int64_t ws_elems) {
+  // the reduce of plain / residual / GELU outputs moves 4 columns per thread
+  const auto al = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  if (!(p.N % 4 == 0 && p.ldc % 4 == 0 && p.sC % 4 == 0 && al(p.C) &&
+        (!p.R || (p.ldr % 4 == 0 && p.sR % 4 == 0 && al(p.R)))))
+    return 1;
   int splits = 1;
   const int nk = (p.K + GT<T>::BK - 1) / GT<T>::BK;
-  while (t128 * splits < 2 * CUS && nk / (splits * 2) >= 8 && splits < 8 &&
+  while (tiles * splits < target && nk / (splits * 2) >= 8 && splits < 8 &&
          (int64_t)(splits * 2) * batch * p.M * p.N <= ws_elems)
     splits *= 2;
-  if (splits > 1 && ws) return launch_t<T, 128, 128, 2, 2, EPI, OutT>(p, batch, splits, ws, st);
-  return launch_t<T, 128, 128, 2, 2, EPI, OutT>(p, batch, 1, nullptr, st);
+  return splits;
+}
+
+template <typename T, int EPI, typename OutT>
+hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipStream_t st) {
+  // 256x256 tiles (8 waves, one block per CU) when they give >= 2 blocks per
+  // CU; 256x128 (4 waves) when M is a multiple of 256 and those fill the CUs;
+  // otherwise 128x128 (4 waves, two blocks per CU). Each splits K when the
+  // tile count alone leaves CUs idle.
+  constexpr int CUS = 256;
+  const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * batch;
+  const int64_t t2x1 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128) * batch;
+  const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
+  if (!ws) ws_elems = 0;
+  int cfg = g_force_tile;
+  if (!cfg) cfg = t256 >= 2 * CUS ? 1 : 3;
+  if (cfg == 1) {
+    const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
+    return launch_t<T, 256, 256, 2, 4, EPI, OutT>(p, batch, sp, sp > 1 ? ws : nullptr, st);
+  }
+  if (cfg == 2) {
+    const int sp = k_splits<T>(p, batch, t2x1, CUS, ws_elems);
+    return launch_t<T, 256, 128, 2, 2, EPI, OutT>(p, batch, sp, sp > 1 ? ws : nullptr, st);
+  }
+  const int sp = k_splits<T>(p, batch, t128, 2 * CUS, ws_elems);
+  return launch_t<T, 128, 128, 2, 2, EPI, OutT>(p, batch, sp, sp > 1 ? ws : nullptr, st);
 }
 
 template <typename T>

@@ -194,9 +194,10 @@ struct Ctx {
   // C = A . B^T-ish per GemmArgs, optionally batched over sequences
   void gemm(int epi, bool out_f32, const GemmArgs& a, int batch = 1, hipStream_t on = nullptr) {
     // class of this launch for the timing hooks: every GEMM, or only the MLP
-    // up-projection with the activation fused
+    // up-projection with the activation fused over a full prefill span
     int cls = TTT_PROF_GEMM;
-    if (m->prof.cls == TTT_PROF_MLP_UP) cls = (epi == EPI_SWIGLU || epi == EPI_GELU) ? TTT_PROF_MLP_UP : -2;
+    if (m->prof.cls == TTT_PROF_MLP_UP)
+      cls = ((epi == EPI_SWIGLU || epi == EPI_GELU) && a.M == m->cfg.batch * m->span) ? TTT_PROF_MLP_UP : -2;
     hipStream_t s = on ? on : st;
     // the split-K workspace belongs to the main stream
     float* ws = on ? nullptr : m->ws;
