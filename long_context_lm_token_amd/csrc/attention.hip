@@ -182,7 +182,7 @@ TTT_DEV void split_range(int j_start, int hi, int nsplit, int sp, int* jb, int* 
 // ============================== forward ==============================
 
 template <typename T, int HD>
-__global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
   typedef AT<T> A;
   constexpr int LDK = HD + A::PADR, LDV = HD + A::PADT;
   constexpr int NKS = HD / A::KS;               // k-steps over the head dim
@@ -255,13 +255,23 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnArgs a) {
     const T* cV = sV[buf];
     if (wactive && !(j0 > wlast || j0 + BKEY - 1 <= wfirst - win)) {
       const bool full = (j0 + BKEY - 1 <= wfirst) && (j0 > wlast - win);
-      f32x16 st[2];
+      // S^T for the two 32-key groups: the two accumulation chains interleave
+      // and the K fragments of step ks+1 are read while step ks multiplies
+      f32x16 st[2] = {f32x16{}, f32x16{}};
+      {
+        typename A::frag kf[2][2];
+        const int kr = lane & 31, kc = hl * (A::KS / 2);
+        kf[0][0] = lds_frag<T>(cK, LDK, kr, kc);
+        kf[0][1] = lds_frag<T>(cK, LDK, 32 + kr, kc);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        st[g] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          st[g] = mfma(lds_frag<T>(cK, LDK, g * 32 + (lane & 31), ks * A::KS + hl * (A::KS / 2)), qf[ks], st[g]);
+        for (int ks = 0; ks < NKS; ++ks) {
+          if (ks + 1 < NKS) {
+            kf[(ks + 1) & 1][0] = lds_frag<T>(cK, LDK, kr, (ks + 1) * A::KS + kc);
+            kf[(ks + 1) & 1][1] = lds_frag<T>(cK, LDK, 32 + kr, (ks + 1) * A::KS + kc);
+          }
+          st[0] = mfma(kf[ks & 1][0], qf[ks], st[0]);
+          st[1] = mfma(kf[ks & 1][1], qf[ks], st[1]);
+        }
       }
       if (!full) {
         // visible iff pq - win < j <= pq, i.e. 0 <= pq - j < win
@@ -303,12 +313,14 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(AttnArgs a) {
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int u = 0; u < KSteps<T>::N; ++u) {
+          // all V^T fragments of this key step first, then their MFMAs
+          typename A::frag vf[DB];
+#pragma unroll
+          for (int i = 0; i < DB; ++i)
+            vf[i] = (i * 32 < HD) ? lds_frag_tr<T>(cV, LDV, i * 32, g, u, lane, HD) : typename A::frag{};
           typename A::frag pf = acc_frag<T>(st[g], u);
 #pragma unroll
-          for (int i = 0; i < DB; ++i) {
-            typename A::frag vf = (i * 32 < HD) ? lds_frag_tr<T>(cV, LDV, i * 32, g, u, lane, HD) : typename A::frag{};
-            o[i] = mfma(vf, pf, o[i]);
-          }
+          for (int i = 0; i < DB; ++i) o[i] = mfma(vf[i], pf, o[i]);
         }
     }
     if (more) {
@@ -393,7 +405,7 @@ __global__ void attn_combine_kernel(AttnArgs a) {
 // ============================== backward: dQ ==============================
 
 template <typename T, int HD>
-__global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   typedef AT<T> A;
   constexpr int LDK = HD + A::PADT, LDV = HD + A::PADR;
   constexpr int NKS = HD / A::KS;
