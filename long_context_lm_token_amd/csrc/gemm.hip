@@ -245,6 +245,78 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
   }
 }
 
+// Epilogue of one block: split-K partials, or the EPI operation on the
+// accumulators of wave (wm, wn). smem: the block's LDS (staged SGD copy).
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
+TTT_DEV void gemm_epilogue(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane,
+                           const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part, T* smem) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TI = WTM / 32, TJ = WTN / 32;
+  if constexpr (EPI == EPI_SGD && sizeof(T) == 2) {
+    if (splits == 1 && p.C2) {
+      sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, smem);
+      return;
+    }
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    // acc[i][2jj] holds gate columns and acc[i][2jj+1] the matching up columns
+    static_assert(TJ % 2 == 0, "SwiGLU epilogue pairs 32-column blocks");
+    if (splits == 1) {
+      OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TJ / 2; ++jj) {
+          const int cb = n0 + wn * WTN + jj * 64;  // multiple of 64
+          if (cb >= p.N) continue;
+          const int u = cb / 2 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            if (row < p.M)
+              C[(int64_t)row * p.ldc + u] = from_f32<OutT>(swiglu_acc(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]));
+          }
+        }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    // epilogue operands (residual or master) of this row block loaded first
+    float in[TJ][16];
+    if constexpr (EPI == EPI_ADD || EPI == EPI_SGD) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          in[j][r] = 0.f;
+          if (splits == 1 && row < p.M && col < p.N)
+            in[j][r] = EPI == EPI_ADD ? p.R[z * p.sR + (int64_t)row * p.ldr + col]
+                                      : p.Wm[z * p.sW + (int64_t)row * p.ldw + col];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row >= p.M) continue;
+        const float v = acc[i][j][r];
+        if (splits > 1)
+          part[(((int64_t)blockIdx.y * gridDim.z + z) * p.M + row) * p.N + col] = v;
+        else
+          store_out<EPI, OutT, T>(p, z, row, col, v, in[j][r]);
+      }
+    }
+  }
+}
+
+
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int splits, float* part) {
   typedef GT<T> G;
@@ -317,69 +389,147 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     __syncthreads();
   }
 
-  // ---- epilogue ----
-  if constexpr (EPI == EPI_SGD && sizeof(T) == 2) {
-    if (splits == 1 && p.C2) {
-      sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, &smem[0][0]);
-      return;
-    }
+  gemm_epilogue<T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, &smem[0][0]);
+}
+
+// ---------------- direct-to-LDS variant (bf16, K % BK == 0) ----------------
+// Operand tiles go from global memory straight into an S-stage LDS ring
+// (global_load_lds: 16 bytes per lane, no register staging), so S-1 tiles are
+// in flight while one is multiplied. Rows hold BK elements; their 16-byte
+// chunks are XOR-swizzled by row so that the fragment reads of consecutive
+// rows hit distinct banks. 128x128 wave tiles (16 MFMA tiles per wave) halve
+// the LDS reads per MFMA of the 128x64 tiles above.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int BK>
+struct DL {
+  static constexpr int CPR = BK / 8;            // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows per 1 KB load instruction
+  static constexpr int RP256 = 256 / (BK * 2);  // rows per 256 bytes of LDS
+  TTT_DEV static int swz(int r) { return (r / RP256) % CPR; }
+};
+
+// issue one ROWS x BK tile (rows row0.., k0..k0+BK) into `tile`; rows past
+// nrows read row nrows-1 (their results are never stored)
+template <int ROWS, int NW, int BK>
+TTT_DEV void dl_issue(const bf16* __restrict__ base, int64_t ld, int row0, int nrows, int k0, bf16* tile, int w,
+                      int lane) {
+  typedef DL<BK> D;
+  constexpr int NQ = ROWS / D::RPI;
+  static_assert(NQ % NW == 0, "whole load instructions per wave");
+  constexpr int PER = NQ / NW;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = w * PER + i;
+    const int r = q * D::RPI + lane / D::CPR;
+    const int c = (lane % D::CPR) ^ D::swz(r);
+    const int gr = min(row0 + r, nrows - 1);
+    const bf16* g = base + (int64_t)gr * ld + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(tile + q * 512), 16, 0, 0);
   }
-  if constexpr (EPI == EPI_SWIGLU) {
-    // acc[i][2jj] holds gate columns and acc[i][2jj+1] the matching up columns
-    static_assert(TJ % 2 == 0, "SwiGLU epilogue pairs 32-column blocks");
-    if (splits == 1) {
-      OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+}
+
+template <int BK>
+TTT_DEV bf16x8 dl_frag(const bf16* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + r * BK + ((c ^ DL<BK>::swz(r)) << 3));
+}
+
+// wait until at most n of this wave's vector-memory operations are in flight
+template <int N>
+TTT_DEV void wait_vm() {
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int splits, float* part) {
+  static_assert(EPI != EPI_SGD, "the SGD epilogue stages through a larger LDS tile");
+  static_assert(S >= 2 && S <= 4, "ring depth");
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN, TI = WTM / 32, TJ = WTN / 32;
+  constexpr int L = (BM + BN) / DL<BK>::RPI / NW;  // load instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) bf16 smem[S][(BM + BN) * BK];
+
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.z;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A) + z * p.sA;
+  const bf16* B = reinterpret_cast<const bf16*>(p.B) + z * p.sB;
+  const int nk_all = p.K / BK;
+  const int per = (nk_all + splits - 1) / splits;
+  const int kt0 = blockIdx.y * per;
+  const int kt1 = min(nk_all, kt0 + per);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+  auto issue = [&](int kt, int st) {
+    dl_issue<BM, NW, BK>(A, p.lda, m0, p.M, kt * BK, smem[st], w, lane);
+    dl_issue<BN, NW, BK>(B, p.ldb, n0, p.N, kt * BK, smem[st] + BM * BK, w, lane);
+  };
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (kt0 + st < kt1) issue(kt0 + st, st);
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int it = kt - kt0;
+    // this wave's loads of tile kt are complete once at most the younger
+    // tiles' loads are outstanding; the barrier then publishes every wave's
+    // part and retires the reads of tile kt-1, whose stage is refilled next
+    const int young = min(S - 2, kt1 - 1 - kt);
+    if (young >= 2) wait_vm<2 * L>();
+    else if (young == 1) wait_vm<L>();
+    else wait_vm<0>();
+    // a plain barrier: a fenced one would also drain the younger tiles' loads
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
+    const bf16* sa = smem[it % S] + wm * WTM * BK;
+    const bf16* sb = smem[it % S] + BM * BK + wn * WTN * BK;
+    // fragments double-buffered in registers: step ks+1 is read from LDS
+    // while the MFMAs of step ks run
+    bf16x8 fa[2][TI], fb[2][TJ];
+    auto read = [&](int ks, int b) {
+      const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) fa[b][i] = dl_frag<BK>(sa, i * 32 + (lane & 31), c);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) fb[b][j] = dl_frag<BK>(sb, j * 32 + (lane & 31), c);
+    };
+    read(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) read(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TJ / 2; ++jj) {
-          const int cb = n0 + wn * WTN + jj * 64;  // multiple of 64
-          if (cb >= p.N) continue;
-          const int u = cb / 2 + (lane & 31);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (row < p.M)
-              C[(int64_t)row * p.ldc + u] = from_f32<OutT>(swiglu_acc(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]));
-          }
-        }
-      return;
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
     }
-  }
+    // schedule: the first step's reads, then each step's MFMAs alternate with
+    // the next step's reads (mask 0x8 = MFMA, 0x100 = LDS read)
+    __builtin_amdgcn_sched_group_barrier(0x100, TI + TJ, 0);
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    // epilogue operands (residual or master) of this row block loaded first
-    float in[TJ][16];
-    if constexpr (EPI == EPI_ADD || EPI == EPI_SGD) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          in[j][r] = 0.f;
-          if (splits == 1 && row < p.M && col < p.N)
-            in[j][r] = EPI == EPI_ADD ? p.R[z * p.sR + (int64_t)row * p.ldr + col]
-                                      : p.Wm[z * p.sW + (int64_t)row * p.ldw + col];
+        for (int q = 0; q < TI + TJ; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row >= p.M) continue;
-        const float v = acc[i][j][r];
-        if (splits > 1)
-          part[(((int64_t)blockIdx.y * gridDim.z + z) * p.M + row) * p.N + col] = v;
-        else
-          store_out<EPI, OutT, T>(p, z, row, col, v, in[j][r]);
+        __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ - (TI + TJ), 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ, 0);
       }
     }
   }
+  __syncthreads();
+  gemm_epilogue<bf16, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, &smem[0][0]);
 }
 
 // sum split-K partials in order and apply the epilogue
@@ -440,7 +590,22 @@ __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __re
   }
 }
 
-int g_force_tile = 0;  // test hook: 0 auto, 1 = 256x256, 2 = 256x128, 3 = 128x128 (each + split-K)
+// test hook: 0 auto, 1 = 256x256, 2 = 256x128, 3 = 128x128, 4 = 256x256 direct-to-LDS
+// (BK 64, two stages), 5 = the same with BK 32 and four stages (each + split-K)
+int g_force_tile = 0;
+
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>
+hipError_t launch_dl(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_dl_kernel<BM, BN, WGM, WGN, BK, S, EPI, OutT>), dim3(tiles, splits, batch),
+                     dim3(WGM * WGN * 64), 0, st, p, splits, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t MN = (int64_t)p.M * p.N;
+  int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
+  hipLaunchKernelGGL((gemm_reduce<bf16, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
+  return hipGetLastError();
+}
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
 hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
@@ -483,11 +648,25 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
   if (!ws) ws_elems = 0;
   int cfg = g_force_tile;
-  if (!cfg) cfg = t256 >= 2 * CUS ? 1 : 3;
+  if (!cfg) {
+    // direct-to-LDS 256x256 when there are enough large tiles (or K is long
+    // enough for split-K to fill the CUs); register-staged kernels otherwise
+    const bool dl = sizeof(T) == 2 && EPI != EPI_SGD && p.K % 64 == 0 && (t256 >= CUS || p.K >= 24576);
+    cfg = dl ? 4 : (t256 >= 2 * CUS ? 1 : 3);
+  }
   if (cfg == 1) {
     const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
     return launch_t<T, 256, 256, 2, 4, EPI, OutT>(p, batch, sp, sp > 1 ? ws : nullptr, st);
   }
+  if constexpr (sizeof(T) == 2 && EPI != EPI_SGD) {
+    if ((cfg == 4 && p.K % 64 == 0) || (cfg == 5 && p.K % 32 == 0)) {
+      const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
+      float* w = sp > 1 ? ws : nullptr;
+      if (cfg == 4) return launch_dl<256, 256, 2, 4, 64, 2, EPI, OutT>(p, batch, sp, w, st);
+      return launch_dl<256, 256, 2, 4, 32, 4, EPI, OutT>(p, batch, sp, w, st);
+    }
+  }
+  if (cfg >= 4) cfg = 1;
   if (cfg == 2) {
     const int sp = k_splits<T>(p, batch, t2x1, CUS, ws_elems);
     return launch_t<T, 256, 128, 2, 2, EPI, OutT>(p, batch, sp, sp > 1 ? ws : nullptr, st);

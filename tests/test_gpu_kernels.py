@@ -78,6 +78,18 @@ def test_gemm_split_k(dtype, shape):
     assert err < 4e-5 * math.sqrt(K), err
 
 
+@pytest.mark.parametrize("tile", [4, 5])
+@pytest.mark.parametrize("epi,shape,ws", [(0, (300, 328, 1024), 0), (1, (257, 520, 2048), 0), (0, (130, 136, 4096), 1 << 24),
+                                          (1, (64, 3072, 3072), 1 << 24), (0, (512, 512, 96), 0)])
+def test_gemm_direct_to_lds(tile, epi, shape, ws):
+    """bf16 tiles loaded straight into an LDS ring (ragged M/N, split-K;
+    K not a multiple of the tile depth falls back to the register-staged kernel)."""
+    M, N, K = shape
+    ref, got, _, _ = run_gemm(torch.bfloat16, epi, M, N, K, batch=2, tile=tile, ws_elems=ws)
+    err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err < 4e-5 * math.sqrt(K), err
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_gemm_store_compute_dtype(dtype):
     ref, got, _, _ = run_gemm(dtype, 0, 130, 64, 64, out_f32=False)
@@ -125,7 +137,8 @@ def _gelu(x):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("epi", [3, 4])
 @pytest.mark.parametrize("tile,ws,shape", [(0, 0, (200, 384, 264)), (1, 0, (300, 640, 200)),
-                                           (3, 1 << 24, (130, 128, 4096)), (3, 0, (70, 192, 96))])
+                                           (3, 1 << 24, (130, 128, 4096)), (3, 0, (70, 192, 96)),
+                                           (5, 0, (300, 640, 256)), (4, 1 << 24, (130, 256, 4096))])
 @pytest.mark.parametrize("out_f32", [True, False])
 def test_gemm_activation_epilogue(dtype, epi, tile, ws, shape, out_f32):
     """Up-projection with the MLP activation in the epilogue (SwiGLU: gate/up
