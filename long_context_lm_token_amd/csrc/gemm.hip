@@ -443,7 +443,7 @@ TTT_DEV void wait_vm() {
 
 template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int splits, float* part) {
-  static_assert(EPI != EPI_SGD, "the SGD epilogue stages through a larger LDS tile");
+  static_assert(EPI != EPI_SGD || BN * (BM + 8) <= S * (BM + BN) * BK, "the staged SGD tile must fit in the ring");
   static_assert(S >= 2 && S <= 4, "ring depth");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, TI = WTM / 32, TJ = WTN / 32;
@@ -591,7 +591,8 @@ __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __re
 }
 
 // test hook: 0 auto, 1 = 256x256, 2 = 256x128, 3 = 128x128, 4 = 256x256 direct-to-LDS
-// (BK 64, two stages), 5 = the same with BK 32 and four stages (each + split-K)
+// (BK 64, two stages), 5 = the same with BK 32 and four stages, 6 / 7 = 128x128
+// direct-to-LDS with two / three stages (each + split-K)
 int g_force_tile = 0;
 
 template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>
@@ -651,21 +652,32 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   if (!cfg) {
     // direct-to-LDS 256x256 when there are enough large tiles (or K is long
     // enough for split-K to fill the CUs); register-staged kernels otherwise
-    const bool dl = sizeof(T) == 2 && EPI != EPI_SGD && p.K % 64 == 0 && (t256 >= CUS || p.K >= 24576);
-    cfg = dl ? 4 : (t256 >= 2 * CUS ? 1 : 3);
+    const bool dl = sizeof(T) == 2 && p.K % 64 == 0;
+    if (dl && EPI != EPI_SGD && (t256 >= CUS || p.K >= 24576)) cfg = 4;
+    else if (dl) cfg = 6;
+    else cfg = t256 >= 2 * CUS ? 1 : 3;
   }
   if (cfg == 1) {
     const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
     return launch_t<T, 256, 256, 2, 4, EPI, OutT>(p, batch, sp, sp > 1 ? ws : nullptr, st);
   }
-  if constexpr (sizeof(T) == 2 && EPI != EPI_SGD) {
-    if ((cfg == 4 && p.K % 64 == 0) || (cfg == 5 && p.K % 32 == 0)) {
+  if constexpr (sizeof(T) == 2) {
+    if ((cfg == 6 || cfg == 7) && p.K % 64 == 0) {
+      const int sp = k_splits<T>(p, batch, t128, cfg == 6 ? 2 * CUS : CUS, ws_elems);
+      float* w = sp > 1 ? ws : nullptr;
+      if (cfg == 6) return launch_dl<128, 128, 2, 2, 64, 2, EPI, OutT>(p, batch, sp, w, st);
+      return launch_dl<128, 128, 2, 2, 64, 3, EPI, OutT>(p, batch, sp, w, st);
+    }
+    if (EPI != EPI_SGD && ((cfg == 4 && p.K % 64 == 0) || (cfg == 5 && p.K % 32 == 0))) {
       const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
       float* w = sp > 1 ? ws : nullptr;
-      if (cfg == 4) return launch_dl<256, 256, 2, 4, 64, 2, EPI, OutT>(p, batch, sp, w, st);
-      return launch_dl<256, 256, 2, 4, 32, 4, EPI, OutT>(p, batch, sp, w, st);
+      if constexpr (EPI != EPI_SGD) {
+        if (cfg == 4) return launch_dl<256, 256, 2, 4, 64, 2, EPI, OutT>(p, batch, sp, w, st);
+        return launch_dl<256, 256, 2, 4, 32, 4, EPI, OutT>(p, batch, sp, w, st);
+      }
     }
   }
+  if (cfg >= 6) cfg = 3;
   if (cfg >= 4) cfg = 1;
   if (cfg == 2) {
     const int sp = k_splits<T>(p, batch, t2x1, CUS, ws_elems);
