@@ -488,11 +488,20 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(AttnArgs a) {
       for (int g = 0; g < 2; ++g) {
         p[g] = f32x16{};
         dp[g] = f32x16{};
+        // S and dP^T chains interleaved; the K / V fragments of step ks+1 are
+        // read while step ks multiplies
+        const int row = g * 32 + (lane & 31), kc = hl * (A::KS / 2);
+        typename A::frag kf[2], vf[2];
+        kf[0] = lds_frag<T>(cK, LDK, row, kc);
+        vf[0] = lds_frag<T>(cV, LDV, row, kc);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const int row = g * 32 + (lane & 31), kk = ks * A::KS + hl * (A::KS / 2);
-          p[g] = mfma(lds_frag<T>(cK, LDK, row, kk), qf[ks], p[g]);
-          dp[g] = mfma(lds_frag<T>(cV, LDV, row, kk), df[ks], dp[g]);
+          if (ks + 1 < NKS) {
+            kf[(ks + 1) & 1] = lds_frag<T>(cK, LDK, row, (ks + 1) * A::KS + kc);
+            vf[(ks + 1) & 1] = lds_frag<T>(cV, LDV, row, (ks + 1) * A::KS + kc);
+          }
+          p[g] = mfma(kf[ks & 1], qf[ks], p[g]);
+          dp[g] = mfma(vf[ks & 1], df[ks], dp[g]);
         }
         const int dj = pq - (j0 + g * 32 + hl * 4);
 #pragma unroll
@@ -506,12 +515,14 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(AttnArgs a) {
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int u = 0; u < KSteps<T>::N; ++u) {
+          // every K^T fragment of this key step first, then their MFMAs
+          typename A::frag kt[DB];
+#pragma unroll
+          for (int i = 0; i < DB; ++i)
+            kt[i] = (i * 32 < HD) ? lds_frag_tr<T>(cK, LDK, i * 32, g, u, lane, HD) : typename A::frag{};
           typename A::frag sf = acc_frag<T>(p[g], u);
 #pragma unroll
-          for (int i = 0; i < DB; ++i) {
-            typename A::frag kf = (i * 32 < HD) ? lds_frag_tr<T>(cK, LDK, i * 32, g, u, lane, HD) : typename A::frag{};
-            dq[i] = mfma(kf, sf, dq[i]);
-          }
+          for (int i = 0; i < DB; ++i) dq[i] = mfma(kt[i], sf, dq[i]);
         }
     }
     if (more) {

@@ -12,7 +12,10 @@
 //   * frozen blocks 0 .. t0-1 and the attention of block t0 do not depend on
 //     W, so their forward runs over long spans of new positions at once
 //     ("span pass": GEMMs with M = batch * span); it ends by storing the
-//     residual after block t0's attention for every position (ystage);
+//     residual after block t0's attention for every position (ystage). The
+//     span passes of a prefill run on their own stream, at most two spans
+//     ahead of the chunk loop, whose small chunk-sized kernels leave compute
+//     units free for them;
 //   * the tail (MLP of block t0, blocks t0+1 .. L-1, final norm, head, CE)
 //     runs per chunk: forward at W_c, backward through the tail, and the SGD
 //     step fused into each trainable matrix's weight-gradient GEMM;
@@ -28,6 +31,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -111,6 +115,11 @@ struct ttt_model {
   // ordered after the input-gradient GEMMs that read W_c; joined per chunk
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> ev;  // pool of ordering events
+  // the frozen prefix of a prefill runs on its own stream (default priority),
+  // overlapping the chunk loop: one event per span, one for the id upload
+  hipStream_t pre = nullptr;
+  std::vector<hipEvent_t> span_ev, reach_ev;  // span done (prefix) / span reached (chunk loop)
+  hipEvent_t ev_ids = nullptr;
   float* ws = nullptr;  // split-K partials
   int64_t ws_elems = 0;
   // key-range splits of the chunk attention: forward partials (dq slices use dq)
@@ -183,6 +192,7 @@ void prof_end(ttt_model* m, int cls, hipStream_t st, hipEvent_t e0, double work)
 struct Ctx {
   ttt_model* m;
   hipStream_t st;
+  bool own_ws = true;  // the split-K workspace belongs to the caller's stream
   hipError_t err = hipSuccess;
   const char* where = "";
   void chk(hipError_t e, const char* w) {
@@ -199,11 +209,12 @@ struct Ctx {
     if (m->prof.cls == TTT_PROF_MLP_UP)
       cls = ((epi == EPI_SWIGLU || epi == EPI_GELU) && a.M == m->cfg.batch * m->span) ? TTT_PROF_MLP_UP : -2;
     hipStream_t s = on ? on : st;
-    // the split-K workspace belongs to the main stream
-    float* ws = on ? nullptr : m->ws;
+    // the split-K workspace belongs to the caller's stream
+    const bool use_ws = !on && own_ws;
+    float* ws = use_ws ? m->ws : nullptr;
     hipEvent_t e0;
     prof_begin(m, cls, s, &e0);
-    chk(gemm_launch(a, m->dt, epi, out_f32, batch, ws, on ? 0 : m->ws_elems, s), "gemm");
+    chk(gemm_launch(a, m->dt, epi, out_f32, batch, ws, use_ws ? m->ws_elems : 0, s), "gemm");
     prof_end(m, cls, s, e0, 2.0 * a.M * a.N * (double)a.K * batch);
   }
   // `to` waits for everything enqueued so far on `from`
@@ -498,6 +509,10 @@ void ttt_model_destroy(ttt_model* m) {
   for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
   for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
   if (m->side) (void)hipStreamDestroy(m->side);
+  if (m->pre) (void)hipStreamDestroy(m->pre);
+  for (hipEvent_t e : m->span_ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : m->reach_ev) (void)hipEventDestroy(e);
+  if (m->ev_ids) (void)hipEventDestroy(m->ev_ids);
   delete m;
 }
 
@@ -688,6 +703,26 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
     }
     m->ev.push_back(e);
   }
+  if (hipStreamCreateWithFlags(&m->pre, hipStreamNonBlocking) != hipSuccess) {
+    m->pre = nullptr;
+    rc = fail(TTT_EHIP, "prefix stream creation failed");
+    ttt_model_destroy(m);
+    return rc;
+  }
+  {
+    const int64_t nspan = (m->maxpos + m->span - 1) / m->span + 1;
+    for (int64_t i = 0; i <= 2 * nspan; ++i) {
+      hipEvent_t e;
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+        rc = fail(TTT_EHIP, "event creation failed");
+        ttt_model_destroy(m);
+        return rc;
+      }
+      if (i == 2 * nspan) m->ev_ids = e;
+      else if (i < nspan) m->span_ev.push_back(e);
+      else m->reach_ev.push_back(e);
+    }
+  }
 
   // ---- upload: transpose [in][out] -> [out][in] ----
   hipError_t e = hipSuccess;
@@ -791,20 +826,50 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t n, float* losses, v
     // the first id of a stream has no predecessor
     for (int s = 0; s < B; ++s) c.chk(fill_f32_launch(losses + s * n, 1, NAN, st), "fill");
   }
-  // frozen prefix over the new positions
-  for (int64_t p = n0; p < n0 + n; p += m->span) {
-    const int S = (int)std::min<int64_t>(m->span, n0 + n - p);
-    span_pass(c, p, S);
-  }
+  // frozen prefix over the new positions, on the prefix stream after the id
+  // upload. The chunk loop waits only for the span that holds its last row;
+  // the prefix stream stays at most two spans ahead of the chunk loop, so its
+  // work spreads over the loop instead of crowding its start.
+  Ctx cp{m, m->pre};
+  cp.own_ws = false;
+  cp.chk(hipEventRecord(m->ev_ids, st), "event record");
+  cp.chk(hipStreamWaitEvent(cp.st, m->ev_ids, 0), "stream wait");
+  std::vector<int64_t> span_start;
+  for (int64_t p = n0; p < n0 + n; p += m->span) span_start.push_back(p);
+  const size_t nsp = span_start.size();
+  size_t issued = 0, waited = 0;
+  auto issue = [&](size_t k) {
+    const int64_t p = span_start[k];
+    if (k >= 2) cp.chk(hipStreamWaitEvent(cp.st, m->reach_ev[k - 2], 0), "stream wait");
+    span_pass(cp, p, (int)std::min<int64_t>(m->span, n0 + n - p));
+    cp.chk(hipEventRecord(m->span_ev[k], cp.st), "event record");
+  };
+  while (issued < std::min<size_t>(2, nsp)) issue(issued++);
+  auto need = [&](int64_t last_pos) {
+    while (waited < nsp && span_start[waited] <= last_pos) {
+      c.chk(hipStreamWaitEvent(st, m->span_ev[waited], 0), "stream wait");
+      // the chunk loop has reached span `waited`: release the one two ahead
+      c.chk(hipEventRecord(m->reach_ev[waited], st), "event record");
+      ++waited;
+      if (issued < nsp && issued <= waited + 1) issue(issued++);
+    }
+  };
   m->n_ids = n0 + n;
   const int64_t n_lab = m->n_ids - 1;
   const int64_t loss_base = n0 - 1;
-  while ((m->chunk + 1) * b <= n_lab && c.err == hipSuccess) {
+  while ((m->chunk + 1) * b <= n_lab && c.err == hipSuccess && cp.err == hipSuccess) {
+    need(m->chunk * b + b - 1);
     tail_pass(c, m->chunk * b, b, true, losses, loss_base, n);
     ++m->chunk;
   }
   const int64_t p0 = m->chunk * b;
+  need(m->n_ids - 1);
   if (p0 < m->n_ids) tail_pass(c, p0, (int)(m->n_ids - p0), false, losses, loss_base, n);
+  need(INT64_MAX);  // the caller's stream covers all work of the call
+  if (c.err == hipSuccess && cp.err != hipSuccess) {
+    c.err = cp.err;
+    c.where = cp.where;
+  }
   return finish(c);
 }
 
