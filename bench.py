@@ -102,9 +102,9 @@ def main():
     roof.update({"kernel": args.prof_class, "launches": k_launch,
                  "avg_launch_us": round(k_ms * 1000 / max(k_launch, 1), 2),
                  "step_frac": round(step_flops / peak_bf16 / (ms_step / 1000), 4),
-                 # the span-pass kernels share the GPU with the chunk loop, so
-                 # their per-launch times include that concurrency
-                 "overlapped": args.prof_class in ("mlp_up",)})
+                 # the span passes run concurrently with the chunk loop, so
+                 # per-launch times include the shared GPU
+                 "overlapped": True})
 
     cpu = None
     if not args.no_cpu_baseline:
