@@ -10,14 +10,65 @@ the roofline of the dominant kernel measured with HIP events on the library's
 stream, and the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes per launch of the roofline kernel, measured with rocprofv3 counters
+# (FETCH_SIZE, WRITE_SIZE) and scaled by the same counters on a plain copy; the
+# record names the hash of the GEMM source it was taken on and is ignored once
+# that source changes
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mlp_up_traffic_3b_span.md")
+GEMM_SOURCE = os.path.join(ROOT, "long_context_lm_token_amd", "csrc", "gemm.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def traffic_bytes(kernel_class):
+    """Stored HBM bytes per launch for the kernel class, or None."""
+    if kernel_class != "mlp_up" or not os.path.exists(TRAFFIC_RECORD):
+        return None
+    text = open(TRAFFIC_RECORD).read()
+    h = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    v = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not h or not v:
+        return None
+    if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest() != h.group(1):
+        return None
+    return int(v.group(1))
+
+
+def probe():
+    """Counter probe: the span MLP up-projection GEMM of the 3B shape (the
+    roofline kernel, fused SwiGLU epilogue, same launch path as a prefill) and
+    a plain device copy of known size, a few launches each."""
+    import torch
+    from long_context_lm_token_amd import binding as bd, synth
+    cfg = synth.get_config("3b")
+    M, N, K = 16384, 2 * cfg["mlp_hidden"], cfg["d_model"]
+    lib = bd.load()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    A = (torch.randn((M, K), device="cuda", generator=g) * 0.02).bfloat16()
+    Bw = (torch.randn((N, K), device="cuda", generator=g) * 0.02).bfloat16()
+    C = torch.empty((M, N // 2), device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        bd.check(lib.ttt_k_gemm(1, 3, 0, M, N, K, bd.ptr(A), K, 0, bd.ptr(Bw), K, 0, bd.ptr(C), N // 2, 0,
+                                None, 0, 0, None, 0, 0, None, 0, 0, 0.0, 0, 1, None, 0, bd.stream_ptr()),
+                 kernel=True)
+    n_copy = 64 << 20  # fp32 elements: 256 MiB read + 256 MiB written per copy
+    src = torch.ones(n_copy, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "mlp_up", "M": M, "N": N, "K": K, "copy_bytes_each_way": n_copy * 4}), flush=True)
 
 
 def main():
@@ -32,11 +83,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=None,
                     help="labelled positions of the CPU-oracle sample (default: one chunk)")
+    ap.add_argument("--probe", action="store_true",
+                    help="run only the roofline kernel and a plain copy (for rocprofv3 counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.probe:
+        probe()
+        return
 
     import numpy as np
     import torch
@@ -98,7 +154,7 @@ def main():
     else:
         achieved = k_work / (k_ms / 1000) / 1e12 if k_ms > 0 else 0.0
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
-                "frac": round(achieved / 2500.0, 4), "traffic": None}
+                "frac": round(achieved / 2500.0, 4), "traffic": traffic_bytes(args.prof_class)}
     roof.update({"kernel": args.prof_class, "launches": k_launch,
                  "avg_launch_us": round(k_ms * 1000 / max(k_launch, 1), 2),
                  "step_frac": round(step_flops / peak_bf16 / (ms_step / 1000), 4),
