@@ -78,11 +78,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="3b")
     ap.add_argument("--seq-len", type=int, default=None)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="independent sequences per step (the length sweep: 16 x 8192, 4 x 32768)")
     ap.add_argument("--prof-class", default="mlp_up",
                     help="kernel class timed with HIP events during the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=None,
                     help="labelled positions of the CPU-oracle sample (default: one chunk)")
+    ap.add_argument("--decode", action="store_true",
+                    help="after the timed prefills, greedy-decode up to the next chunk boundary and "
+                         "through the update it triggers, timed separately (reported under 'decode')")
     ap.add_argument("--probe", action="store_true",
                     help="run only the roofline kernel and a plain copy (for rocprofv3 counters)")
     args = ap.parse_args()
@@ -100,14 +105,16 @@ def main():
 
     cfg = synth.get_config(args.config)
     T = args.seq_len or cfg["seq_len"]
-    B = 1
+    B = args.batch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] config {args.config}: generating weights on the GPU")
     w = synth.make_weights(cfg, seed=0, device="cuda")
     toks = torch.as_tensor(synth.make_batch(cfg, B, T + 1, seed=1)).to(dev)
     stream = torch.cuda.current_stream()
-    model = bd.TTTModel(cfg, w, batch=B, max_positions=T + 1, stream=stream)
+    # room for the decode measurement's tokens (up to one chunk) when asked
+    max_pos = T + 1 + (cfg["mini_batch"] if args.decode else 0)
+    model = bd.TTTModel(cfg, w, batch=B, max_positions=max_pos, stream=stream)
     log(f"[bench] model created, library device bytes {model.device_bytes() / 2**30:.1f} GiB")
     if args.no_cpu_baseline:
         del w
@@ -162,6 +169,10 @@ def main():
                  # per-launch times include the shared GPU
                  "overlapped": True})
 
+    dec = None
+    if args.decode:
+        dec = decode_timing(model, B, T + 1, cfg["mini_batch"])
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, w, toks, args.cpu_positions)
@@ -178,8 +189,34 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if dec is not None:
+        out["decode"] = dec
     print(json.dumps(out), flush=True)
     model.close()
+
+
+def decode_timing(model, B, n_ids, b):
+    """Greedy decode after a full prefill of n_ids ids: the tokens before the
+    next chunk boundary (forward of one position each), then the token whose
+    arrival completes a chunk (the chunk's backward and SGD step run before
+    its forward), each timed between synchronisations."""
+    import torch
+    n_lab = n_ids - 1
+    plain = b - 1 - (n_lab % b)  # decoded ids that complete no chunk
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if plain:
+        model.decode(plain)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    model.decode(1)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    log(f"[bench] decode: {plain} plain tokens {(t1 - t0) * 1000 / max(plain, 1):.2f} ms each, "
+        f"update token {(t2 - t1) * 1000:.2f} ms")
+    return {"batch": B, "plain_tokens": plain, "ms_per_token": round((t1 - t0) * 1000 / max(plain, 1), 3),
+            "update_token_ms": round((t2 - t1) * 1000, 3),
+            "ms_per_token_incl_update": round((t2 - t0) * 1000 / (plain + 1), 3)}
 
 
 def cpu_baseline(cfg, w, toks, positions):
