@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="3b")
     ap.add_argument("--seq-len", type=int, default=None)
+    ap.add_argument("--span", type=int, default=0,
+                    help="rows per frozen-prefix pass (0: the library default)")
     ap.add_argument("--batch", type=int, default=1,
                     help="independent sequences per step (the length sweep: 16 x 8192, 4 x 32768)")
     ap.add_argument("--prof-class", default="mlp_up",
@@ -114,7 +116,7 @@ def main():
     stream = torch.cuda.current_stream()
     # room for the decode measurement's tokens (up to one chunk) when asked
     max_pos = T + 1 + (cfg["mini_batch"] if args.decode else 0)
-    model = bd.TTTModel(cfg, w, batch=B, max_positions=max_pos, stream=stream)
+    model = bd.TTTModel(cfg, w, batch=B, max_positions=max_pos, stream=stream, prefill_span=args.span)
     log(f"[bench] model created, library device bytes {model.device_bytes() / 2**30:.1f} GiB")
     if args.no_cpu_baseline:
         del w
