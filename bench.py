@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=None,
                     help="labelled positions of the CPU-oracle sample (default: one chunk)")
+    ap.add_argument("--full-attention", action="store_true",
+                    help="measure the static full-attention baseline instead: window = the stream, no "
+                         "inner loop, the top blocks in 16K-row passes (same kernels)")
     ap.add_argument("--decode", action="store_true",
                     help="after the timed prefills, greedy-decode up to the next chunk boundary and "
                          "through the update it triggers, timed separately (reported under 'decode')")
@@ -107,6 +110,8 @@ def main():
 
     cfg = synth.get_config(args.config)
     T = args.seq_len or cfg["seq_len"]
+    if args.full_attention:
+        cfg = dict(cfg, window=T + 1, mini_batch=min(16384, T))
     B = args.batch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -116,7 +121,8 @@ def main():
     stream = torch.cuda.current_stream()
     # room for the decode measurement's tokens (up to one chunk) when asked
     max_pos = T + 1 + (cfg["mini_batch"] if args.decode else 0)
-    model = bd.TTTModel(cfg, w, batch=B, max_positions=max_pos, stream=stream, prefill_span=args.span)
+    model = bd.TTTModel(cfg, w, batch=B, max_positions=max_pos, stream=stream, prefill_span=args.span,
+                        forward_only=args.full_attention)
     log(f"[bench] model created, library device bytes {model.device_bytes() / 2**30:.1f} GiB")
     if args.no_cpu_baseline:
         del w
@@ -153,7 +159,7 @@ def main():
     fwd = 2 * T * L * (2 * d * hq + 2 * d * hq + m * d * h) + 2 * T * V * d + 4 * hq * L * pairs
     bwd = (2 * T * V * d + (nt - 1) * (8 * T * d * hq + 4 * hq * pairs + 2 * hq * T * (b + 1)
                                        + 2 * T * m * d * h) + nt * 2 * T * m * d * ht + 2 * T * d * ht) * B
-    step_flops = (fwd * B + bwd)
+    step_flops = fwd * B + (0 if args.full_attention else bwd)
     peak_bf16 = 2.5e15
 
     if args.prof_class == "ce":
@@ -186,7 +192,9 @@ def main():
         "s_per_1k_tokens": round(ms_step / 1000 / (tok / 1000), 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (Zipf(1.1) ids with a repeated 1024-id span; N(0,0.02) bf16 weights)",
-        "config": {"workload": f"{args.config}-shape TTT-E2E prefill, {B} x {T} tokens, b={b}, k={k}",
+        "config": {"workload": (f"{args.config}-shape static full-attention prefill (no inner loop), {B} x {T} tokens"
+                                if args.full_attention else
+                                f"{args.config}-shape TTT-E2E prefill, {B} x {T} tokens, b={b}, k={k}"),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

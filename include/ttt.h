@@ -62,7 +62,12 @@ enum ttt_mat { TTT_UP = 0, TTT_GATE = 1, TTT_DOWN = 2 };
  * attention cache and position counter. max_positions bounds the stream
  * length (ids) per sequence. prefill_span bounds how many positions the
  * frozen lower blocks process per pass (0 = library default).
- * max_device_bytes (0 = unlimited) caps the library's allocation. */
+ * max_device_bytes (0 = unlimited) caps the library's allocation.
+ * forward_only != 0 turns the inner loop off: every position is scored at
+ * the initial weights and no backward or SGD step runs (the static model;
+ * with window >= the stream length it is the full-attention Transformer whose
+ * prefill time the technical review compares TTT-E2E with: its Figure 1 and
+ * section 11). */
 typedef struct ttt_config {
   int32_t vocab, d_model, n_blocks, n_heads, head_dim;
   int32_t mlp_kind;          /* enum ttt_mlp */
@@ -76,6 +81,7 @@ typedef struct ttt_config {
   int64_t max_positions;
   int32_t prefill_span;
   int64_t max_device_bytes;
+  int32_t forward_only;
 } ttt_config;
 
 /* Initial weights, all device pointers in cfg.dtype, row-major [in][out].

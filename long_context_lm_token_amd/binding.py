@@ -30,7 +30,8 @@ class TTTConfig(ctypes.Structure):
                 ("n_ttt_blocks", c_i32), ("ttt_hidden", c_i32), ("static_hidden", c_i32),
                 ("rope", c_i32), ("rope_theta", c_f32), ("norm_eps", c_f32), ("window", c_i32),
                 ("mini_batch", c_i32), ("lr", c_f32), ("dtype", c_i32), ("batch", c_i32),
-                ("max_positions", c_i64), ("prefill_span", c_i32), ("max_device_bytes", c_i64)]
+                ("max_positions", c_i64), ("prefill_span", c_i32), ("max_device_bytes", c_i64),
+                ("forward_only", c_i32)]
 
 
 _PP = ctypes.POINTER(c_vp)
@@ -109,7 +110,8 @@ def ptr(t):
     return c_vp(t.data_ptr()) if t is not None else c_vp(0)
 
 
-def make_config(cfg: dict, batch=1, max_positions=None, prefill_span=0, max_device_bytes=0) -> TTTConfig:
+def make_config(cfg: dict, batch=1, max_positions=None, prefill_span=0, max_device_bytes=0,
+                forward_only=False) -> TTTConfig:
     mp = max_positions if max_positions is not None else cfg["seq_len"] + 1
     return TTTConfig(vocab=cfg["vocab"], d_model=cfg["d_model"], n_blocks=cfg["n_blocks"],
                      n_heads=cfg["n_heads"], head_dim=cfg["head_dim"],
@@ -120,7 +122,7 @@ def make_config(cfg: dict, batch=1, max_positions=None, prefill_span=0, max_devi
                      norm_eps=cfg["norm_eps"], window=cfg["window"], mini_batch=cfg["mini_batch"],
                      lr=cfg["lr"], dtype=TTT_BF16 if cfg["dtype"] == "bf16" else TTT_FP32,
                      batch=batch, max_positions=mp, prefill_span=prefill_span,
-                     max_device_bytes=max_device_bytes)
+                     max_device_bytes=max_device_bytes, forward_only=1 if forward_only else 0)
 
 
 # ---------------------------------------------------------------------------
@@ -179,10 +181,10 @@ class TTTModel:
     """Owns one library model; tokens and losses are torch device tensors."""
 
     def __init__(self, cfg: dict, weights: dict, batch=1, max_positions=None, prefill_span=0,
-                 max_device_bytes=0, stream=None):
+                 max_device_bytes=0, stream=None, forward_only=False):
         self.cfg = cfg
         self.batch = batch
-        self.c = make_config(cfg, batch, max_positions, prefill_span, max_device_bytes)
+        self.c = make_config(cfg, batch, max_positions, prefill_span, max_device_bytes, forward_only)
         self.h, self._keep = ttt_model_create(self.c, weights, cfg["n_blocks"], stream)
         self.stream = stream
 

@@ -668,6 +668,12 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
       if (cfg == 6) return launch_dl<128, 128, 2, 2, 64, 2, EPI, OutT>(p, batch, sp, w, st);
       return launch_dl<128, 128, 2, 2, 64, 3, EPI, OutT>(p, batch, sp, w, st);
     }
+    if ((cfg == 8 && p.K % 64 == 0) || (cfg == 9 && p.K % 32 == 0)) {
+      const int sp = k_splits<T>(p, batch, t128, cfg == 8 ? CUS : 2 * CUS, ws_elems);
+      float* w = sp > 1 ? ws : nullptr;
+      if (cfg == 8) return launch_dl<128, 128, 2, 2, 64, 4, EPI, OutT>(p, batch, sp, w, st);
+      return launch_dl<128, 128, 2, 2, 32, 4, EPI, OutT>(p, batch, sp, w, st);
+    }
     if (EPI != EPI_SGD && ((cfg == 4 && p.K % 64 == 0) || (cfg == 5 && p.K % 32 == 0))) {
       const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
       float* w = sp > 1 ? ws : nullptr;
@@ -677,7 +683,7 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
       }
     }
   }
-  if (cfg >= 6) cfg = 3;
+  if (cfg >= 6) cfg = 3;  // 6..9 where they do not apply
   if (cfg >= 4) cfg = 1;
   if (cfg == 2) {
     const int sp = k_splits<T>(p, batch, t2x1, CUS, ws_elems);

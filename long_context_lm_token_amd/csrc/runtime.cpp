@@ -859,7 +859,7 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t n, float* losses, v
   const int64_t loss_base = n0 - 1;
   while ((m->chunk + 1) * b <= n_lab && c.err == hipSuccess && cp.err == hipSuccess) {
     need(m->chunk * b + b - 1);
-    tail_pass(c, m->chunk * b, b, true, losses, loss_base, n);
+    tail_pass(c, m->chunk * b, b, !m->cfg.forward_only, losses, loss_base, n);
     ++m->chunk;
   }
   const int64_t p0 = m->chunk * b;
@@ -891,7 +891,7 @@ int ttt_decode(ttt_model* m, int64_t n_new, int32_t* tokens_out, float* losses, 
     const int64_t n_lab = m->n_ids - 1;
     // a completed chunk is applied before the next position is computed
     while ((m->chunk + 1) * b <= n_lab && c.err == hipSuccess) {
-      tail_pass(c, m->chunk * b, b, true, nullptr, 0, 0);
+      tail_pass(c, m->chunk * b, b, !m->cfg.forward_only, nullptr, 0, 0);
       ++m->chunk;
     }
     // forward of the new position with the current W: its logits pick the next id

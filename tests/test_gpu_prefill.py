@@ -126,3 +126,25 @@ def test_bf16_small_model():
     check_losses(g, o, BF16_TOL["loss"])
     compare_weights(cfg, model, ors, wn, BF16_TOL["w"], BF16_TOL["dw"])
     model.close()
+
+
+def test_forward_only_is_the_static_model():
+    """forward_only: every position scored at W_init in one causal pass (the
+    oracle's static losses; with a window as long as the stream, full causal
+    attention), and the fast weights never move."""
+    cfg = small_cfg(window=128, mini_batch=32, span=16, period=64)
+    n = 3 * 32 + 7
+    wd, wn = dev_weights(cfg, std=0.2)
+    toks = synth.make_batch(cfg, 2, n, seed=4)
+    model = bd.TTTModel(cfg, wd, batch=2, max_positions=n + 8, forward_only=True)
+    g = model.prefill(torch.as_tensor(toks).cuda()).cpu().numpy()
+    torch.cuda.synchronize()
+    for s in range(2):
+        ref = O.Oracle(cfg, wn).static_losses(toks[s])
+        np.testing.assert_allclose(g[s, 1:], ref, rtol=0, atol=FP32_TOL["loss"])
+        t0 = cfg["n_blocks"] - cfg["n_ttt_blocks"]
+        for l in range(t0, cfg["n_blocks"]):
+            for name in ("w_up", "w_gate", "w_down"):
+                got = model.get_weights(s, l, name).cpu().numpy()
+                np.testing.assert_array_equal(got, wn[f"{l}.{name}"])
+    model.close()
