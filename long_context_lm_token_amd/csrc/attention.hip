@@ -170,6 +170,22 @@ struct Stage {
   }
 };
 
+// Workgroup coordinates with an XCD-aware remap. Workgroups go round-robin to
+// the 8 XCDs in launch order (x fastest); the query (or key) blocks of one
+// head and split are consecutive in x and read the same K/V, so each XCD is
+// given a contiguous run of logical workgroups and those blocks share its L2.
+struct Blk { int x, y, z; };
+TTT_DEV Blk blk() {
+  const int nx = gridDim.x, ny = gridDim.y, n = nx * ny * gridDim.z;
+  int p = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  if ((n & 7) == 0) p = (p & 7) * (n >> 3) + (p >> 3);
+  Blk b;
+  b.x = p % nx;
+  b.y = (p / nx) % ny;
+  b.z = p / (nx * ny);
+  return b;
+}
+
 // key-tile range [jb, je) (positions, multiples of BKEY) of split `sp`
 TTT_DEV void split_range(int j_start, int hi, int nsplit, int sp, int* jb, int* je) {
   const int ntiles = (hi - j_start) / BKEY + 1;
@@ -191,10 +207,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T sV[2][BKEY * LDV];
 
   const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
-  const int s = blockIdx.z / nsplit, sp = blockIdx.z % nsplit, h = blockIdx.y;
+  const Blk bk = blk();
+  const int s = bk.z / nsplit, sp = bk.z % nsplit, h = bk.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hl = lane >> 5;
   const int M = a.M;
-  const int qb0 = blockIdx.x * QB;
+  const int qb0 = bk.x * QB;
   const int qw0 = qb0 + w * WQ;
   const int q = qw0 + (lane & 31);
   const bool qvalid = q < M;
@@ -414,10 +431,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T sV[2][BKEY * LDV];
 
   const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
-  const int s = blockIdx.z / nsplit, sp = blockIdx.z % nsplit, h = blockIdx.y;
+  const Blk bk = blk();
+  const int s = bk.z / nsplit, sp = bk.z % nsplit, h = bk.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hl = lane >> 5;
   const int M = a.M;
-  const int qb0 = blockIdx.x * QB;
+  const int qb0 = bk.x * QB;
   const int qw0 = qb0 + w * WQ;
   const int q = qw0 + (lane & 31);
   const bool qvalid = q < M;
@@ -557,10 +575,11 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T sD[2][BQT * LD];
   __shared__ float sL[2][BQT], sDl[2][BQT];
 
-  const int s = blockIdx.z, h = blockIdx.y;
+  const Blk bk = blk();
+  const int s = bk.z, h = bk.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hl = lane >> 5;
   const int M = a.M;
-  const int kb0 = blockIdx.x * QB;
+  const int kb0 = bk.x * QB;
   const int kw0 = kb0 + w * WQ;
   const int kr = kw0 + (lane & 31);     // key row within the chunk
   const bool kvalid = kr < M;
