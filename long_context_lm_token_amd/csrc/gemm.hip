@@ -621,9 +621,10 @@ hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStre
   return hipGetLastError();
 }
 
-// K splits that bring `tiles` blocks up to `target` (at least 8 K tiles per split)
+// K splits that bring `tiles` blocks up to `target` (at least 8 K tiles per
+// split); with max_kt > 0, also until a split has at most max_kt K tiles
 template <typename T>
-int k_splits(const GemmArgs& p, int batch, int64_t tiles, int64_t target, int64_t ws_elems) {
+int k_splits(const GemmArgs& p, int batch, int64_t tiles, int64_t target, int64_t ws_elems, int max_kt = 0) {
   // the reduce of plain / residual / GELU outputs moves 4 columns per thread
   const auto al = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
   if (!(p.N % 4 == 0 && p.ldc % 4 == 0 && p.sC % 4 == 0 && al(p.C) &&
@@ -631,8 +632,8 @@ int k_splits(const GemmArgs& p, int batch, int64_t tiles, int64_t target, int64_
     return 1;
   int splits = 1;
   const int nk = (p.K + GT<T>::BK - 1) / GT<T>::BK;
-  while (tiles * splits < target && nk / (splits * 2) >= 8 && splits < 8 &&
-         (int64_t)(splits * 2) * batch * p.M * p.N <= ws_elems)
+  while ((tiles * splits < target || (max_kt > 0 && tiles * splits < 2 * target && nk / splits > max_kt)) &&
+         nk / (splits * 2) >= 8 && splits < 8 && (int64_t)(splits * 2) * batch * p.M * p.N <= ws_elems)
     splits *= 2;
   return splits;
 }
@@ -663,7 +664,9 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   }
   if constexpr (sizeof(T) == 2) {
     if ((cfg == 6 || cfg == 7) && p.K % 64 == 0) {
-      const int sp = k_splits<T>(p, batch, t128, cfg == 6 ? 2 * CUS : CUS, ws_elems);
+      // 128x128, two blocks per CU: at least 3/4 of the 512 slots, and short K
+      // ranges per split (long ones keep splitting while the blocks fit twice)
+      const int sp = k_splits<T>(p, batch, t128, cfg == 6 ? 3 * CUS / 2 : CUS, ws_elems, cfg == 6 ? 48 : 0);
       float* w = sp > 1 ? ws : nullptr;
       if (cfg == 6) return launch_dl<128, 128, 2, 2, 64, 2, EPI, OutT>(p, batch, sp, w, st);
       return launch_dl<128, 128, 2, 2, 64, 3, EPI, OutT>(p, batch, sp, w, st);
