@@ -45,9 +45,10 @@ int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N
  * 3 = 128x128, 4 = 256x256 with operands loaded straight into a two-stage LDS
  * ring (bf16, K a multiple of 64, not epi 2), 5 = the same with a four-stage
  * ring (K a multiple of 32), 6 / 7 = 128x128 direct-to-LDS with a two / three
- * stage ring (bf16, K a multiple of 64); each splits K when the tile count is
- * low and a workspace is given; 4 and 5 fall back to 1, 6 and 7 to 3 where
- * they do not apply). Process-wide. */
+ * stage ring (bf16, K a multiple of 64), 8 / 9 = 128x128 with a four-stage
+ * ring of 64 / 32 deep K tiles; each splits K when the tile count is low and
+ * a workspace is given; 4 and 5 fall back to 1, 6 to 9 to 3 where they do
+ * not apply). Process-wide. */
 void ttt_k_gemm_tile(int32_t cfg);
 
 /* Sliding-window attention forward over a ring cache (query p sees keys

@@ -592,7 +592,8 @@ __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __re
 
 // test hook: 0 auto, 1 = 256x256, 2 = 256x128, 3 = 128x128, 4 = 256x256 direct-to-LDS
 // (BK 64, two stages), 5 = the same with BK 32 and four stages, 6 / 7 = 128x128
-// direct-to-LDS with two / three stages (each + split-K)
+// direct-to-LDS with two / three stages, 8 / 9 = 128x128 with four stages of BK
+// 64 / 32 (each + split-K)
 int g_force_tile = 0;
 
 template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>

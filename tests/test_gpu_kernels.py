@@ -78,7 +78,7 @@ def test_gemm_split_k(dtype, shape):
     assert err < 4e-5 * math.sqrt(K), err
 
 
-@pytest.mark.parametrize("tile", [4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("epi,shape,ws", [(0, (300, 328, 1024), 0), (1, (257, 520, 2048), 0), (0, (130, 136, 4096), 1 << 24),
                                           (1, (64, 3072, 3072), 1 << 24), (0, (512, 512, 96), 0)])
 def test_gemm_direct_to_lds(tile, epi, shape, ws):
