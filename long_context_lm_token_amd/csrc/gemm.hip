@@ -245,75 +245,98 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
   }
 }
 
-// Epilogue of one block: split-K partials, or the EPI operation on the
-// accumulators of wave (wm, wn). smem: the block's LDS (staged SGD copy).
-template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
-TTT_DEV void gemm_epilogue(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane,
-                           const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part, T* smem) {
+// Epilogue body of one block for the non-staged operations. CHECK = false
+// for tiles inside the matrix: the stores then run without per-element
+// bounds branches (which would otherwise make the compiler move large
+// accumulator sets through scratch).
+template <bool CHECK, typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
+TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane,
+                      const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TI = WTM / 32, TJ = WTN / 32;
-  if constexpr (EPI == EPI_SGD && sizeof(T) == 2) {
-    if (splits == 1 && p.C2) {
-      sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, smem);
-      return;
-    }
-  }
-  if constexpr (EPI == EPI_SWIGLU) {
-    // acc[i][2jj] holds gate columns and acc[i][2jj+1] the matching up columns
-    static_assert(TJ % 2 == 0, "SwiGLU epilogue pairs 32-column blocks");
-    if (splits == 1) {
-      OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+  if (splits > 1) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int jj = 0; jj < TJ / 2; ++jj) {
-          const int cb = n0 + wn * WTN + jj * 64;  // multiple of 64
-          if (cb >= p.N) continue;
-          const int u = cb / 2 + (lane & 31);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (row < p.M)
-              C[(int64_t)row * p.ldc + u] = from_f32<OutT>(swiglu_acc(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]));
-          }
-        }
-      return;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    // epilogue operands (residual or master) of this row block loaded first
-    float in[TJ][16];
-    if constexpr (EPI == EPI_ADD || EPI == EPI_SGD) {
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int col = n0 + wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          in[j][r] = 0.f;
-          if (splits == 1 && row < p.M && col < p.N)
-            in[j][r] = EPI == EPI_ADD ? p.R[z * p.sR + (int64_t)row * p.ldr + col]
-                                      : p.Wm[z * p.sW + (int64_t)row * p.ldw + col];
+          if (!CHECK || (row < p.M && col < p.N))
+            part[(((int64_t)blockIdx.y * gridDim.z + z) * p.M + row) * p.N + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    // acc[i][2jj] holds gate columns and acc[i][2jj+1] the matching up columns
+    static_assert(TJ % 2 == 0, "SwiGLU epilogue pairs 32-column blocks");
+    OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TJ / 2; ++jj) {
+        const int cb = n0 + wn * WTN + jj * 64;  // multiple of 64
+        if (CHECK && cb >= p.N) continue;
+        const int u = cb / 2 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (!CHECK || row < p.M)
+            C[(int64_t)row * p.ldc + u] = from_f32<OutT>(swiglu_acc(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]));
+        }
+      }
+    return;
+  } else {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      // epilogue operands (residual or master) of this row block loaded first
+      float in[TJ][16];
+      if constexpr (EPI == EPI_ADD || EPI == EPI_SGD) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            in[j][r] = 0.f;
+            if (!CHECK || (row < p.M && col < p.N))
+              in[j][r] = EPI == EPI_ADD ? p.R[z * p.sR + (int64_t)row * p.ldr + col]
+                                        : p.Wm[z * p.sW + (int64_t)row * p.ldw + col];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+        if (CHECK && col >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (CHECK && row >= p.M) continue;
+          store_out<EPI, OutT, T>(p, z, row, col, acc[i][j][r], in[j][r]);
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row >= p.M) continue;
-        const float v = acc[i][j][r];
-        if (splits > 1)
-          part[(((int64_t)blockIdx.y * gridDim.z + z) * p.M + row) * p.N + col] = v;
-        else
-          store_out<EPI, OutT, T>(p, z, row, col, v, in[j][r]);
-      }
+  }
+}
+
+// Epilogue of one block: split-K partials, or the EPI operation on the
+// accumulators of wave (wm, wn). smem: the block's LDS (staged SGD copy).
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
+TTT_DEV void gemm_epilogue(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane,
+                           const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part, T* smem) {
+  if constexpr (EPI == EPI_SGD && sizeof(T) == 2) {
+    if (splits == 1 && p.C2) {
+      sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, smem);
+      return;
     }
   }
+  if (m0 + BM <= p.M && n0 + BN <= p.N)
+    epi_body<false, T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part);
+  else
+    epi_body<true, T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part);
 }
 
 
