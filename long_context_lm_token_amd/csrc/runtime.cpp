@@ -125,6 +125,10 @@ struct ttt_model {
   // key-range splits of the chunk attention: forward partials (dq slices use dq)
   static constexpr int kMaxSplit = 8;
   float *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
+  // the same for span passes of at most one chunk of rows (decode, the last
+  // rows of a prefill): their own buffers, as span passes run on the prefix
+  // stream beside the chunk loop
+  float *spart_o = nullptr, *spart_m = nullptr, *spart_l = nullptr;
 
   bool poisoned = false;
   int64_t bytes = 0;
@@ -261,6 +265,13 @@ void span_pass(Ctx& c, int64_t p0, int S) {
     a.q = m->sQ; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
     a.seq_stride = (int64_t)m->cap_s * HD; a.cap = m->cap_s; a.o = m->sO; a.ldo = HD; a.lse = m->sL;
     a.M = S; a.H = m->H; a.hd = m->hd; a.B = B; a.pos0 = p0; a.window = m->cfg.window; a.scale = m->scale;
+    if (S <= m->cfg.mini_batch) {
+      // few queries (decode, the last rows of a prefill): split each query
+      // block's key range over workgroups
+      a.nsplit = std::min(ttt_model::kMaxSplit,
+                          attn_splits(S, m->H, B, std::min<int64_t>(m->cfg.window, p0 + S)));
+      a.part_o = m->spart_o; a.part_m = m->spart_m; a.part_l = m->spart_l;
+    }
     {
       hipEvent_t e0;
       prof_begin(m, TTT_PROF_ATTN_FWD, c.st, &e0);
@@ -676,6 +687,9 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   m->part_o = A.f32(ttt_model::kMaxSplit * Rt * HD);
   m->part_m = A.f32(ttt_model::kMaxSplit * Rt * m->H);
   m->part_l = A.f32(ttt_model::kMaxSplit * Rt * m->H);
+  m->spart_o = A.f32(ttt_model::kMaxSplit * Rt * HD);
+  m->spart_m = A.f32(ttt_model::kMaxSplit * Rt * m->H);
+  m->spart_l = A.f32(ttt_model::kMaxSplit * Rt * m->H);
   m->dres_c = A.el(Rt * d); m->dZ = A.el(Rt * mg * hf); m->dO = A.el(Rt * HD); m->dqkv = A.el(Rt * 3 * HD);
   m->Tdres.resize(nt); m->Ta.resize(nt); m->Tdz.resize(nt); m->Tn.resize(nt);
   for (int j = 0; j < nt; ++j) {
