@@ -613,6 +613,79 @@ __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __re
   }
 }
 
+// ---------------- skinny products (M <= 8 rows of A, bf16) ----------------
+// Memory-bound on B (the weights): each wave streams whole rows of B with
+// 16-byte loads per lane and forms the M dot products against the rows of A
+// (small, cache-resident), then reduces them across the wave. SwiGLU: a wave
+// takes one hidden unit, i.e. its interleaved gate and up rows.
+constexpr int GV_MAXM = 8;
+TTT_DEV float dot8(bf16x8 a, bf16x8 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+  return s;
+}
+
+template <int EPI, typename OutT>
+__global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
+  const int z = blockIdx.z;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A) + z * p.sA;
+  const bf16* B = reinterpret_cast<const bf16*>(p.B) + z * p.sB;
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * 4;
+  constexpr bool GLU = EPI == EPI_SWIGLU;
+  const int nout = GLU ? p.N / 2 : p.N;
+  for (int o = blockIdx.x * 4 + (threadIdx.x >> 6); o < nout; o += nw) {
+    const int n = GLU ? gate_col(o) : o;
+    const bf16* b0 = B + (int64_t)n * p.ldb;
+    const bf16* b1 = b0 + 32 * p.ldb;  // SwiGLU: the matching up row
+    float acc[GV_MAXM], acc2[GV_MAXM];
+#pragma unroll
+    for (int m = 0; m < GV_MAXM; ++m) { acc[m] = 0.f; acc2[m] = 0.f; }
+    for (int k = lane * 8; k < p.K; k += 512) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(b0 + k);
+      bf16x8 bu;
+      if constexpr (GLU) bu = *reinterpret_cast<const bf16x8*>(b1 + k);
+#pragma unroll
+      for (int m = 0; m < GV_MAXM; ++m) {
+        if (m < p.M) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(A + (int64_t)m * p.lda + k);
+          acc[m] += dot8(av, bv);
+          if constexpr (GLU) acc2[m] += dot8(av, bu);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < GV_MAXM; ++m) {
+      if (m < p.M) {
+        acc[m] = wave_sum(acc[m]);
+        if constexpr (GLU) acc2[m] = wave_sum(acc2[m]);
+      }
+    }
+    // lane m writes row m
+    float v = 0.f, v2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < GV_MAXM; ++m)
+      if (lane == m) { v = acc[m]; v2 = acc2[m]; }
+    if (lane < p.M) {
+      const int row = lane;
+      if constexpr (GLU) {
+        reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)row * p.ldc + o] = from_f32<OutT>(swiglu_acc(v, v2));
+      } else {
+        apply<EPI, OutT, bf16>(p, z, row, n, v);
+      }
+    }
+  }
+}
+
+template <int EPI, typename OutT>
+hipError_t launch_gemv(const GemmArgs& p, int batch, hipStream_t st) {
+  const int nout = EPI == EPI_SWIGLU ? p.N / 2 : p.N;
+  const int blocks = std::min((nout + 3) / 4, 4096);
+  hipLaunchKernelGGL((gemv_kernel<EPI, OutT>), dim3(blocks, 1, batch), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 // test hook: 0 auto, 1 = 256x256, 2 = 256x128, 3 = 128x128, 4 = 256x256 direct-to-LDS
 // (BK 64, two stages), 5 = the same with BK 32 and four stages, 6 / 7 = 128x128
 // direct-to-LDS with two / three stages, 8 / 9 = 128x128 with four stages of BK
@@ -674,6 +747,10 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
   if (!ws) ws_elems = 0;
   int cfg = g_force_tile;
+  if constexpr (sizeof(T) == 2 && EPI != EPI_SGD) {
+    // a few rows of A (decode): one streaming pass over B
+    if (!cfg && p.M <= GV_MAXM) return launch_gemv<EPI, OutT>(p, batch, st);
+  }
   if (!cfg) {
     // direct-to-LDS 256x256 when there are enough large tiles (or K is long
     // enough for split-K to fill the CUs); register-staged kernels otherwise

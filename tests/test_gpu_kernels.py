@@ -90,6 +90,41 @@ def test_gemm_direct_to_lds(tile, epi, shape, ws):
     assert err < 4e-5 * math.sqrt(K), err
 
 
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("epi,out_f32", [(0, True), (0, False), (1, True), (3, False), (4, True)])
+def test_gemm_skinny(M, epi, out_f32):
+    """A few rows of A (decode): the streaming skinny-product kernel, batched,
+    against fp64 for every epilogue but SGD."""
+    lib = bd.load()
+    N, K, batch = 640, 1000, 2
+    A, Ad = rnd((batch, M, K), 1, torch.bfloat16)
+    Bm, Bd = rnd((batch, N, K), 2, torch.bfloat16)
+    z = np.einsum("zmk,znk->zmn", A, Bm)
+    R = Rd = None
+    if epi == 0:
+        ref = z
+    elif epi == 1:
+        R, Rd = rnd((batch, M, N), 3, torch.float32)
+        ref = R + z
+    elif epi == 3:
+        u = np.arange(N // 2)
+        gc = (u // 32) * 64 + u % 32
+        ref = _silu(z[:, :, gc]) * z[:, :, gc + 32]
+    else:
+        ref = _gelu(z)
+    NO = ref.shape[2]
+    cdt = torch.float32 if (out_f32 or epi == 1) else torch.bfloat16
+    C = torch.zeros((batch, M, NO), dtype=cdt, device="cuda")
+    bd.check(lib.ttt_k_gemm(1, epi, int(out_f32), M, N, K, bd.ptr(Ad), K, M * K, bd.ptr(Bd), K, N * K,
+                            bd.ptr(C), NO, M * NO, None, 0, 0, bd.ptr(Rd), N, M * N, None, 0, 0, 0.0, 0, batch,
+                            None, 0, bd.stream_ptr()), kernel=True)
+    sync()
+    got = C.float().cpu().numpy()
+    scale = max(np.abs(ref).max(), 1.0)
+    tol = (4e-5 * math.sqrt(K) if cdt == torch.float32 else 2 ** -8 * 2) * scale
+    assert np.abs(got - ref).max() <= tol
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_gemm_store_compute_dtype(dtype):
     ref, got, _, _ = run_gemm(dtype, 0, 130, 64, 64, out_f32=False)
