@@ -56,7 +56,7 @@ void ttt_k_gemm_tile(int32_t cfg);
  * q, o: [B*M][H*hd] rows (row s*M+i = position pos0+i of sequence s);
  * kc, vc: [B][cap][H*hd], key position j at slot j % cap (cap multiple of 64);
  * lse: fp32 [B][H][M] natural-log sum of exp of the scaled scores.
- * nsplit (1..8) splits each query block's key range over workgroups; with
+ * nsplit (1..16) splits each query block's key range over workgroups; with
  * nsplit > 1, H <= 64 and ws is an fp32 workspace of nsplit*B*M*(H*hd + 2*H)
  * elements. */
 int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
 constexpr int COMBINE_MAX_H = 64;
 template <typename T>
 __global__ void attn_combine_kernel(AttnArgs a) {
-  __shared__ float wgt[8][COMBINE_MAX_H];
+  __shared__ float wgt[16][COMBINE_MAX_H];
   const int64_t row = blockIdx.x;  // s*M + q
   const int s = row / a.M, q = row % a.M;
   const int HD = a.H * a.hd;
@@ -759,14 +759,14 @@ int attn_splits(int M, int H, int B, int64_t keys_per_query) {
   // enough waves to cover the CUs twice, each split keeping >= 8 key tiles
   const int64_t waves = (int64_t)((M + WQ - 1) / WQ) * H * B;
   int ns = 1;
-  while (waves * ns < 2048 && keys_per_query / (BKEY * ns * 2) >= 8 && ns < 8) ns *= 2;
+  while (waves * ns < 2048 && keys_per_query / (BKEY * ns * 2) >= 8 && ns < 16) ns *= 2;
   return ns;
 }
 
 hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
   if (a.nsplit > 1 && (!a.part_o || !a.part_m || !a.part_l)) return hipErrorInvalidValue;
-  if (a.nsplit > 8 || (a.nsplit > 1 && (a.H > COMBINE_MAX_H || a.ldo % 4))) return hipErrorInvalidValue;
+  if (a.nsplit > 16 || (a.nsplit > 1 && (a.H > COMBINE_MAX_H || a.ldo % 4))) return hipErrorInvalidValue;
   TTT_HD_SWITCH(fwd_t)
 }
 

@@ -62,7 +62,7 @@ int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc,
                    float scale, int32_t nsplit, float* ws, void* stream) {
   if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
     return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
-  if (nsplit < 1 || nsplit > 8 || (nsplit > 1 && !ws)) return kfail(TTT_EINVAL, "nsplit in 1..8, ws for > 1");
+  if (nsplit < 1 || nsplit > 16 || (nsplit > 1 && !ws)) return kfail(TTT_EINVAL, "nsplit in 1..16, ws for > 1");
   AttnArgs a = mk(q, kc, vc, cap, B, M, H, hd, pos0, window, scale);
   a.o = o; a.ldo = (int64_t)H * hd; a.lse = lse;
   a.nsplit = nsplit;
@@ -79,7 +79,7 @@ int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc,
                    int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, int32_t nsplit, void* stream) {
   if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
     return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
-  if (nsplit < 1 || nsplit > 8) return kfail(TTT_EINVAL, "nsplit in 1..8");
+  if (nsplit < 1 || nsplit > 16) return kfail(TTT_EINVAL, "nsplit in 1..16");
   AttnArgs a = mk(q, kc, vc, cap, B, M, H, hd, pos0, window, scale);
   const int64_t HD = (int64_t)H * hd;
   a.lse = const_cast<float*>(lse); a.dout = dout; a.lddo = HD; a.delta = delta;

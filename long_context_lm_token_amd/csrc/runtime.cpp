@@ -123,7 +123,7 @@ struct ttt_model {
   float* ws = nullptr;  // split-K partials
   int64_t ws_elems = 0;
   // key-range splits of the chunk attention: forward partials (dq slices use dq)
-  static constexpr int kMaxSplit = 8;
+  static constexpr int kMaxSplit = 16;
   float *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
   // the same for span passes of at most one chunk of rows (decode, the last
   // rows of a prefill): their own buffers, as span passes run on the prefix
