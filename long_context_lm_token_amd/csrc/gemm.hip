@@ -628,51 +628,62 @@ TTT_DEV float dot8(bf16x8 a, bf16x8 b) {
 
 template <int EPI, typename OutT>
 __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
+  // each wave streams GV_ROWS outputs at once (more loads in flight)
+  constexpr int GV_ROWS = 2;
+  constexpr bool GLU = EPI == EPI_SWIGLU;
+  constexpr int NB = GLU ? 2 * GV_ROWS : GV_ROWS;  // rows of B per wave step
   const int z = blockIdx.z;
   const bf16* A = reinterpret_cast<const bf16*>(p.A) + z * p.sA;
   const bf16* B = reinterpret_cast<const bf16*>(p.B) + z * p.sB;
   const int lane = threadIdx.x & 63;
   const int nw = gridDim.x * 4;
-  constexpr bool GLU = EPI == EPI_SWIGLU;
   const int nout = GLU ? p.N / 2 : p.N;
-  for (int o = blockIdx.x * 4 + (threadIdx.x >> 6); o < nout; o += nw) {
-    const int n = GLU ? gate_col(o) : o;
-    const bf16* b0 = B + (int64_t)n * p.ldb;
-    const bf16* b1 = b0 + 32 * p.ldb;  // SwiGLU: the matching up row
-    float acc[GV_MAXM], acc2[GV_MAXM];
+  for (int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * GV_ROWS; o0 < nout; o0 += nw * GV_ROWS) {
+    const bf16* brow[NB];
 #pragma unroll
-    for (int m = 0; m < GV_MAXM; ++m) { acc[m] = 0.f; acc2[m] = 0.f; }
+    for (int q = 0; q < GV_ROWS; ++q) {
+      const int o = min(o0 + q, nout - 1);  // a tail wave repeats the last output (not stored)
+      const int n = GLU ? gate_col(o) : o;
+      brow[q] = B + (int64_t)n * p.ldb;
+      if constexpr (GLU) brow[GV_ROWS + q] = brow[q] + 32 * p.ldb;  // the matching up row
+    }
+    float acc[NB][GV_MAXM];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int m = 0; m < GV_MAXM; ++m) acc[q][m] = 0.f;
     for (int k = lane * 8; k < p.K; k += 512) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(b0 + k);
-      bf16x8 bu;
-      if constexpr (GLU) bu = *reinterpret_cast<const bf16x8*>(b1 + k);
+      bf16x8 bv[NB];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) bv[q] = *reinterpret_cast<const bf16x8*>(brow[q] + k);
 #pragma unroll
       for (int m = 0; m < GV_MAXM; ++m) {
         if (m < p.M) {
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(A + (int64_t)m * p.lda + k);
-          acc[m] += dot8(av, bv);
-          if constexpr (GLU) acc2[m] += dot8(av, bu);
+#pragma unroll
+          for (int q = 0; q < NB; ++q) acc[q][m] += dot8(av, bv[q]);
         }
       }
     }
 #pragma unroll
-    for (int m = 0; m < GV_MAXM; ++m) {
-      if (m < p.M) {
-        acc[m] = wave_sum(acc[m]);
-        if constexpr (GLU) acc2[m] = wave_sum(acc2[m]);
-      }
-    }
-    // lane m writes row m
-    float v = 0.f, v2 = 0.f;
+    for (int q = 0; q < NB; ++q)
 #pragma unroll
-    for (int m = 0; m < GV_MAXM; ++m)
-      if (lane == m) { v = acc[m]; v2 = acc2[m]; }
+      for (int m = 0; m < GV_MAXM; ++m)
+        if (m < p.M) acc[q][m] = wave_sum(acc[q][m]);
+    // lane m writes row m of each output
     if (lane < p.M) {
-      const int row = lane;
-      if constexpr (GLU) {
-        reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)row * p.ldc + o] = from_f32<OutT>(swiglu_acc(v, v2));
-      } else {
-        apply<EPI, OutT, bf16>(p, z, row, n, v);
+#pragma unroll
+      for (int q = 0; q < GV_ROWS; ++q) {
+        const int o = o0 + q;
+        if (o >= nout) break;
+        float v = 0.f, v2 = 0.f;
+#pragma unroll
+        for (int m = 0; m < GV_MAXM; ++m)
+          if (lane == m) { v = acc[q][m]; if constexpr (GLU) v2 = acc[GV_ROWS + q][m]; }
+        if constexpr (GLU)
+          reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)lane * p.ldc + o] = from_f32<OutT>(swiglu_acc(v, v2));
+        else
+          apply<EPI, OutT, bf16>(p, z, lane, o, v);
       }
     }
   }
@@ -681,7 +692,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
 template <int EPI, typename OutT>
 hipError_t launch_gemv(const GemmArgs& p, int batch, hipStream_t st) {
   const int nout = EPI == EPI_SWIGLU ? p.N / 2 : p.N;
-  const int blocks = std::min((nout + 3) / 4, 4096);
+  const int blocks = std::min((nout + 7) / 8, 4096);  // 4 waves of 2 outputs
   hipLaunchKernelGGL((gemv_kernel<EPI, OutT>), dim3(blocks, 1, batch), dim3(256), 0, st, p);
   return hipGetLastError();
 }
