@@ -48,7 +48,8 @@ int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N
  * stage ring (bf16, K a multiple of 64), 8 / 9 = 128x128 with a four-stage
  * ring of 64 / 32 deep K tiles; each splits K when the tile count is low and
  * a workspace is given; 4 and 5 fall back to 1, 6 to 9 to 3 where they do
- * not apply). Process-wide. */
+ * not apply). cfg >> 8, when non-zero, forces the number of K splits (1 when
+ * the workspace is too small or K has fewer tiles). Process-wide. */
 void ttt_k_gemm_tile(int32_t cfg);
 
 /* Sliding-window attention forward over a ring cache (query p sees keys

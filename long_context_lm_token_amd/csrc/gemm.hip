@@ -700,8 +700,9 @@ hipError_t launch_gemv(const GemmArgs& p, int batch, hipStream_t st) {
 // test hook: 0 auto, 1 = 256x256, 2 = 256x128, 3 = 128x128, 4 = 256x256 direct-to-LDS
 // (BK 64, two stages), 5 = the same with BK 32 and four stages, 6 / 7 = 128x128
 // direct-to-LDS with two / three stages, 8 / 9 = 128x128 with four stages of BK
-// 64 / 32 (each + split-K)
+// 64 / 32 (each + split-K); bits 8.. force the number of K splits (0: chosen)
 int g_force_tile = 0;
+int g_force_splits = 0;
 
 template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>
 hipError_t launch_dl(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
@@ -740,6 +741,8 @@ int k_splits(const GemmArgs& p, int batch, int64_t tiles, int64_t target, int64_
     return 1;
   int splits = 1;
   const int nk = (p.K + GT<T>::BK - 1) / GT<T>::BK;
+  if (g_force_splits > 0)
+    return (int64_t)g_force_splits * batch * p.M * p.N <= ws_elems && nk >= g_force_splits ? g_force_splits : 1;
   while ((tiles * splits < target || (max_kt > 0 && tiles * splits < 2 * target && nk / splits > max_kt)) &&
          nk / (splits * 2) >= 8 && splits < 8 && (int64_t)(splits * 2) * batch * p.M * p.N <= ws_elems)
     splits *= 2;
@@ -827,7 +830,10 @@ hipError_t dispatch(const GemmArgs& p, int epi, bool out_f32, int batch, float* 
 
 }  // namespace
 
-void gemm_force_tile(int cfg) { g_force_tile = cfg; }
+void gemm_force_tile(int cfg) {
+  g_force_tile = cfg & 255;
+  g_force_splits = cfg >> 8;
+}
 
 hipError_t gemm_launch(const GemmArgs& p, int dtype, int epi, bool out_f32, int batch, float* ws, int64_t ws_elems,
                        hipStream_t st) {
