@@ -59,7 +59,8 @@ void ttt_k_gemm_tile(int32_t cfg);
  * lse: fp32 [B][H][M] natural-log sum of exp of the scaled scores.
  * nsplit (1..16) splits each query block's key range over workgroups; with
  * nsplit > 1, H <= 64 and ws is an fp32 workspace of nsplit*B*M*(H*hd + 2*H)
- * elements. */
+ * elements. Every slot of a 64-key tile that holds a visible key must hold
+ * finite K and V values (the tile's other keys get weight exactly 0). */
 int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
                    float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
                    float scale, int32_t nsplit, float* ws, void* stream);
@@ -72,6 +73,11 @@ int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc,
 int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, const float* lse,
                    const void* dout, const float* delta, float* dq, float* dk, float* dv, int32_t B, int32_t M,
                    int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, int32_t nsplit, void* stream);
+
+/* Test hook: 0 runs bf16 head-dim-128 forwards on the register-staged kernel
+ * (the kernel of the other head dims), 1 (default) on the direct-to-LDS one.
+ * Process-wide. */
+void ttt_k_attn_fwd_kernel(int32_t dl);
 
 /* The library's choice of key-range splits for M queries per sequence. */
 int32_t ttt_k_attn_splits(int32_t M, int32_t H, int32_t B, int64_t keys_per_query);

@@ -85,6 +85,8 @@ def load():
                                    c_i64, c_i32, c_f32, c_i32, c_vp, c_vp]
     lib.ttt_k_attn_bwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                    c_i32, c_i32, c_i32, c_i64, c_i32, c_f32, c_i32, c_vp]
+    lib.ttt_k_attn_fwd_kernel.argtypes = [c_i32]
+    lib.ttt_k_attn_fwd_kernel.restype = None
     lib.ttt_k_attn_splits.argtypes = [c_i32, c_i32, c_i32, c_i64]
     lib.ttt_k_attn_delta.argtypes = [c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
     lib.ttt_k_ce.argtypes = [c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp, c_vp, c_vp]

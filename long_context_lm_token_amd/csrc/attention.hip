@@ -380,10 +380,252 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// ---- forward, bf16 with head dim 128: direct-to-LDS tiles, pipelined scores ----
+// The same computation as attn_fwd_kernel with three changes:
+//  * K and V tiles go from global memory straight into LDS (global_load_lds,
+//    16 bytes per lane): no staging registers, no per-element copy code. The
+//    rows are unpadded (256 bytes); their 16-byte chunks are XOR-swizzled so
+//    that K's row-wise fragment reads (16 rows, one chunk) and V's transposing
+//    reads (4 rows x 2 chunks per 16 lanes) hit distinct banks.
+//  * Keys past the last query of the block are read as stored: their scores
+//    are masked to -inf, so their weights are exactly 0; the caches hold
+//    finite values, so 0 * V adds nothing.
+//  * K and V have separate two-slot rings. Iteration t multiplies S(t+1) =
+//    K(t+1) Q^T while it exponentiates tile t (one basic block, so the
+//    scheduler interleaves the MFMAs with the softmax VALU work), then
+//    accumulates V(t)^T P(t)^T. Its loads (K(t+2), V(t+1)) overlap the whole
+//    iteration.
+constexpr int FD_HD = 128;
+typedef __attribute__((address_space(3))) void fd_lds_t;
+
+// K row r keeps 16-byte chunk c at chunk c ^ (r % 16); V row r at c ^ 4 (r % 4)
+TTT_DEV int fd_kswz(int r) { return r & 15; }
+TTT_DEV int fd_vswz(int r) { return (r & 3) << 2; }
+
+// this wave's 4 of the 16 one-KB loads of a 64-row tile whose row 0 is `base`:
+// load i of wave w fills LDS bytes [1 KB (4w + i), +1 KB), rows 4(4w+i) ..
+// +3; `off` holds each lane's element offset from `base` (swizzled chunk)
+TTT_DEV void fd_issue(const bf16* base, const uint32_t (&off)[4], bf16* tile, int w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (fd_lds_t*)(tile + (w * 4 + i) * 512), 16, 0, 0);
+}
+template <bool ISK>
+TTT_DEV void fd_offsets(int64_t ld, int w, int lane, uint32_t (&off)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (w * 4 + i) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (ISK ? fd_kswz(r) : fd_vswz(r));
+    off[i] = (uint32_t)(r * ld + c * 8);
+  }
+}
+
+// wait until none of this wave's vector-memory loads (LDS-DMA included) is in flight
+TTT_DEV void fd_wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+TTT_DEV bf16x8 fd_kfrag(const bf16* t, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(t + r * FD_HD + ((c ^ fd_kswz(r)) << 3));
+}
+
+// V^T fragment (see lds_frag_tr) from the swizzled V tile; rows key and key+8
+// share their swizzle (key % 4)
+TTT_DEV bf16x8 fd_vfrag(const bf16* t, int d0, int g, int u, int lane) {
+  const int key = g * 32 + u * 16 + (lane >> 5) * 4 + ((lane & 15) >> 2);
+  const int col = d0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  const int off = key * FD_HD + (((col >> 3) ^ fd_vswz(key)) << 3) + (col & 7);
+  typedef __attribute__((address_space(3))) s16x4 lds_v4;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + off));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + off + 8 * FD_HD));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
+  constexpr int NKS = FD_HD / 16, DB = FD_HD / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 sK[2][BKEY * FD_HD];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[2][BKEY * FD_HD];
+
+  const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
+  const Blk bk = blk();
+  const int s = bk.z / nsplit, sp = bk.z % nsplit, h = bk.y;
+  const int lane = threadIdx.x & 63, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int M = a.M;
+  const int qb0 = bk.x * QB;
+  const int qw0 = qb0 + w * WQ;
+  const int q = qw0 + (lane & 31);
+  const bool qvalid = q < M;
+  const int pos0 = (int)a.pos0;
+  const int pq = pos0 + (qvalid ? q : M - 1);
+  const int win = a.window;
+  const bf16* Kc = reinterpret_cast<const bf16*>(a.kc) + s * a.seq_stride + h * FD_HD;
+  const bf16* Vc = reinterpret_cast<const bf16*>(a.vc) + s * a.seq_stride + h * FD_HD;
+
+  bf16x8 qf[NKS];
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((int64_t)s * M + (qvalid ? q : 0)) * a.ldq + h * FD_HD;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hl * 8) : bf16x8{};
+  }
+
+  const int qlast_blk = min(qb0 + QB, M) - 1;
+  const int lo = max(0, pos0 + qb0 - win + 1);
+  const int hi = pos0 + qlast_blk;
+  int jb, je;
+  split_range(lo & ~(BKEY - 1), hi, nsplit, sp, &jb, &je);
+  const int nt = (je - jb) / BKEY;
+  const bool wactive = qw0 < M;
+  const int wfirst = pos0 + qw0;
+  const int wlast = pos0 + min(qw0 + WQ, M) - 1;
+
+  const float c2 = a.scale * LOG2E;
+  float m_i = NEG_BIG, l_i = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+
+  // a 64-aligned key tile occupies 64 consecutive ring slots (cap % 64 == 0);
+  // tile t starts at ring row (jb + 64 t) mod cap, and nt * 64 <= cap
+  uint32_t koff[4], voff[4];
+  fd_offsets<true>(a.ldk, w, lane, koff);
+  fd_offsets<false>(a.ldk, w, lane, voff);
+  const int r0 = jb % a.cap;
+  auto row = [&](int t) {
+    const int r = r0 + t * BKEY;
+    return (int64_t)(r >= a.cap ? r - a.cap : r) * a.ldk;
+  };
+  auto scores = [&](const bf16* cK, f32x16 (&st)[2]) {
+    st[0] = f32x16{};
+    st[1] = f32x16{};
+    const int kr = lane & 31;
+    bf16x8 kf[2][2];
+    kf[0][0] = fd_kfrag(cK, kr, hl);
+    kf[0][1] = fd_kfrag(cK, 32 + kr, hl);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS) {
+        kf[(ks + 1) & 1][0] = fd_kfrag(cK, kr, (ks + 1) * 2 + hl);
+        kf[(ks + 1) & 1][1] = fd_kfrag(cK, 32 + kr, (ks + 1) * 2 + hl);
+      }
+      st[0] = mfma(kf[ks & 1][0], qf[ks], st[0]);
+      st[1] = mfma(kf[ks & 1][1], qf[ks], st[1]);
+    }
+  };
+  // one key tile: cur = S(t) in, nxt = S(t+1) out
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    // this wave's loads of K(t+1) and V(t) are the only ones in flight; after
+    // the barrier every wave's are in LDS and K(t) / V(t-1) are no longer read
+    fd_wait_loads();
+    __syncthreads();
+    if (t + 2 < nt) fd_issue(Kc + row(t + 2), koff, sK[t & 1], w);
+    if (t + 1 < nt) fd_issue(Vc + row(t + 1), voff, sV[(t + 1) & 1], w);
+    if (!wactive) return;
+    const int j0 = jb + t * BKEY;
+    // masking and the running max of tile t
+    if (!((j0 + BKEY - 1 <= wfirst) && (j0 > wlast - win))) {
+      // visible iff pq - win < j <= pq, i.e. 0 <= pq - j < win
+      const int dj = pq - (j0 + hl * 4);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const unsigned tt = (unsigned)(dj - g * 32 - (r >> 2) * 8 - (r & 3));
+          if (tt >= (unsigned)win) cur[g][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[g][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    if (__any(mx > m_i + RESCALE_SLACK)) {   // wave-uniform branch
+      const float m_new = fmaxf(m_i, mx);
+      const float alpha = ex2(m_i - m_new);
+      l_i *= alpha;
+      m_i = m_new;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) o[i] *= alpha;
+    }
+    // S(t+1) (the last step computes an unused one from a stale slot)
+    // alongside the exponentials of tile t
+    scores(sK[(t + 1) & 1], nxt);
+    bf16x8 pf[2][2];
+    float rs = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = ex2(fmaf(cur[g][u * 8 + e], c2, -m_i));
+          rs += pv;
+          pf[g][u][e] = (bf16)pv;
+        }
+    l_i += rs;
+    const bf16* cV = sV[t & 1];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 vf[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) vf[i] = fd_vfrag(cV, i * 32, g, u, lane);
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[i] = mfma(vf[i], pf[g][u], o[i]);
+      }
+  };
+
+  f32x16 sa[2], sb[2];
+  if (nt > 0) {
+    fd_issue(Kc + row(0), koff, sK[0], w);
+    fd_issue(Vc + row(0), voff, sV[0], w);
+    if (nt > 1) fd_issue(Kc + row(1), koff, sK[1], w);
+    fd_wait_loads();
+    __syncthreads();
+    if (wactive) scores(sK[0], sa);
+  }
+  // two steps per trip, so the score tiles swap roles without copies
+  for (int t = 0; t < nt; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < nt) step(t + 1, sb, sa);
+  }
+
+  if (!wactive || !qvalid) return;
+  const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
+  if (nsplit == 1) {
+    const float inv = 1.f / l_tot;
+    bf16* O = reinterpret_cast<bf16*>(a.o) + ((int64_t)s * M + q) * a.ldo + h * FD_HD;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[i * 32 + acc_row(r, hl)] = from_f32<bf16>(o[i][r] * inv);
+    if (hl == 0) a.lse[((int64_t)s * a.H + h) * M + q] = m_i * LN2 + logf(l_tot);
+  } else {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t row = (int64_t)s * M + q;
+    float* O = a.part_o + ((int64_t)sp * a.B * M + row) * a.ldo + h * FD_HD;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[i * 32 + acc_row(r, hl)] = o[i][r] * inv;
+    if (hl == 0) {
+      const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * M + q;
+      a.part_m[li] = m_i;
+      a.part_l[li] = l_tot;
+    }
+  }
+}
+
 // merge split partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - m).
 // One workgroup per row: the normalised weights of every (split, head) go to
 // LDS first, then each thread combines 4 consecutive columns.
 constexpr int COMBINE_MAX_H = 64;
+// test hook: 0 keeps bf16 head-dim-128 forwards on the register-staged kernel
+int g_attn_dl = 1;
 template <typename T>
 __global__ void attn_combine_kernel(AttnArgs a) {
   __shared__ float wgt[16][COMBINE_MAX_H];
@@ -717,7 +959,12 @@ template <typename T, int HD>
 hipError_t fwd_t(const AttnArgs& a, hipStream_t st) {
   const int ns = a.nsplit > 0 ? a.nsplit : 1;
   dim3 grid((a.M + QB - 1) / QB, a.H, a.B * ns);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
+      a.seq_stride % 8 == 0)
+    hipLaunchKernelGGL(attn_fwd_dl_kernel, grid, dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   hipLaunchKernelGGL((attn_combine_kernel<T>), dim3(a.B * a.M), dim3(256), 0, st, a);
@@ -769,6 +1016,8 @@ hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st) {
   if (a.nsplit > 16 || (a.nsplit > 1 && (a.H > COMBINE_MAX_H || a.ldo % 4))) return hipErrorInvalidValue;
   TTT_HD_SWITCH(fwd_t)
 }
+
+void attn_force_fwd_kernel(int dl) { g_attn_dl = dl; }
 
 hipError_t attn_bwd_launch(const AttnArgs& a, int dt, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;

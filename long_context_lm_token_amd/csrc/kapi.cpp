@@ -88,6 +88,8 @@ int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc,
   return kdone(attn_bwd_launch(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
+void ttt_k_attn_fwd_kernel(int32_t dl) { attn_force_fwd_kernel(dl); }
+
 int32_t ttt_k_attn_splits(int32_t M, int32_t H, int32_t B, int64_t keys_per_query) {
   return attn_splits(M, H, B, keys_per_query);
 }

@@ -252,8 +252,10 @@ def attn_case(dtype, B, M, H, hd, pos0, window, seed=0):
     K, _ = rnd((B, npos, H, hd), seed + 1, dtype)
     V, _ = rnd((B, npos, H, hd), seed + 2, dtype)
     q, qd = rnd((B, M, H, hd), seed + 3, dtype)
-    kc = np.zeros((B, cap, HD))
-    vc = np.zeros((B, cap, HD))
+    # slots outside the window hold unrelated finite values: they must get weight 0
+    junk = np.random.default_rng(seed + 4)
+    kc = junk.standard_normal((B, cap, HD)) * 3
+    vc = junk.standard_normal((B, cap, HD)) * 3
     for i, p in enumerate(range(lo, pos0 + M)):
         kc[:, p % cap] = K[:, i].reshape(B, HD)
         vc[:, p % cap] = V[:, i].reshape(B, HD)
@@ -261,14 +263,15 @@ def attn_case(dtype, B, M, H, hd, pos0, window, seed=0):
     return dict(cap=cap, K=K, V=V, q=q, qd=qd.reshape(B * M, HD).contiguous(), kcd=kcd, vcd=vcd, lo=lo)
 
 
-@pytest.mark.parametrize("dtype,hd", [(torch.float32, 16), (torch.float32, 64), (torch.bfloat16, 64),
-                                      (torch.bfloat16, 128)])
+@pytest.mark.parametrize("dtype,hd,dl", [(torch.float32, 16, 1), (torch.float32, 64, 1), (torch.bfloat16, 64, 1),
+                                         (torch.bfloat16, 128, 1), (torch.bfloat16, 128, 0)])
 @pytest.mark.parametrize("B,M,H,pos0,window,nsplit", [(1, 100, 2, 0, 128, 1), (2, 64, 3, 300, 96, 1),
                                                       (1, 200, 2, 1000, 64, 1), (1, 1, 2, 517, 256, 1),
                                                       (1, 130, 2, 900, 512, 4), (2, 64, 3, 1500, 1024, 8),
                                                       (1, 1, 2, 2000, 1024, 8), (1, 100, 2, 0, 128, 2),
                                                       (1, 1, 3, 4000, 2048, 16), (2, 33, 2, 3000, 2048, 16)])
-def test_attention_fwd_bwd(dtype, hd, B, M, H, pos0, window, nsplit):
+def test_attention_fwd_bwd(dtype, hd, dl, B, M, H, pos0, window, nsplit):
+    """dl: forward kernel of bf16 head dim 128 (1 direct-to-LDS, 0 register-staged)."""
     lib = bd.load()
     c = attn_case(dtype, B, M, H, hd, pos0, window)
     HD = H * hd
@@ -276,10 +279,14 @@ def test_attention_fwd_bwd(dtype, hd, B, M, H, pos0, window, nsplit):
     o = torch.zeros((B * M, HD), dtype=dtype, device="cuda")
     lse = torch.zeros((B, H, M), dtype=torch.float32, device="cuda")
     ws = torch.zeros(nsplit * B * M * (HD + 2 * H), device="cuda")
-    bd.check(lib.ttt_k_attn_fwd(kdt(dtype), bd.ptr(c["qd"]), bd.ptr(c["kcd"]), bd.ptr(c["vcd"]), c["cap"],
-                                bd.ptr(o), bd.ptr(lse), B, M, H, hd, pos0, window, scale, nsplit, bd.ptr(ws),
-                                bd.stream_ptr()),
-             kernel=True)
+    lib.ttt_k_attn_fwd_kernel(dl)
+    try:
+        bd.check(lib.ttt_k_attn_fwd(kdt(dtype), bd.ptr(c["qd"]), bd.ptr(c["kcd"]), bd.ptr(c["vcd"]), c["cap"],
+                                    bd.ptr(o), bd.ptr(lse), B, M, H, hd, pos0, window, scale, nsplit, bd.ptr(ws),
+                                    bd.stream_ptr()),
+                 kernel=True)
+    finally:
+        lib.ttt_k_attn_fwd_kernel(1)
     do, dod = rnd((B, M, H, hd), 9, dtype)
     dod = dod.reshape(B * M, HD).contiguous()
     delta = torch.zeros((B, H, M), dtype=torch.float32, device="cuda")
