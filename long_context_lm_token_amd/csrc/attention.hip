@@ -384,9 +384,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
 // The same computation as attn_fwd_kernel with three changes:
 //  * K and V tiles go from global memory straight into LDS (global_load_lds,
 //    16 bytes per lane): no staging registers, no per-element copy code. The
-//    rows are unpadded (256 bytes); their 16-byte chunks are XOR-swizzled so
-//    that K's row-wise fragment reads (16 rows, one chunk) and V's transposing
-//    reads (4 rows x 2 chunks per 16 lanes) hit distinct banks.
+//    rows are unpadded (256 bytes); their 16-byte chunks are XOR-swizzled
+//    (fd_swz) so that K's row-wise fragment reads and V's transposing reads
+//    hit distinct banks.
 //  * Keys past the last query of the block are read as stored: their scores
 //    are masked to -inf, so their weights are exactly 0; the caches hold
 //    finite values, so 0 * V adds nothing.
@@ -398,9 +398,19 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnArgs a) {
 constexpr int FD_HD = 128;
 typedef __attribute__((address_space(3))) void fd_lds_t;
 
-// K row r keeps 16-byte chunk c at chunk c ^ (r % 16); V row r at c ^ 4 (r % 4)
-TTT_DEV int fd_kswz(int r) { return r & 15; }
-TTT_DEV int fd_vswz(int r) { return (r & 3) << 2; }
+// Row r of a tile keeps its 16-byte chunk c at chunk c ^ swz<Z>(r):
+//  Z = 0: r % 16, for tiles read row-wise (a 16-lane fragment read takes one
+//         chunk of 16 consecutive rows);
+//  Z = 1: 4 (r % 4), for tiles read transposed (a 16-lane transposing read
+//         takes 2 chunks of 4 consecutive rows, 4-aligned);
+//  Z = 2: 4 (r % 4) + (r / 4) % 4, for tiles read both ways (a bijection on
+//         16 consecutive rows that also keeps the 4-row groups apart).
+template <int Z>
+TTT_DEV int fd_swz(int r) {
+  if constexpr (Z == 0) return r & 15;
+  else if constexpr (Z == 1) return (r & 3) << 2;
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 
 // this wave's 4 of the 16 one-KB loads of a 64-row tile whose row 0 is `base`:
 // load i of wave w fills LDS bytes [1 KB (4w + i), +1 KB), rows 4(4w+i) ..
@@ -410,12 +420,12 @@ TTT_DEV void fd_issue(const bf16* base, const uint32_t (&off)[4], bf16* tile, in
   for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (fd_lds_t*)(tile + (w * 4 + i) * 512), 16, 0, 0);
 }
-template <bool ISK>
+template <int Z>
 TTT_DEV void fd_offsets(int64_t ld, int w, int lane, uint32_t (&off)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (w * 4 + i) * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (ISK ? fd_kswz(r) : fd_vswz(r));
+    const int c = (lane & 15) ^ fd_swz<Z>(r);
     off[i] = (uint32_t)(r * ld + c * 8);
   }
 }
@@ -423,19 +433,23 @@ TTT_DEV void fd_offsets(int64_t ld, int w, int lane, uint32_t (&off)[4]) {
 // wait until none of this wave's vector-memory loads (LDS-DMA included) is in flight
 TTT_DEV void fd_wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-TTT_DEV bf16x8 fd_kfrag(const bf16* t, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(t + r * FD_HD + ((c ^ fd_kswz(r)) << 3));
+// row-wise fragment: row r, 8 elements from chunk c
+template <int Z>
+TTT_DEV bf16x8 fd_frag(const bf16* t, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(t + r * FD_HD + ((c ^ fd_swz<Z>(r)) << 3));
 }
 
-// V^T fragment (see lds_frag_tr) from the swizzled V tile; rows key and key+8
-// share their swizzle (key % 4)
-TTT_DEV bf16x8 fd_vfrag(const bf16* t, int d0, int g, int u, int lane) {
+// transposed-view fragment (see lds_frag_tr) of a swizzled tile
+template <int Z>
+TTT_DEV bf16x8 fd_frag_tr(const bf16* t, int d0, int g, int u, int lane) {
   const int key = g * 32 + u * 16 + (lane >> 5) * 4 + ((lane & 15) >> 2);
   const int col = d0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  const int off = key * FD_HD + (((col >> 3) ^ fd_vswz(key)) << 3) + (col & 7);
+  const int c = col >> 3;
+  const int o0 = key * FD_HD + ((c ^ fd_swz<Z>(key)) << 3) + (col & 7);
+  const int o1 = (key + 8) * FD_HD + ((c ^ fd_swz<Z>(key + 8)) << 3) + (col & 7);
   typedef __attribute__((address_space(3))) s16x4 lds_v4;
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + off));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + off + 8 * FD_HD));
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + o0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + o1));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v;
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
@@ -490,8 +504,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
   // a 64-aligned key tile occupies 64 consecutive ring slots (cap % 64 == 0);
   // tile t starts at ring row (jb + 64 t) mod cap, and nt * 64 <= cap
   uint32_t koff[4], voff[4];
-  fd_offsets<true>(a.ldk, w, lane, koff);
-  fd_offsets<false>(a.ldk, w, lane, voff);
+  fd_offsets<0>(a.ldk, w, lane, koff);
+  fd_offsets<1>(a.ldk, w, lane, voff);
   const int r0 = jb % a.cap;
   auto row = [&](int t) {
     const int r = r0 + t * BKEY;
@@ -502,13 +516,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
     st[1] = f32x16{};
     const int kr = lane & 31;
     bf16x8 kf[2][2];
-    kf[0][0] = fd_kfrag(cK, kr, hl);
-    kf[0][1] = fd_kfrag(cK, 32 + kr, hl);
+    kf[0][0] = fd_frag<0>(cK, kr, hl);
+    kf[0][1] = fd_frag<0>(cK, 32 + kr, hl);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks + 1 < NKS) {
-        kf[(ks + 1) & 1][0] = fd_kfrag(cK, kr, (ks + 1) * 2 + hl);
-        kf[(ks + 1) & 1][1] = fd_kfrag(cK, 32 + kr, (ks + 1) * 2 + hl);
+        kf[(ks + 1) & 1][0] = fd_frag<0>(cK, kr, (ks + 1) * 2 + hl);
+        kf[(ks + 1) & 1][1] = fd_frag<0>(cK, 32 + kr, (ks + 1) * 2 + hl);
       }
       st[0] = mfma(kf[ks & 1][0], qf[ks], st[0]);
       st[1] = mfma(kf[ks & 1][1], qf[ks], st[1]);
@@ -573,7 +587,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
       for (int u = 0; u < 2; ++u) {
         bf16x8 vf[DB];
 #pragma unroll
-        for (int i = 0; i < DB; ++i) vf[i] = fd_vfrag(cV, i * 32, g, u, lane);
+        for (int i = 0; i < DB; ++i) vf[i] = fd_frag_tr<1>(cV, i * 32, g, u, lane);
 #pragma unroll
         for (int i = 0; i < DB; ++i) o[i] = mfma(vf[i], pf[g][u], o[i]);
       }
@@ -624,7 +638,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
 // One workgroup per row: the normalised weights of every (split, head) go to
 // LDS first, then each thread combines 4 consecutive columns.
 constexpr int COMBINE_MAX_H = 64;
-// test hook: 0 keeps bf16 head-dim-128 forwards on the register-staged kernel
+// test hook: 0 keeps bf16 head-dim-128 forwards and dQ on the register-staged kernels
 int g_attn_dl = 1;
 template <typename T>
 __global__ void attn_combine_kernel(AttnArgs a) {
@@ -803,6 +817,141 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(AttnArgs a) {
     }
 }
 
+// dQ kernel for bf16 with head dim 128: the computation of attn_bwd_dq_kernel
+// with K and V tiles loaded straight into swizzled LDS (two-slot rings, tile
+// t+1 in flight during tile t), K swizzled for both its row-wise reads (S) and
+// its transposed reads (dQ^T += K^T dS^T), and the window mask applied only
+// on tiles that cross a window edge. Keys past the last query are read as
+// stored: their weights are masked to 0, and the caches hold finite values.
+__global__ __launch_bounds__(NT, 2) void attn_bwd_dq_dl_kernel(AttnArgs a) {
+  constexpr int NKS = FD_HD / 16, DB = FD_HD / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 sK[2][BKEY * FD_HD];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[2][BKEY * FD_HD];
+
+  const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
+  const Blk bk = blk();
+  const int s = bk.z / nsplit, sp = bk.z % nsplit, h = bk.y;
+  const int lane = threadIdx.x & 63, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int M = a.M;
+  const int qb0 = bk.x * QB;
+  const int qw0 = qb0 + w * WQ;
+  const int q = qw0 + (lane & 31);
+  const bool qvalid = q < M;
+  const int pos0 = (int)a.pos0;
+  const int pq = pos0 + (qvalid ? q : M - 1);
+  const int win = a.window;
+  const bf16* Kc = reinterpret_cast<const bf16*>(a.kc) + s * a.seq_stride + h * FD_HD;
+  const bf16* Vc = reinterpret_cast<const bf16*>(a.vc) + s * a.seq_stride + h * FD_HD;
+
+  bf16x8 qf[NKS], df[NKS];
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((int64_t)s * M + (qvalid ? q : 0)) * a.ldq + h * FD_HD;
+    const bf16* drow = reinterpret_cast<const bf16*>(a.dout) + ((int64_t)s * M + (qvalid ? q : 0)) * a.lddo + h * FD_HD;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hl * 8) : bf16x8{};
+      df[ks] = qvalid ? *reinterpret_cast<const bf16x8*>(drow + ks * 16 + hl * 8) : bf16x8{};
+    }
+  }
+  const int64_t li = ((int64_t)s * a.H + h) * M + (qvalid ? q : 0);
+  const float lse2 = qvalid ? a.lse[li] * LOG2E : 0.f;
+  const float dlt = qvalid ? a.delta[li] : 0.f;
+
+  const int qlast_blk = min(qb0 + QB, M) - 1;
+  const int lo = max(0, pos0 + qb0 - win + 1);
+  const int hi = pos0 + qlast_blk;
+  int jb, je;
+  split_range(lo & ~(BKEY - 1), hi, nsplit, sp, &jb, &je);
+  const int nt = (je - jb) / BKEY;
+  const bool wactive = qw0 < M;
+  const int wfirst = pos0 + qw0;
+  const int wlast = pos0 + min(qw0 + WQ, M) - 1;
+  const float c2 = a.scale * LOG2E;
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+
+  uint32_t koff[4], voff[4];
+  fd_offsets<2>(a.ldk, w, lane, koff);
+  fd_offsets<0>(a.ldk, w, lane, voff);
+  const int r0 = jb % a.cap;
+  auto row = [&](int t) {
+    const int r = r0 + t * BKEY;
+    return (int64_t)(r >= a.cap ? r - a.cap : r) * a.ldk;
+  };
+  if (nt > 0) {
+    fd_issue(Kc + row(0), koff, sK[0], w);
+    fd_issue(Vc + row(0), voff, sV[0], w);
+  }
+  for (int t = 0; t < nt; ++t) {
+    // this wave's loads of tile t are the only ones in flight; after the
+    // barrier every wave's are in LDS and tile t-1 is no longer read
+    fd_wait_loads();
+    __syncthreads();
+    if (t + 1 < nt) {
+      fd_issue(Kc + row(t + 1), koff, sK[(t + 1) & 1], w);
+      fd_issue(Vc + row(t + 1), voff, sV[(t + 1) & 1], w);
+    }
+    const int j0 = jb + t * BKEY;
+    if (!wactive || j0 > wlast || j0 + BKEY - 1 <= wfirst - win) continue;
+    const bf16* cK = sK[t & 1];
+    const bf16* cV = sV[t & 1];
+    const bool full = (j0 + BKEY - 1 <= wfirst) && (j0 > wlast - win);
+    // the two 32-key halves one after the other (one half's S and dP live)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      f32x16 p = f32x16{}, dp = f32x16{};
+      // S and dP^T chains interleaved; the K / V fragments of step ks+1 are
+      // read while step ks multiplies
+      const int r = g * 32 + (lane & 31);
+      bf16x8 kf[2], vf[2];
+      kf[0] = fd_frag<2>(cK, r, hl);
+      vf[0] = fd_frag<0>(cV, r, hl);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) {
+          kf[(ks + 1) & 1] = fd_frag<2>(cK, r, (ks + 1) * 2 + hl);
+          vf[(ks + 1) & 1] = fd_frag<0>(cV, r, (ks + 1) * 2 + hl);
+        }
+        p = mfma(kf[ks & 1], qf[ks], p);
+        dp = mfma(vf[ks & 1], df[ks], dp);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[e] = ex2(fmaf(p[e], c2, -lse2));
+      if (!full) {
+        // a real branch (tiles crossing a window edge are few): the empty
+        // volatile asm keeps the compiler from turning it into selects
+        asm volatile("" ::: "memory");
+        // visible iff 0 <= pq - j < win
+        const int dj = pq - (j0 + g * 32 + hl * 4);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((unsigned)(dj - (e >> 2) * 8 - (e & 3)) >= (unsigned)win) p[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[e] *= dp[e] - dlt;  // dS
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 kt[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) kt[i] = fd_frag_tr<2>(cK, i * 32, g, u, lane);
+        const bf16x8 sf = acc_frag<bf16>(p, u);
+#pragma unroll
+        for (int i = 0; i < DB; ++i) dq[i] = mfma(kt[i], sf, dq[i]);
+      }
+    }
+  }
+  if (!wactive || !qvalid) return;
+  // split sp writes its own slice of dq (the slices are summed by the caller's pack)
+  float* out = a.dq + (int64_t)sp * a.B * M * a.lddq + ((int64_t)s * M + q) * a.lddq + h * FD_HD;
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[i * 32 + acc_row(e, hl)] = dq[i][e] * a.scale;
+}
+
 // ============================== backward: dK, dV ==============================
 
 constexpr int BQT = 64;  // query tile of the key-owned kernel
@@ -974,7 +1123,12 @@ template <typename T, int HD>
 hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
   const int ns = a.nsplit > 0 ? a.nsplit : 1;
   dim3 grid((a.M + QB - 1) / QB, a.H, a.B * ns);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
+      a.seq_stride % 8 == 0)
+    hipLaunchKernelGGL(attn_bwd_dq_dl_kernel, grid, dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid2((a.M + QB - 1) / QB, a.H, a.B);
