@@ -749,6 +749,28 @@ int k_splits(const GemmArgs& p, int batch, int64_t tiles, int64_t target, int64_
   return splits;
 }
 
+// K splits of the 256x256 direct-to-LDS kernel (one block per CU): with
+// fewer tiles than half the CUs, as many splits as fill the CUs in one round
+// (a second, partial round costs more than it spreads); otherwise only a long
+// K (over 128 K tiles), halved down to at most 128 K tiles per split.
+template <int BK>
+int dl_splits(const GemmArgs& p, int batch, int64_t tiles, int64_t slots, int64_t ws_elems) {
+  const auto al = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  if (!(p.N % 4 == 0 && p.ldc % 4 == 0 && p.sC % 4 == 0 && al(p.C) &&
+        (!p.R || (p.ldr % 4 == 0 && p.sR % 4 == 0 && al(p.R)))))
+    return 1;
+  const int nk = p.K / BK;
+  const auto fits = [&](int sp) { return (int64_t)sp * batch * p.M * p.N <= ws_elems && nk / sp >= 8; };
+  if (g_force_splits > 0) return fits(g_force_splits) ? g_force_splits : 1;
+  int sp = 1;
+  if (tiles < 128) {
+    while (sp < 8 && tiles * (sp + 1) <= slots && fits(sp + 1)) ++sp;
+  } else {
+    while (nk / sp > 128 && sp < 8 && fits(sp * 2)) sp *= 2;
+  }
+  return sp;
+}
+
 template <typename T, int EPI, typename OutT>
 hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipStream_t st) {
   // 256x256 tiles (8 waves, one block per CU) when they give >= 2 blocks per
@@ -793,7 +815,7 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
       return launch_dl<128, 128, 2, 2, 32, 4, EPI, OutT>(p, batch, sp, w, st);
     }
     if (EPI != EPI_SGD && ((cfg == 4 && p.K % 64 == 0) || (cfg == 5 && p.K % 32 == 0))) {
-      const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
+      const int sp = cfg == 4 ? dl_splits<64>(p, batch, t256, CUS, ws_elems) : k_splits<T>(p, batch, t256, CUS, ws_elems);
       float* w = sp > 1 ? ws : nullptr;
       if constexpr (EPI != EPI_SGD) {
         if (cfg == 4) return launch_dl<256, 256, 2, 4, 64, 2, EPI, OutT>(p, batch, sp, w, st);
