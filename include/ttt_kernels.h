@@ -74,7 +74,7 @@ int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc,
                    const void* dout, const float* delta, float* dq, float* dk, float* dv, int32_t B, int32_t M,
                    int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale, int32_t nsplit, void* stream);
 
-/* Test hook: 0 runs bf16 head-dim-128 forwards and dQ passes on the
+/* Test hook: 0 runs bf16 head-dim-128 attention (forward, dQ, dK/dV) on the
  * register-staged kernels (those of the other head dims), 1 (default) on the
  * direct-to-LDS ones. Process-wide. */
 void ttt_k_attn_fwd_kernel(int32_t dl);

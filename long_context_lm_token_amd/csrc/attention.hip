@@ -638,7 +638,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
 // One workgroup per row: the normalised weights of every (split, head) go to
 // LDS first, then each thread combines 4 consecutive columns.
 constexpr int COMBINE_MAX_H = 64;
-// test hook: 0 keeps bf16 head-dim-128 forwards and dQ on the register-staged kernels
+// test hook: 0 keeps bf16 head-dim-128 attention on the register-staged kernels
 int g_attn_dl = 1;
 template <typename T>
 __global__ void attn_combine_kernel(AttnArgs a) {
@@ -1104,6 +1104,200 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
 }
 
+// dK / dV kernel for bf16 with head dim 128: the computation of
+// attn_bwd_dkdv_kernel with eight waves per workgroup. Waves w and w+4 own
+// the same 32 keys (K, V fragments in registers) and take the two 32-query
+// halves of every 64-query tile, so two waves share each SIMD and each walks
+// half of the work; their partial dK, dV are summed through LDS at the end.
+// Q and dO tiles go straight into LDS (read both row-wise and transposed:
+// swizzle 2), the per-query statistics by 4-byte DMA; the mask is applied
+// only on tiles that cross the diagonal, the window edge or the last row.
+constexpr int DKDV_NT = 512;
+__global__ __launch_bounds__(DKDV_NT) void attn_bwd_dkdv_dl_kernel(AttnArgs a) {
+  constexpr int NKS = FD_HD / 16, DB = FD_HD / 32;
+  // Q tiles, then dO tiles (one array: the final exchange reuses all 64 KB)
+  __shared__ __attribute__((aligned(1024))) bf16 sQD[2][2][BQT * FD_HD];
+  __shared__ __attribute__((aligned(1024))) bf16 sVk[QB * FD_HD];  // this block's V rows
+  __shared__ __attribute__((aligned(16))) float sL[2][BQT], sDl[2][BQT];
+  bf16 (&sQ)[2][BQT * FD_HD] = sQD[0];
+  bf16 (&sD)[2][BQT * FD_HD] = sQD[1];
+
+  const Blk bk = blk();
+  const int s = bk.z, h = bk.y;
+  const int lane = threadIdx.x & 63, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int kq = w & 3, qg = w >> 2;  // key group, query half
+  const int M = a.M;
+  const int kb0 = bk.x * QB;
+  const int kw0 = kb0 + kq * WQ;
+  const int kr = kw0 + (lane & 31);  // key row within the chunk
+  const bool kvalid = kr < M;
+  const int pos0 = (int)a.pos0;
+  const int pk = pos0 + (kvalid ? kr : M - 1);
+  const int win = a.window;
+  const bf16* Kc = reinterpret_cast<const bf16*>(a.kc) + s * a.seq_stride + h * FD_HD;
+  const bf16* Vc = reinterpret_cast<const bf16*>(a.vc) + s * a.seq_stride + h * FD_HD;
+  const bf16* Q = reinterpret_cast<const bf16*>(a.q) + (int64_t)s * M * a.ldq + h * FD_HD;
+  const bf16* DO = reinterpret_cast<const bf16*>(a.dout) + (int64_t)s * M * a.lddo + h * FD_HD;
+  const float* LSE = a.lse + ((int64_t)s * a.H + h) * M;
+  const float* DLT = a.delta + ((int64_t)s * a.H + h) * M;
+
+  // K fragments in registers; the block's V rows (keys kb0 .., ring slots,
+  // past the last key the last one) in LDS, 4 one-KB loads per wave
+  bf16x8 kf[NKS];
+  {
+    const bf16* krow = Kc + (int64_t)(pk % a.cap) * a.ldk;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = kvalid ? *reinterpret_cast<const bf16x8*>(krow + ks * 16 + hl * 8) : bf16x8{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (w * 4 + i) * 4 + (lane >> 4);
+      const int64_t slot = (pos0 + min(kb0 + r, M - 1)) % a.cap;
+      __builtin_amdgcn_global_load_lds((const void*)(Vc + slot * a.ldk + ((lane & 15) ^ fd_swz<0>(r)) * 8),
+                                       (fd_lds_t*)(sVk + (w * 4 + i) * 512), 16, 0, 0);
+    }
+  }
+  const float c2 = a.scale * LOG2E;
+  const int klast_blk = min(kb0 + QB, M) - 1;
+  const bool wactive = kw0 < M;
+  const int wk_first = kw0, wk_last = min(kw0 + WQ, M) - 1;
+  // query tiles that can see keys of this block: [kb0, klast_blk + win - 1]
+  const int q_end = min(M, klast_blk + win);
+  const int q_start = kb0 & ~(BQT - 1);
+  const int nt = q_end > q_start ? (q_end - q_start + BQT - 1) / BQT : 0;
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+
+  // this wave's 2 of the 16 one-KB loads of a 64-row tile (rows past the
+  // last query read the last row: their weights are masked to 0); waves 0
+  // and 1 also bring the tile's 64 log-sum-exps / deltas (4 bytes a lane)
+  uint32_t qoff[2];
+  int qrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (w * 2 + i) * 4 + (lane >> 4);
+    qrow[i] = r;
+    qoff[i] = (uint32_t)(((lane & 15) ^ fd_swz<2>(r)) * 8);
+  }
+  auto issue = [&](int t) {
+    const int q0 = q_start + t * BQT, b = t & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t r = min(q0 + qrow[i], M - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(Q + r * a.ldq + qoff[i]), (fd_lds_t*)(sQ[b] + (w * 2 + i) * 512),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(DO + r * a.lddo + qoff[i]),
+                                       (fd_lds_t*)(sD[b] + (w * 2 + i) * 512), 16, 0, 0);
+    }
+    if (w < 2) {
+      const float* src = (w == 0 ? LSE : DLT) + min(q0 + lane, M - 1);
+      __builtin_amdgcn_global_load_lds((const void*)src, (fd_lds_t*)(w == 0 ? sL[b] : sDl[b]), 4, 0, 0);
+    }
+  };
+
+  if (nt > 0) issue(0);
+  for (int t = 0; t < nt; ++t) {
+    // this wave's loads of tile t are the only ones in flight; after the
+    // barrier every wave's are in LDS and tile t-1 is no longer read
+    fd_wait_loads();
+    __syncthreads();
+    if (t + 1 < nt) issue(t + 1);
+    const int qa = q_start + t * BQT + qg * WQ;  // this wave's 32 queries: qa ..
+    // does any (query, key) pair satisfy 0 <= q - k < win ?
+    if (!wactive || qa + WQ - 1 < wk_first || qa > wk_last + win - 1) continue;
+    const int b = t & 1;
+    const bf16* cQ = sQ[b];
+    const bf16* cD = sD[b];
+    f32x16 p = f32x16{}, dp = f32x16{};
+    const int row = qg * WQ + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      p = mfma(fd_frag<2>(cQ, row, ks * 2 + hl), kf[ks], p);
+      dp = mfma(fd_frag<2>(cD, row, ks * 2 + hl), fd_frag<0>(sVk, kq * WQ + (lane & 31), ks * 2 + hl), dp);
+      // fragments are read a couple of steps ahead, not all at once (with
+      // 160 registers of keys and accumulators held, more would spill)
+      if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    // rows of the accumulators are queries: acc_row(e, hl) = 8 (e/4) + 4 hl + e%4,
+    // so each group of 4 registers takes 4 consecutive statistics
+    const float* Lq = &sL[b][qg * WQ + hl * 4];
+    const float* Dq = &sDl[b][qg * WQ + hl * 4];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lq + k4 * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[k4 * 4 + e] = ex2(fmaf(p[k4 * 4 + e], c2, -l4[e] * LOG2E));
+    }
+    const bool full = qa - wk_last >= 0 && qa + WQ - 1 - wk_first < win && qa + WQ - 1 < M && wk_last == kw0 + WQ - 1;
+    if (!full) {
+      asm volatile("" ::: "memory");  // a real branch, not selects
+      // visible iff 0 <= q - k < win, the query row exists and the key does
+      const int dq0 = qa + hl * 4 - kr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int dqe = dq0 + (e >> 2) * 8 + (e & 3);
+        if ((unsigned)dqe >= (unsigned)win || qa + (e >> 2) * 8 + hl * 4 + (e & 3) >= M || !kvalid) p[e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dq + k4 * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[k4 * 4 + e] = p[k4 * 4 + e] * (dp[k4 * 4 + e] - d4[e]);  // dS
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 pf = acc_frag<bf16>(p, u), sf = acc_frag<bf16>(dp, u);
+#pragma unroll
+      for (int i = 0; i < DB; ++i) dv[i] = mfma(fd_frag_tr<2>(cD, i * 32, qg, u, lane), pf, dv[i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < DB; ++i) dk[i] = mfma(fd_frag_tr<2>(cQ, i * 32, qg, u, lane), sf, dk[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // sum the two query halves' partials: dK, then dV, through the ring's LDS
+  // (per key group 4 x 16 x 64 floats, lane-contiguous)
+  float* xch = reinterpret_cast<float*>(&sQD[0][0][0]);
+  float* xg = xch + kq * (DB * 16 * 64);
+  __syncthreads();
+  if (qg == 1) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xg[(i * 16 + e) * 64 + lane] = dk[i][e];
+  }
+  __syncthreads();
+  if (qg == 0) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dk[i][e] += xg[(i * 16 + e) * 64 + lane];
+  }
+  __syncthreads();
+  if (qg == 1) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xg[(i * 16 + e) * 64 + lane] = dv[i][e];
+  }
+  __syncthreads();
+  if (qg == 1 || !wactive || !kvalid) return;
+  float* dko = a.dk + ((int64_t)s * M + kr) * a.lddk + h * FD_HD;
+  float* dvo = a.dv + ((int64_t)s * M + kr) * a.lddk + h * FD_HD;
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int d = i * 32 + acc_row(e, hl);
+      dko[d] = dk[i][e] * a.scale;
+      dvo[d] = dv[i][e] + xg[(i * 16 + e) * 64 + lane];
+    }
+}
+
 template <typename T, int HD>
 hipError_t fwd_t(const AttnArgs& a, hipStream_t st) {
   const int ns = a.nsplit > 0 ? a.nsplit : 1;
@@ -1132,7 +1326,12 @@ hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid2((a.M + QB - 1) / QB, a.H, a.B);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid2, dim3(NT), 0, st, a);
+  const bool dl = sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && al16(a.q) &&
+                  al16(a.dout) && a.ldk % 8 == 0 && a.seq_stride % 8 == 0 && a.ldq % 8 == 0 && a.lddo % 8 == 0;
+  if (dl)
+    hipLaunchKernelGGL(attn_bwd_dkdv_dl_kernel, grid2, dim3(DKDV_NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid2, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
