@@ -803,7 +803,10 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
     if ((cfg == 6 || cfg == 7) && p.K % 64 == 0) {
       // 128x128, two blocks per CU: at least 3/4 of the 512 slots, and short K
       // ranges per split (long ones keep splitting while the blocks fit twice)
-      const int sp = k_splits<T>(p, batch, t128, cfg == 6 ? 3 * CUS / 2 : CUS, ws_elems, cfg == 6 ? 48 : 0);
+      // (a short K over >= 128 tiles gains nothing from a split and its reduce)
+      const int sp = cfg == 6 && t128 >= 128 && p.K <= 48 * 64
+                         ? 1
+                         : k_splits<T>(p, batch, t128, cfg == 6 ? 3 * CUS / 2 : CUS, ws_elems, cfg == 6 ? 48 : 0);
       float* w = sp > 1 ? ws : nullptr;
       if (cfg == 6) return launch_dl<128, 128, 2, 2, 64, 2, EPI, OutT>(p, batch, sp, w, st);
       return launch_dl<128, 128, 2, 2, 64, 3, EPI, OutT>(p, batch, sp, w, st);
