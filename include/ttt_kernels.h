@@ -52,6 +52,13 @@ int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N
  * the workspace is too small or K has fewer tiles). Process-wide. */
 void ttt_k_gemm_tile(int32_t cfg);
 
+/* Test hook: mn = 1 makes ttt_k_gemm read both operands MN-major, element
+ * (m, k) at A[k*lda + m] and (n, k) at B[k*ldb + n] (bf16, epi 0 or 2, M and
+ * N multiples of 128, K of 64, no split; the layout the weight-gradient
+ * products read their activations in). 0 restores K-contiguous operands.
+ * Process-wide. */
+void ttt_k_gemm_operands(int32_t mn);
+
 /* Sliding-window attention forward over a ring cache (query p sees keys
  * p-window < j <= p; technical review section 2.1 Eq. 1 and section 5).
  * q, o: [B*M][H*hd] rows (row s*M+i = position pos0+i of sequence s);

@@ -81,6 +81,8 @@ def load():
                                c_f32, ctypes.c_uint32, c_i32, c_vp, c_i64, c_vp]
     lib.ttt_k_gemm_tile.argtypes = [c_i32]
     lib.ttt_k_gemm_tile.restype = None
+    lib.ttt_k_gemm_operands.argtypes = [c_i32]
+    lib.ttt_k_gemm_operands.restype = None
     lib.ttt_k_attn_fwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_f32, c_i32, c_vp, c_vp]
     lib.ttt_k_attn_bwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,

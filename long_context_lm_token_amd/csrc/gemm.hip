@@ -464,8 +464,48 @@ TTT_DEV void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>
+// MN-major operands (128-wide tiles, 64 K rows): K row r of a tile keeps its
+// 16-byte chunk c at chunk c ^ 4 (r % 4), so the 4 rows x 2 chunks of a
+// 16-lane transposing read hit distinct banks
+TTT_DEV int mn_swz(int r) { return (r & 3) << 2; }
+
+// this wave's 4 of the 16 one-KB loads of the 64 x 128 tile (K rows k0..,
+// columns c0..c0+127)
+TTT_DEV void mn_issue(const bf16* __restrict__ base, int64_t ld, int c0, int k0, bf16* tile, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = w * 4 + i;
+    const int r = q * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ mn_swz(r);
+    const bf16* g = base + (int64_t)(k0 + r) * ld + c0 + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(tile + q * 512), 16, 0, 0);
+  }
+}
+
+// MFMA operand (32 rows d0.. on the lanes, K step ks of 16) of a [k][128]
+// tile, read with two transposing reads. The K order within the step is
+// permuted (k = 16 ks' + 8 (e / 4) + 4 (lane / 32) + e % 4 for element e);
+// both operands are read this way, so the products pair up unchanged.
+TTT_DEV bf16x8 mn_frag(const bf16* t, int d0, int ks, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_v4;
+  const int k = ks * 16 + (lane >> 5) * 4 + ((lane & 15) >> 2);
+  const int col = d0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  const int c = col >> 3;
+  const int o0 = k * 128 + ((c ^ mn_swz(k)) << 3) + (col & 7);
+  const int o1 = (k + 8) * 128 + ((c ^ mn_swz(k + 8)) << 3) + (col & 7);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + o0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(bf16*)(t + o1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT, bool MN = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int splits, float* part) {
+  static_assert(!MN || (BM == 128 && BN == 128 && BK == 64), "MN-major operands: 128 x 128 tiles, 64 deep");
   static_assert(EPI != EPI_SGD || BN * (BM + 8) <= S * (BM + BN) * BK, "the staged SGD tile must fit in the ring");
   static_assert(S >= 2 && S <= 4, "ring depth");
   constexpr int NW = WGM * WGN;
@@ -494,8 +534,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
   auto issue = [&](int kt, int st) {
-    dl_issue<BM, NW, BK>(A, p.lda, m0, p.M, kt * BK, smem[st], w, lane);
-    dl_issue<BN, NW, BK>(B, p.ldb, n0, p.N, kt * BK, smem[st] + BM * BK, w, lane);
+    if constexpr (MN) {
+      mn_issue(A, p.lda, m0, kt * BK, smem[st], w, lane);
+      mn_issue(B, p.ldb, n0, kt * BK, smem[st] + BM * BK, w, lane);
+    } else {
+      dl_issue<BM, NW, BK>(A, p.lda, m0, p.M, kt * BK, smem[st], w, lane);
+      dl_issue<BN, NW, BK>(B, p.ldb, n0, p.N, kt * BK, smem[st] + BM * BK, w, lane);
+    }
   };
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
@@ -513,17 +558,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int
     // a plain barrier: a fenced one would also drain the younger tiles' loads
     asm volatile("s_barrier" ::: "memory");
     if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
-    const bf16* sa = smem[it % S] + wm * WTM * BK;
-    const bf16* sb = smem[it % S] + BM * BK + wn * WTN * BK;
+    const bf16* sa = smem[it % S] + (MN ? 0 : wm * WTM * BK);
+    const bf16* sb = smem[it % S] + BM * BK + (MN ? 0 : wn * WTN * BK);
     // fragments double-buffered in registers: step ks+1 is read from LDS
     // while the MFMAs of step ks run
     bf16x8 fa[2][TI], fb[2][TJ];
     auto read = [&](int ks, int b) {
-      const int c = ks * 2 + (lane >> 5);
+      if constexpr (MN) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i) fa[b][i] = dl_frag<BK>(sa, i * 32 + (lane & 31), c);
+        for (int i = 0; i < TI; ++i) fa[b][i] = mn_frag(sa, wm * WTM + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) fb[b][j] = dl_frag<BK>(sb, j * 32 + (lane & 31), c);
+        for (int j = 0; j < TJ; ++j) fb[b][j] = mn_frag(sb, wn * WTN + j * 32, ks, lane);
+      } else {
+        const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) fa[b][i] = dl_frag<BK>(sa, i * 32 + (lane & 31), c);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) fb[b][j] = dl_frag<BK>(sb, j * 32 + (lane & 31), c);
+      }
     };
     read(0, 0);
 #pragma unroll
@@ -535,17 +587,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
     }
     // schedule: the first step's reads, then each step's MFMAs alternate with
-    // the next step's reads (mask 0x8 = MFMA, 0x100 = LDS read)
-    __builtin_amdgcn_sched_group_barrier(0x100, TI + TJ, 0);
+    // the next step's reads (mask 0x8 = MFMA, 0x100 = LDS read); MN-major
+    // fragments take two reads each
+    constexpr int RD = (MN ? 2 : 1) * (TI + TJ);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) {
+        if constexpr (MN) {
 #pragma unroll
-        for (int q = 0; q < TI + TJ; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int q = 0; q < TI * TJ; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, (RD + TI * TJ - 1) / (TI * TJ), 0);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < TI + TJ; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ - (TI + TJ), 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ - (TI + TJ), 0);
       } else {
         __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ, 0);
       }
@@ -704,15 +766,15 @@ hipError_t launch_gemv(const GemmArgs& p, int batch, hipStream_t st) {
 int g_force_tile = 0;
 int g_force_splits = 0;
 
-template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT>
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT, bool MN = false>
 hipError_t launch_dl(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dl_kernel<BM, BN, WGM, WGN, BK, S, EPI, OutT>), dim3(tiles, splits, batch),
+  hipLaunchKernelGGL((gemm_dl_kernel<BM, BN, WGM, WGN, BK, S, EPI, OutT, MN>), dim3(tiles, splits, batch),
                      dim3(WGM * WGN * 64), 0, st, p, splits, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  const int64_t MN = (int64_t)p.M * p.N;
-  int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
+  const int64_t elems = (int64_t)p.M * p.N;
+  int blocks = (int)std::min<int64_t>((elems + 255) / 256, 4096);
   hipLaunchKernelGGL((gemm_reduce<bf16, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
   return hipGetLastError();
 }
@@ -782,6 +844,16 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   const int64_t t2x1 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128) * batch;
   const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
   if (!ws) ws_elems = 0;
+  if constexpr (sizeof(T) == 2 && (EPI == EPI_SGD || EPI == EPI_STORE)) {
+    if (p.mn) {
+      const auto al = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+      if (p.M % 128 || p.N % 128 || p.K % 64 || p.lda % 8 || p.ldb % 8 || p.sA % 8 || p.sB % 8 || !al(p.A) ||
+          !al(p.B))
+        return hipErrorInvalidValue;
+      return launch_dl<128, 128, 2, 2, 64, 2, EPI, OutT, true>(p, batch, 1, nullptr, st);
+    }
+  }
+  if (p.mn) return hipErrorInvalidValue;
   int cfg = g_force_tile;
   if constexpr (sizeof(T) == 2 && EPI != EPI_SGD) {
     // a few rows of A (decode): one streaming pass over B

@@ -11,6 +11,7 @@
 
 namespace {
 thread_local std::string k_err;
+int g_gemm_mn = 0;  // test hook: operands of ttt_k_gemm stored MN-major
 int kfail(int code, const char* msg) {
   k_err = msg;
   return code;
@@ -42,10 +43,13 @@ int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N
   g.C2 = C2; g.ldc2 = ldc2; g.sC2 = sC2;
   g.M = M; g.N = N; g.K = K; g.R = R; g.ldr = ldr; g.sR = sR; g.Wm = Wm; g.ldw = ldw; g.sW = sW; g.lr = lr;
   g.sr_seed = sr_seed;
+  g.mn = g_gemm_mn;
   return kdone(gemm_launch(g, dtype, epi, out_f32 != 0, batch, ws, ws_elems, static_cast<hipStream_t>(stream)));
 }
 
 void ttt_k_gemm_tile(int32_t cfg) { gemm_force_tile(cfg); }
+
+void ttt_k_gemm_operands(int32_t mn) { g_gemm_mn = mn != 0; }
 
 static AttnArgs mk(const void* q, const void* kc, const void* vc, int32_t cap, int32_t B, int32_t M, int32_t H,
                    int32_t hd, int64_t pos0, int32_t window, float scale) {

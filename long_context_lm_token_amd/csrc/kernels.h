@@ -28,6 +28,9 @@ struct GemmArgs {
   // stochastically from the fp32 master with a counter-based hash of
   // (sr_seed, batch, row, col); 0 = round to nearest even
   uint32_t sr_seed;
+  // bf16 only: A and B stored MN-major, element (m, k) at A[k * lda + m] and
+  // (n, k) at B[k * ldb + n] (M, N multiples of 128, K of 64; no split)
+  int mn;
 };
 
 // ws: fp32 split-K workspace of ws_elems elements (may be null: no split)

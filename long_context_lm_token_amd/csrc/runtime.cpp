@@ -108,9 +108,17 @@ struct ttt_model {
   float* tQKV = nullptr;
   float *dres = nullptr, *dn = nullptr, *dA = nullptr, *delta = nullptr, *dq = nullptr, *dk = nullptr,
         *dv = nullptr;
-  void *dres_c = nullptr, *dZ = nullptr, *dO = nullptr, *dqkv = nullptr;
+  void *dres_c = nullptr, *dO = nullptr, *dqkv = nullptr;
+  // per tail block: the bf16 gradient at its MLP output and the activation
+  // gradient dZ, which the side stream's weight-gradient products read while
+  // the chunk loop moves on to the blocks below
+  std::vector<void*> dres_b, dZ_b;
+  // the weight-gradient products read their operands MN-major (bf16 with
+  // d and the trainable width multiples of 128, b of 64); otherwise from the
+  // token-contiguous copies below
+  bool mn_dw = false;
   // token-contiguous operands of the weight-gradient GEMMs, per tail block: [B][cols][b]
-  std::vector<void*> Tdres, Ta, Tdz, Tn;
+  std::vector<void*> Tdres, Ta, Tdz, Tn;  // token-contiguous copies (when !mn_dw)
   // the weight-gradient + SGD GEMMs run on a second stream (default priority),
   // ordered after the input-gradient GEMMs that read W_c; joined per chunk
   hipStream_t side = nullptr;
@@ -367,54 +375,74 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
   if (!bwd) return;
 
   // ---------------- backward ----------------
-  // every product below reads both operands K-contiguous: input grads use the
-  // [in][out] copies of the weights, weight grads use token-contiguous
-  // (transposed) copies of the activations and output gradients
+  // every product below reads both operands K-contiguous, except the weight
+  // gradients: input grads use the [in][out] copies of the weights; weight
+  // grads read the activations and output gradients token-major (MN-major
+  // operands), or token-contiguous copies of them
   c.gemm(EPI_STORE, true, ga(m->tdz, V, m->wout_b, V, m->dn, d, R, d, V));
-  c.chk(rmsnorm_bwd_launch(m->txL, m->trf, m->gfin, m->dn, R, d, m->dres, m->dres_c, false, m->dt, c.st),
+  c.chk(rmsnorm_bwd_launch(m->txL, m->trf, m->gfin, m->dn, R, d, m->dres, m->dres_b[m->nt - 1], false, m->dt,
+                           c.st),
         "norm_bwd");
-  const bool master = m->dt == 1;
+  const bool master = m->dt == 1, mnw = m->mn_dw;
   const int64_t sbgu = (int64_t)d * zw, sbd = (int64_t)hf * d;  // per-seq strides of the [in][out] copies
   for (int j = m->nt - 1; j >= 0; --j) {
     const int l = m->t0 + j;
     const int hcols = j == 0 ? ht : hf;
+    void* drc = m->dres_b[j];  // gradient at this block's MLP output (compute dtype)
+    void* dz = m->dZ_b[j];
     // dA = dres . W_down^T  (reads W_c before its update below)
-    GemmArgs g = ga(m->dres_c, d, m->fb_d[j], d, m->dA, hf, M, hcols, d);
+    GemmArgs g = ga(drc, d, m->fb_d[j], d, m->dA, hf, M, hcols, d);
     g.sA = (int64_t)M * d; g.sB = sbd; g.sC = (int64_t)M * hf;
     c.gemm(EPI_STORE, true, g, B);
     // W_down trainable columns: W^T[d][ht] -= eta * dres^T . A_t  (side stream,
     // after the dA GEMM above has read W_c)
-    c.transpose(m->dres_c, M, d, d, m->Tdres[j], M, B, (int64_t)M * d, (int64_t)d * M);
-    c.transpose(m->ta[j], M, ht, hf, m->Ta[j], M, B, (int64_t)M * hf, (int64_t)ht * M);
-    c.order(c.st, m->side, m->ev[2 * j]);
-    g = ga(m->Tdres[j], M, m->Ta[j], M, master ? m->f_d[j] : nullptr, hf, d, ht, M);
-    g.sA = (int64_t)d * M; g.sB = (int64_t)ht * M; g.sC = sd;
+    if (mnw) {
+      c.order(c.st, m->side, m->ev[2 * j]);
+      g = ga(drc, d, m->ta[j], hf, master ? m->f_d[j] : nullptr, hf, d, ht, M);
+      g.sA = (int64_t)M * d; g.sB = (int64_t)M * hf; g.mn = 1;
+    } else {
+      c.transpose(drc, M, d, d, m->Tdres[j], M, B, (int64_t)M * d, (int64_t)d * M);
+      c.transpose(m->ta[j], M, ht, hf, m->Ta[j], M, B, (int64_t)M * hf, (int64_t)ht * M);
+      c.order(c.st, m->side, m->ev[2 * j]);
+      g = ga(m->Tdres[j], M, m->Ta[j], M, master ? m->f_d[j] : nullptr, hf, d, ht, M);
+      g.sA = (int64_t)d * M; g.sB = (int64_t)ht * M;
+    }
+    g.sC = sd;
     g.Wm = master ? m->m_d[j] : static_cast<float*>(m->f_d[j]);
     g.ldw = master ? ht : hf; g.sW = master ? smd : sd;
     g.C2 = m->fb_d[j]; g.ldc2 = d; g.sC2 = sbd;
     g.lr = m->cfg.lr;
     g.sr_seed = sr_seed(P0 / m->cfg.mini_batch, j, 2);
     c.gemm(EPI_SGD, false, g, B, m->side);
-    c.chk(act_bwd_launch(m->tz[j], m->dA, R, hcols, zw, hf, hf, mg == 2, m->dZ, zw, m->dt, c.st), "act_bwd");
+    c.chk(act_bwd_launch(m->tz[j], m->dA, R, hcols, zw, hf, hf, mg == 2, dz, zw, m->dt, c.st), "act_bwd");
     if (j >= 1) {
       // dn = dZ . W_gu^T (reads W_c before its update below)
-      g = ga(m->dZ, zw, m->fb_gu[j], zw, m->dn, d, M, d, zw);
+      g = ga(dz, zw, m->fb_gu[j], zw, m->dn, d, M, d, zw);
       g.sA = (int64_t)M * zw; g.sB = sbgu; g.sC = (int64_t)M * d;
       c.gemm(EPI_STORE, true, g, B);
     }
     // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ_t^T . n  (side stream)
-    c.transpose(m->tn[j], M, d, d, m->Tn[j], M, B, (int64_t)M * d, (int64_t)d * M);
-    for (int part = 0; part < mg; ++part) {
-      void* tdz = off(m->Tdz[j], (int64_t)part * B * ht * M, es);
-      c.transpose(off(m->dZ, (int64_t)part * hf, es), M, ht, zw, tdz, M, B, (int64_t)M * zw, (int64_t)ht * M);
+    if (!mnw) {
+      c.transpose(m->tn[j], M, d, d, m->Tn[j], M, B, (int64_t)M * d, (int64_t)d * M);
+      for (int part = 0; part < mg; ++part) {
+        void* tdz = off(m->Tdz[j], (int64_t)part * B * ht * M, es);
+        c.transpose(off(dz, (int64_t)part * hf, es), M, ht, zw, tdz, M, B, (int64_t)M * zw, (int64_t)ht * M);
+      }
     }
     c.order(c.st, m->side, m->ev[2 * j + 1]);
     for (int part = 0; part < mg; ++part) {
       const int64_t zoff = (int64_t)part * hf;      // column of dZ / row of the forward copy
       const int64_t moff = (int64_t)part * ht * d;  // row block of the master
-      void* tdz = off(m->Tdz[j], (int64_t)part * B * ht * M, es);
-      g = ga(tdz, M, m->Tn[j], M, master ? off(m->f_gu[j], zoff * d, es) : nullptr, d, ht, d, M);
-      g.sA = (int64_t)ht * M; g.sB = (int64_t)d * M; g.sC = sgu;
+      void* fcopy = master ? off(m->f_gu[j], zoff * d, es) : nullptr;
+      if (mnw) {
+        g = ga(off(dz, zoff, es), zw, m->tn[j], d, fcopy, d, ht, d, M);
+        g.sA = (int64_t)M * zw; g.sB = (int64_t)M * d; g.mn = 1;
+      } else {
+        void* tdz = off(m->Tdz[j], (int64_t)part * B * ht * M, es);
+        g = ga(tdz, M, m->Tn[j], M, fcopy, d, ht, d, M);
+        g.sA = (int64_t)ht * M; g.sB = (int64_t)d * M;
+      }
+      g.sC = sgu;
       g.Wm = master ? m->m_gu[j] + moff : reinterpret_cast<float*>(off(m->f_gu[j], zoff * d, es));
       g.ldw = d; g.sW = master ? smgu : sgu;
       g.C2 = off(m->fb_gu[j], zoff, es); g.ldc2 = zw; g.sC2 = sbgu;
@@ -451,7 +479,8 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
                                m->cfg.rope ? m->rope : nullptr, m->dqkv, m->dt, c.st),
           "rope_bwd");
     c.gemm(EPI_STORE, true, ga(m->dqkv, 3 * HD, m->wqkv_b[l], 3 * HD, m->dn, d, R, d, 3 * HD));
-    c.chk(rmsnorm_bwd_launch(m->tx[j], m->tr1[j], m->g_attn[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
+    // the gradient at block j's input is the one at block j-1's MLP output
+    c.chk(rmsnorm_bwd_launch(m->tx[j], m->tr1[j], m->g_attn[l], m->dn, R, d, m->dres, m->dres_b[j - 1], true, m->dt,
                              c.st),
           "norm_bwd");
   }
@@ -690,10 +719,15 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   m->spart_o = A.f32(ttt_model::kMaxSplit * Rt * HD);
   m->spart_m = A.f32(ttt_model::kMaxSplit * Rt * m->H);
   m->spart_l = A.f32(ttt_model::kMaxSplit * Rt * m->H);
-  m->dres_c = A.el(Rt * d); m->dZ = A.el(Rt * mg * hf); m->dO = A.el(Rt * HD); m->dqkv = A.el(Rt * 3 * HD);
-  m->Tdres.resize(nt); m->Ta.resize(nt); m->Tdz.resize(nt); m->Tn.resize(nt);
+  m->dres_c = A.el(Rt * d); m->dO = A.el(Rt * HD); m->dqkv = A.el(Rt * 3 * HD);
+  m->mn_dw = m->dt == 1 && d % 128 == 0 && ht % 128 == 0 && m->cfg.mini_batch % 64 == 0 && hf % 8 == 0;
+  m->dres_b.resize(nt); m->dZ_b.resize(nt);
+  if (!m->mn_dw) { m->Tdres.resize(nt); m->Ta.resize(nt); m->Tdz.resize(nt); m->Tn.resize(nt); }
   for (int j = 0; j < nt; ++j) {
-    m->Tdres[j] = A.el(Rt * d); m->Ta[j] = A.el(Rt * ht); m->Tdz[j] = A.el(Rt * mg * ht); m->Tn[j] = A.el(Rt * d);
+    m->dres_b[j] = A.el(Rt * d); m->dZ_b[j] = A.el(Rt * mg * hf);
+    if (!m->mn_dw) {
+      m->Tdres[j] = A.el(Rt * d); m->Ta[j] = A.el(Rt * ht); m->Tdz[j] = A.el(Rt * mg * ht); m->Tn[j] = A.el(Rt * d);
+    }
   }
   m->ws_elems = std::min<int64_t>((int64_t)1 << 26, 8 * Rt * std::max({d, 3 * HD, hf}));
   m->ws = A.f32(m->ws_elems);

@@ -167,6 +167,59 @@ def test_gemm_sgd_epilogue(dtype, tile, ws, sr_seed):
         assert abs(err.mean()) < 0.05 * np.abs(err).mean()
 
 
+@pytest.mark.parametrize("epi,out_f32,sr_seed", [(0, True, 0), (0, False, 0), (2, False, 0), (2, False, 5)])
+@pytest.mark.parametrize("shape,batch", [((128, 128, 64), 2), ((256, 384, 192), 2), ((4096, 3072, 1024), 1)])
+def test_gemm_mn_major_operands(epi, out_f32, sr_seed, shape, batch):
+    """Both operands stored MN-major (as the weight-gradient products read
+    their activations): C = A^T-layout . B^T-layout, plain store and the SGD
+    epilogue, against fp64."""
+    lib = bd.load()
+    M, N, K = shape
+    At, Atd = rnd((batch, K, M), 1, torch.bfloat16)
+    Bt, Btd = rnd((batch, K, N), 2, torch.bfloat16)
+    z = np.einsum("zkm,zkn->zmn", At, Bt)
+    lr = 0.37
+    C = torch.zeros((batch, M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    C2 = Wd = None
+    if epi == 2:
+        Wm, Wd = rnd((batch, M, N), 4, torch.float32)
+        ref = Wm - lr * z
+        C2 = torch.zeros((batch, N, M), dtype=torch.bfloat16, device="cuda")
+    else:
+        ref = z
+    lib.ttt_k_gemm_operands(1)
+    try:
+        bd.check(lib.ttt_k_gemm(1, epi, int(out_f32), M, N, K, bd.ptr(Atd), M, K * M, bd.ptr(Btd), N, K * N,
+                                bd.ptr(C), N, M * N, bd.ptr(C2), M, M * N, None, 0, 0, bd.ptr(Wd), N, M * N,
+                                lr, sr_seed, batch, None, 0, bd.stream_ptr()), kernel=True)
+        sync()
+    finally:
+        lib.ttt_k_gemm_operands(0)
+    got = C.float().cpu().numpy()
+    if epi == 2:
+        got_w = Wd.cpu().numpy()
+        np.testing.assert_allclose(got_w, ref, rtol=1e-5, atol=1e-4)
+        np.testing.assert_array_equal(C2.float().cpu().numpy(), got.transpose(0, 2, 1))
+        np.testing.assert_allclose(got, got_w, rtol=2 ** -7 if sr_seed else 2 ** -8, atol=0)
+    else:
+        scale = max(np.abs(ref).max(), 1.0)
+        tol = (4e-5 * math.sqrt(K) if out_f32 else 2 ** -7) * scale
+        assert np.abs(got - ref).max() <= tol
+
+
+def test_gemm_mn_major_rejects_ragged_shapes():
+    lib = bd.load()
+    A = torch.zeros(64 * 200, dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros(200 * 128, dtype=torch.float32, device="cuda")
+    lib.ttt_k_gemm_operands(1)
+    try:
+        rc = lib.ttt_k_gemm(1, 0, 1, 200, 128, 64, bd.ptr(A), 200, 0, bd.ptr(A), 128, 0, bd.ptr(C), 128, 0, None, 0,
+                            0, None, 0, 0, None, 0, 0, 0.0, 0, 1, None, 0, bd.stream_ptr())
+    finally:
+        lib.ttt_k_gemm_operands(0)
+    assert rc != 0
+
+
 def _silu(x):
     return x / (1.0 + np.exp(-x))
 

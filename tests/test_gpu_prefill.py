@@ -128,6 +128,19 @@ def test_bf16_small_model():
     model.close()
 
 
+def test_bf16_two_sequences_head_dim_128():
+    """bf16 with head dim 128 (the direct-to-LDS attention kernels) and two
+    sequences (per-sequence strides of every product, incl. the weight
+    gradients read MN-major), several chunks, against the oracle."""
+    cfg = small_cfg(dtype="bf16", vocab=512, d_model=256, n_heads=2, head_dim=128, mlp_hidden=512,
+                    ttt_hidden=256, static_hidden=256, n_blocks=4, n_ttt_blocks=2, window=128,
+                    mini_batch=64, lr=0.05, span=32, period=256)
+    model, wn, g, o, ors, _ = run_prefill(cfg, 4 * 64 + 5, batch=2, std=0.05)
+    check_losses(g, o, BF16_TOL["loss"])
+    compare_weights(cfg, model, ors, wn, BF16_TOL["w"], BF16_TOL["dw"])
+    model.close()
+
+
 def test_forward_only_is_the_static_model():
     """forward_only: every position scored at W_init in one causal pass (the
     oracle's static losses; with a window as long as the stream, full causal
