@@ -533,13 +533,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
+  // each tile walks its K range from its own starting point ((tm + tn) mod
+  // the range): tiles that share an operand panel then ask for a given K
+  // slice an iteration or more apart, so one takes the miss beyond L2 and the
+  // others find the slice in L2, instead of all waiting on the same miss
+  const int nkt = kt1 - kt0;
+  const int rot = nkt > 0 ? (tm + tn) % nkt : 0;
   auto issue = [&](int kt, int st) {
+    int kp = kt - kt0 + rot;
+    kp = kt0 + (kp >= nkt ? kp - nkt : kp);
     if constexpr (MN) {
-      mn_issue(A, p.lda, m0, kt * BK, smem[st], w, lane);
-      mn_issue(B, p.ldb, n0, kt * BK, smem[st] + BM * BK, w, lane);
+      mn_issue(A, p.lda, m0, kp * BK, smem[st], w, lane);
+      mn_issue(B, p.ldb, n0, kp * BK, smem[st] + BM * BK, w, lane);
     } else {
-      dl_issue<BM, NW, BK>(A, p.lda, m0, p.M, kt * BK, smem[st], w, lane);
-      dl_issue<BN, NW, BK>(B, p.ldb, n0, p.N, kt * BK, smem[st] + BM * BK, w, lane);
+      dl_issue<BM, NW, BK>(A, p.lda, m0, p.M, kp * BK, smem[st], w, lane);
+      dl_issue<BN, NW, BK>(B, p.ldb, n0, p.N, kp * BK, smem[st] + BM * BK, w, lane);
     }
   };
 #pragma unroll
