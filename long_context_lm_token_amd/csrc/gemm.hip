@@ -139,6 +139,7 @@ TTT_DEV int gate_col(int u) { return (u >> 5) * 64 + (u & 31); }
 // Apply the epilogue to one element (row, col) of batch z (not EPI_SWIGLU).
 template <int EPI, typename OutT, typename T>
 TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
+  static_assert(EPI != EPI_ROPE, "the rotary epilogue needs column pairs");
   if constexpr (EPI == EPI_GELU) {
     OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
     C[(int64_t)row * p.ldc + col] = from_f32<OutT>(gelu_acc(v));
@@ -162,6 +163,7 @@ TTT_DEV void apply(const GemmArgs& p, int z, int row, int col, float v) {
 // Epilogue store when the operand (residual / master value) is already loaded.
 template <int EPI, typename OutT, typename T>
 TTT_DEV void store_out(const GemmArgs& p, int z, int row, int col, float v, float in) {
+  static_assert(EPI != EPI_ROPE, "the rotary epilogue needs column pairs");
   if constexpr (EPI == EPI_GELU) {
     reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)row * p.ldc + col] = from_f32<OutT>(gelu_acc(v));
   } else if constexpr (EPI == EPI_STORE) {
@@ -269,7 +271,62 @@ TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, 
       }
     return;
   }
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_ROPE) {
+    // acc[i][2jj] holds dims e = 32 sb + u of a head part, acc[i][2jj+1] their
+    // rotation partners e + hd/2
+    static_assert(TJ % 2 == 0, "the rotary epilogue pairs 32-column blocks");
+    const RopeOut& ro = p.rope;
+    const int hd = ro.hd, half = hd / 2, HDm = ro.H * hd;
+    // with S % 32 == 0 a 32-row block is one run of positions of one
+    // sequence (its position and ring slot follow from its first row);
+    // otherwise (the few rows that end a stream) every row is placed itself
+    const int S = ro.S, cap = ro.cap;
+    const bool runs = S % 32 == 0;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int rb = m0 + wm * WTM + i * 32;  // first row of this 32-row block
+      const int sq0 = rb / S;
+      const int pos0 = (int)ro.p0 + rb % S;   // positions fit in 31 bits
+      const int slot0 = pos0 % cap;
+#pragma unroll
+      for (int jj = 0; jj < TJ / 2; ++jj) {
+        const int cb = n0 + wn * WTN + jj * 64;  // multiple of 64
+        if (CHECK && cb >= p.N) continue;
+        const int hp = cb / hd, part = hp / ro.H, h = hp % ro.H;
+        const int e1 = ((cb % hd) / 64) * 32 + (lane & 31);
+        OutT* const qb = reinterpret_cast<OutT*>(ro.q) + h * hd + e1;
+        OutT* const cb_ = reinterpret_cast<OutT*>(part == 1 ? ro.kc : ro.vc) + h * hd + e1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row within the block
+          const int row = rb + rr;
+          if (CHECK && row >= p.M) continue;
+          int pos, slot, sq;
+          if (runs) {
+            pos = pos0 + rr;
+            slot = slot0 + rr;
+            if (slot >= cap) slot -= cap;
+            sq = sq0;
+          } else {
+            sq = row / S;
+            pos = (int)ro.p0 + row % S;
+            slot = pos % cap;
+          }
+          float y1 = acc[i][2 * jj][r], y2 = acc[i][2 * jj + 1][r];
+          if (part < 2 && ro.tab) {
+            const float2 cs = ro.tab[(int64_t)pos * half + e1];
+            const float a = y1, b = y2;
+            y1 = a * cs.x - b * cs.y;
+            y2 = a * cs.y + b * cs.x;
+          }
+          OutT* dst = part == 0 ? qb + (int64_t)row * ro.ldq : cb_ + sq * ro.seq_stride + (int64_t)slot * HDm;
+          dst[0] = from_f32<OutT>(y1);
+          dst[half] = from_f32<OutT>(y2);
+        }
+      }
+    }
+    return;
+  } else if constexpr (EPI == EPI_SWIGLU) {
     // acc[i][2jj] holds gate columns and acc[i][2jj+1] the matching up columns
     static_assert(TJ % 2 == 0, "SwiGLU epilogue pairs 32-column blocks");
     OutT* C = reinterpret_cast<OutT*>(p.C) + z * p.sC;
@@ -781,6 +838,7 @@ hipError_t launch_dl(const GemmArgs& p, int batch, int splits, float* ws, hipStr
                      dim3(WGM * WGN * 64), 0, st, p, splits, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
+  if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
   const int64_t elems = (int64_t)p.M * p.N;
   int blocks = (int)std::min<int64_t>((elems + 255) / 256, 4096);
   hipLaunchKernelGGL((gemm_reduce<bf16, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
@@ -794,6 +852,7 @@ hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStre
                      dim3(WGM * WGN * 64), 0, st, p, splits, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
+  if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
   const int64_t MN = (int64_t)p.M * p.N;
   int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
   hipLaunchKernelGGL((gemm_reduce<T, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
@@ -863,7 +922,7 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   }
   if (p.mn) return hipErrorInvalidValue;
   int cfg = g_force_tile;
-  if constexpr (sizeof(T) == 2 && EPI != EPI_SGD) {
+  if constexpr (sizeof(T) == 2 && EPI != EPI_SGD && EPI != EPI_ROPE) {
     // a few rows of A (decode): one streaming pass over B
     if (!cfg && p.M <= GV_MAXM) return launch_gemv<EPI, OutT>(p, batch, st);
   }
@@ -930,6 +989,7 @@ hipError_t dispatch(const GemmArgs& p, int epi, bool out_f32, int batch, float* 
   if (epi == EPI_GELU)
     return out_f32 ? pick<T, EPI_GELU, float>(p, batch, ws, ws_elems, st)
                    : pick<T, EPI_GELU, T>(p, batch, ws, ws_elems, st);
+  if (epi == EPI_ROPE) return pick<T, EPI_ROPE, T>(p, batch, nullptr, 0, st);  // never split
   return hipErrorInvalidValue;
 }
 
@@ -945,6 +1005,12 @@ hipError_t gemm_launch(const GemmArgs& p, int dtype, int epi, bool out_f32, int 
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
   if (p.K % (dtype == 1 ? 8 : 4)) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU && p.N % 64) return hipErrorInvalidValue;
+  if (epi == EPI_ROPE) {
+    const RopeOut& r = p.rope;
+    if (batch != 1 || r.hd % 64 || r.H < 1 || p.N != 3 * r.H * r.hd || r.S < 1 || r.cap < 32 || !r.q || !r.kc ||
+        !r.vc || r.ldq < r.H * r.hd || p.M % r.S || r.p0 < 0 || r.p0 + r.S > ((int64_t)1 << 31))
+      return hipErrorInvalidValue;
+  }
   if (dtype == 1) return dispatch<bf16>(p, epi, out_f32, batch, ws, ws_elems, st);
   return dispatch<float>(p, epi, out_f32, batch, ws, ws_elems, st);
 }

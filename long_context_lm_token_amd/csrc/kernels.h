@@ -7,7 +7,26 @@
 // EPI_SWIGLU: B's rows (output columns) come in blocks of 32 gate / 32 up
 // columns; C[m][u] = silu(gate_u) * up_u for hidden unit u, C has N/2 columns.
 // EPI_GELU: C = gelu(acc).
-enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SGD = 2, EPI_SWIGLU = 3, EPI_GELU = 4 };
+// EPI_ROPE: the attention's Q/K/V projection with the rotary embedding and
+// the split applied to the fp32 accumulators (GemmArgs::rope). B's rows (the
+// output columns) are the q, k, v parts of each head, each permuted in
+// 32-row blocks so that every 64-column block holds dims 32s.. 32s+31 and
+// then their rotation partners hd/2 + 32s..: with nb = hd/32 blocks, block
+// order [0, nb/2, 1, nb/2 + 1, ...] (hd a multiple of 64). Outputs in the
+// compute dtype: q [rows][H*hd], k and v into ring caches at slot pos % cap.
+// Never split over K.
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SGD = 2, EPI_SWIGLU = 3, EPI_GELU = 4, EPI_ROPE = 5 };
+
+// outputs of EPI_ROPE: row s*S + i of the product is position p0 + i of
+// sequence s; tab: [pos][hd/2] (cos, sin), or null for no rotation
+struct RopeOut {
+  void* q;
+  void* kc;
+  void* vc;
+  const float2* tab;
+  int64_t ldq, seq_stride, p0;
+  int cap, S, H, hd;
+};
 
 // C[m][n] (epilogue)= sum_k A[m*lda + k] * B[n*ldb + k], batched over z.
 struct GemmArgs {
@@ -28,6 +47,7 @@ struct GemmArgs {
   // stochastically from the fp32 master with a counter-based hash of
   // (sr_seed, batch, row, col); 0 = round to nearest even
   uint32_t sr_seed;
+  RopeOut rope;  // EPI_ROPE
   // bf16 only: A and B stored MN-major, element (m, k) at A[k * lda + m] and
   // (n, k) at B[k * ldb + n] (M, N multiples of 128, K of 64; no split)
   int mn;

@@ -98,6 +98,10 @@ struct ttt_model {
   float *sX = nullptr, *sR = nullptr, *sL = nullptr;
   void *sU = nullptr, *sQ = nullptr, *sO = nullptr, *sA = nullptr;
   float* sQKV = nullptr;
+  // bf16 with hd % 64 == 0: the QKV projection takes the rotary embedding and
+  // the split into q / the K, V caches in its epilogue (EPI_ROPE); wqkv_t's
+  // rows are then permuted in 32-row blocks (see EPI_ROPE)
+  bool qkv_rope = false;
 
   // tail workspace (rows = B * b), per tail block where saved for the backward
   std::vector<float*> tx, ty, tr1, tr2, tlse;
@@ -256,6 +260,27 @@ inline uint32_t sr_seed(int64_t chunk, int j, int mat) {
   return (uint32_t)(chunk * 64 + j * 4 + mat) * 2654435761u | 1u;
 }
 
+// Q/K/V of block l for R = B*S rows (positions p0.. of each sequence): q into
+// q_out, k and v into the block's ring caches (slot pos % cap), RoPE applied;
+// in one product with the rotation in its epilogue, or through fp32 qkv
+void qkv(Ctx& c, const void* u, int l, int R, int S, int64_t p0, float* qkv32, void* q_out, int cap) {
+  ttt_model* m = c.m;
+  const int d = m->d, HD = m->HD;
+  const float2* tab = m->cfg.rope ? m->rope : nullptr;
+  if (m->qkv_rope) {
+    GemmArgs g = ga(u, d, m->wqkv_t[l], d, nullptr, 0, R, 3 * HD, d);
+    g.rope.q = q_out; g.rope.kc = m->kc[l]; g.rope.vc = m->vc[l]; g.rope.tab = tab;
+    g.rope.ldq = HD; g.rope.seq_stride = (int64_t)cap * HD; g.rope.p0 = p0;
+    g.rope.cap = cap; g.rope.S = S; g.rope.H = m->H; g.rope.hd = m->hd;
+    c.gemm(EPI_ROPE, false, g);
+    return;
+  }
+  c.gemm(EPI_STORE, true, ga(u, d, m->wqkv_t[l], d, qkv32, 3 * HD, R, 3 * HD, d));
+  c.chk(rope_split_launch(qkv32, R, S, m->H, m->hd, p0, tab, q_out, m->kc[l], m->vc[l], cap, (int64_t)cap * HD,
+                          m->dt, c.st),
+        "rope");
+}
+
 // ---------- the span pass: frozen prefix over positions [p0, p0+S) ----------
 void span_pass(Ctx& c, int64_t p0, int S) {
   ttt_model* m = c.m;
@@ -264,10 +289,7 @@ void span_pass(Ctx& c, int64_t p0, int S) {
   c.chk(embed_launch(m->ids, m->maxpos, p0, S, B, m->embed, d, m->V, m->sX, m->dt, c.st), "embed");
   for (int l = 0; l <= m->t0; ++l) {
     c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_attn[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
-    c.gemm(EPI_STORE, true, ga(m->sU, d, m->wqkv_t[l], d, m->sQKV, 3 * HD, R, 3 * HD, d));
-    c.chk(rope_split_launch(m->sQKV, R, S, m->H, m->hd, p0, m->cfg.rope ? m->rope : nullptr, m->sQ,
-                            m->kc[l], m->vc[l], m->cap_s, (int64_t)m->cap_s * HD, m->dt, c.st),
-          "rope");
+    qkv(c, m->sU, l, R, S, p0, m->sQKV, m->sQ, m->cap_s);
     AttnArgs a;
     memset(&a, 0, sizeof(a));
     a.q = m->sQ; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
@@ -323,10 +345,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     if (j >= 1) {
       y = m->ty[j];
       c.chk(rmsnorm_fwd_launch(m->tx[j], R, d, m->g_attn[l], eps, m->tU, m->tr1[j], m->dt, c.st), "norm");
-      c.gemm(EPI_STORE, true, ga(m->tU, d, m->wqkv_t[l], d, m->tQKV, 3 * HD, R, 3 * HD, d));
-      c.chk(rope_split_launch(m->tQKV, R, M, m->H, m->hd, P0, m->cfg.rope ? m->rope : nullptr, m->tq[j],
-                              m->kc[l], m->vc[l], m->cap_t, (int64_t)m->cap_t * HD, m->dt, c.st),
-            "rope");
+      qkv(c, m->tU, l, R, M, P0, m->tQKV, m->tq[j], m->cap_t);
       AttnArgs a;
       memset(&a, 0, sizeof(a));
       a.q = m->tq[j]; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
@@ -692,7 +711,8 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   // span workspace
   const int64_t Rs = (int64_t)B * span;
   m->sX = A.f32(Rs * d); m->sR = A.f32(Rs); m->sL = A.f32(Rs * m->H);
-  m->sU = A.el(Rs * d); m->sQKV = A.f32(Rs * 3 * HD); m->sQ = A.el(Rs * HD); m->sO = A.el(Rs * HD);
+  m->qkv_rope = m->dt == 1 && m->hd % 64 == 0;
+  m->sU = A.el(Rs * d); m->sQKV = m->qkv_rope ? nullptr : A.f32(Rs * 3 * HD); m->sQ = A.el(Rs * HD); m->sO = A.el(Rs * HD);
   m->sA = A.el(Rs * h);
   // tail workspace
   const int64_t Rt = (int64_t)B * b;
@@ -710,7 +730,7 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
     m->tz[j] = A.f32(Rt * mg * hf); m->ta[j] = A.el(Rt * hf);
   }
   m->txL = A.f32(Rt * d); m->trf = A.f32(Rt); m->tlog = A.f32(Rt * V);
-  m->tf = A.el(Rt * d); m->tdz = A.el(Rt * V); m->tU = A.el(Rt * d); m->tQKV = A.f32(Rt * 3 * HD);
+  m->tf = A.el(Rt * d); m->tdz = A.el(Rt * V); m->tU = A.el(Rt * d); m->tQKV = m->qkv_rope ? nullptr : A.f32(Rt * 3 * HD);
   m->dres = A.f32(Rt * d); m->dn = A.f32(Rt * d); m->dA = A.f32(Rt * hf); m->delta = A.f32(Rt * m->H);
   m->dq = A.f32(ttt_model::kMaxSplit * Rt * HD); m->dk = A.f32(Rt * HD); m->dv = A.f32(Rt * HD);
   m->part_o = A.f32(ttt_model::kMaxSplit * Rt * HD);
@@ -783,9 +803,24 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   for (int l = 0; l < L; ++l) {
     ck(hipMemcpyAsync(m->g_attn[l], w->attn_norm[l], d * es, hipMemcpyDeviceToDevice, st));
     ck(hipMemcpyAsync(m->g_mlp[l], w->mlp_norm[l], d * es, hipMemcpyDeviceToDevice, st));
-    ck(put_t(w->wq[l], d, HD, m->wqkv_t[l], d, dt, dt, st));
-    ck(put_t(w->wk[l], d, HD, off(m->wqkv_t[l], (int64_t)HD * d, es), d, dt, dt, st));
-    ck(put_t(w->wv[l], d, HD, off(m->wqkv_t[l], (int64_t)2 * HD * d, es), d, dt, dt, st));
+    if (m->qkv_rope) {
+      // each head part's 32-column blocks of W^T to their permuted row blocks
+      // (block b -> 2b in the first half, 2(b - nb/2) + 1 in the second),
+      // batched over the heads
+      const int hd = m->hd, nb = hd / 32;
+      const void* src3[3] = {w->wq[l], w->wk[l], w->wv[l]};
+      for (int part = 0; part < 3; ++part)
+        for (int b = 0; b < nb; ++b) {
+          const int k = b < nb / 2 ? 2 * b : 2 * (b - nb / 2) + 1;
+          ck(transpose_launch(static_cast<const char*>(src3[part]) + (int64_t)32 * b * es, d, 32, HD, dt,
+                              off(m->wqkv_t[l], ((int64_t)part * HD + 32 * k) * d, es), d, dt, st, m->H, hd,
+                              (int64_t)hd * d));
+        }
+    } else {
+      ck(put_t(w->wq[l], d, HD, m->wqkv_t[l], d, dt, dt, st));
+      ck(put_t(w->wk[l], d, HD, off(m->wqkv_t[l], (int64_t)HD * d, es), d, dt, dt, st));
+      ck(put_t(w->wv[l], d, HD, off(m->wqkv_t[l], (int64_t)2 * HD * d, es), d, dt, dt, st));
+    }
     ck(put_t(w->wo[l], HD, d, m->wo_t[l], HD, dt, dt, st));
     if (l > t0) {
       const void* qkv[3] = {w->wq[l], w->wk[l], w->wv[l]};

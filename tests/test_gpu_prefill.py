@@ -141,6 +141,33 @@ def test_bf16_two_sequences_head_dim_128():
     model.close()
 
 
+def test_decode_bf16_head_dim_128():
+    """bf16 decode with head dim 128 (one-row Q/K/V products with the rotary
+    epilogue, one-query attention), across a chunk boundary, against the
+    oracle fed the generated ids."""
+    cfg = small_cfg(dtype="bf16", vocab=512, d_model=256, n_heads=2, head_dim=128, mlp_hidden=512,
+                    ttt_hidden=256, static_hidden=256, n_blocks=4, n_ttt_blocks=2, window=128,
+                    mini_batch=64, lr=0.05, span=32, period=256)
+    wd, wn = dev_weights(cfg, std=0.05)
+    prompt = synth.make_batch(cfg, 2, 41, seed=3)
+    model = bd.TTTModel(cfg, wd, batch=2, max_positions=200)
+    model.prefill(torch.as_tensor(prompt).cuda())
+    gen, gl = model.decode(45)
+    torch.cuda.synchronize()
+    gen = gen.cpu().numpy()
+    gl = gl.cpu().numpy()
+    for s in range(2):
+        orc = O.Oracle(cfg, wn)
+        orc.prefill(prompt[s])
+        lo = []
+        for t in gen[s]:
+            z = orc.last_logits
+            assert z[t] >= z.max() - 5e-2     # the GPU's id is (within bf16 noise) the oracle's argmax
+            lo.append(orc.prefill([int(t)])[0])
+        np.testing.assert_allclose(gl[s], lo, atol=BF16_TOL["loss"], rtol=0)
+    model.close()
+
+
 def test_forward_only_is_the_static_model():
     """forward_only: every position scored at W_init in one causal pass (the
     oracle's static losses; with a window as long as the stream, full causal
