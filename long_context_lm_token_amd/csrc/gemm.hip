@@ -99,7 +99,7 @@ TTT_DEV typename GT<T>::frag read_frag(const T* s, int row, int k) {
 TTT_DEV void tile_coords(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
   const int ntiles = tiles_m * tiles_n;
   if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
-  constexpr int GROUP = 8;
+  constexpr int GROUP = 4;
   const int group = t / (GROUP * tiles_n);
   const int first_m = group * GROUP;
   const int gsz = min(tiles_m - first_m, GROUP);
