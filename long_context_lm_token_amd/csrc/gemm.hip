@@ -753,11 +753,34 @@ TTT_DEV float dot8(bf16x8 a, bf16x8 b) {
   return s;
 }
 
+// EPI_ROPE for one row and one rotation pair: 64-column block cb, offset u < 32
+template <typename OutT>
+TTT_DEV void rope_store(const RopeOut& ro, int row, int cb, int u, float y1, float y2) {
+  const int hd = ro.hd, half = hd / 2;
+  const int hp = cb / hd, part = hp / ro.H, h = hp % ro.H;
+  const int e1 = ((cb % hd) / 64) * 32 + u;
+  const int sq = row / ro.S;
+  const int64_t pos = ro.p0 + row % ro.S;
+  if (part < 2 && ro.tab) {
+    const float2 cs = ro.tab[pos * half + e1];
+    const float a = y1, b = y2;
+    y1 = a * cs.x - b * cs.y;
+    y2 = a * cs.y + b * cs.x;
+  }
+  OutT* dst = part == 0 ? reinterpret_cast<OutT*>(ro.q) + (int64_t)row * ro.ldq
+                        : reinterpret_cast<OutT*>(part == 1 ? ro.kc : ro.vc) + sq * ro.seq_stride +
+                              (pos % ro.cap) * (int64_t)(ro.H * hd);
+  dst += h * hd + e1;
+  dst[0] = from_f32<OutT>(y1);
+  dst[half] = from_f32<OutT>(y2);
+}
+
 template <int EPI, typename OutT>
 __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
   // each wave streams GV_ROWS outputs at once (more loads in flight)
   constexpr int GV_ROWS = 2;
-  constexpr bool GLU = EPI == EPI_SWIGLU;
+  // SwiGLU and the rotary split both pair column c with c + 32 (64-column blocks)
+  constexpr bool GLU = EPI == EPI_SWIGLU || EPI == EPI_ROPE;
   constexpr int NB = GLU ? 2 * GV_ROWS : GV_ROWS;  // rows of B per wave step
   const int z = blockIdx.z;
   const bf16* A = reinterpret_cast<const bf16*>(p.A) + z * p.sA;
@@ -807,7 +830,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
 #pragma unroll
         for (int m = 0; m < GV_MAXM; ++m)
           if (lane == m) { v = acc[q][m]; if constexpr (GLU) v2 = acc[GV_ROWS + q][m]; }
-        if constexpr (GLU)
+        if constexpr (EPI == EPI_ROPE)
+          rope_store<OutT>(p.rope, lane, (o >> 5) * 64, o & 31, v, v2);
+        else if constexpr (GLU)
           reinterpret_cast<OutT*>(p.C)[z * p.sC + (int64_t)lane * p.ldc + o] = from_f32<OutT>(swiglu_acc(v, v2));
         else
           apply<EPI, OutT, bf16>(p, z, lane, o, v);
@@ -818,7 +843,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
 
 template <int EPI, typename OutT>
 hipError_t launch_gemv(const GemmArgs& p, int batch, hipStream_t st) {
-  const int nout = EPI == EPI_SWIGLU ? p.N / 2 : p.N;
+  const int nout = (EPI == EPI_SWIGLU || EPI == EPI_ROPE) ? p.N / 2 : p.N;
   const int blocks = std::min((nout + 7) / 8, 4096);  // 4 waves of 2 outputs
   hipLaunchKernelGGL((gemv_kernel<EPI, OutT>), dim3(blocks, 1, batch), dim3(256), 0, st, p);
   return hipGetLastError();
@@ -922,7 +947,7 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   }
   if (p.mn) return hipErrorInvalidValue;
   int cfg = g_force_tile;
-  if constexpr (sizeof(T) == 2 && EPI != EPI_SGD && EPI != EPI_ROPE) {
+  if constexpr (sizeof(T) == 2 && EPI != EPI_SGD) {
     // a few rows of A (decode): one streaming pass over B
     if (!cfg && p.M <= GV_MAXM) return launch_gemv<EPI, OutT>(p, batch, st);
   }
