@@ -954,8 +954,11 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   if (!cfg) {
     // direct-to-LDS 256x256 when there are enough large tiles (or K is long
     // enough for split-K to fill the CUs); register-staged kernels otherwise
+    // (also when a short K leaves 128x128 tiles unsplit over more than one
+    // round of block slots, and the large tiles alone cover over half the CUs)
     const bool dl = sizeof(T) == 2 && p.K % 64 == 0;
-    if (dl && EPI != EPI_SGD && (t256 >= CUS || p.K >= 24576)) cfg = 4;
+    const bool ragged128 = t256 > CUS / 2 && t128 > 2 * CUS && p.K <= 48 * 64;
+    if (dl && EPI != EPI_SGD && (t256 >= CUS || ragged128 || p.K >= 24576)) cfg = 4;
     else if (dl) cfg = 6;
     else cfg = t256 >= 2 * CUS ? 1 : 3;
   }
