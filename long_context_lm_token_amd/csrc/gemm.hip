@@ -952,13 +952,14 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
     if (!cfg && p.M <= GV_MAXM) return launch_gemv<EPI, OutT>(p, batch, st);
   }
   if (!cfg) {
-    // direct-to-LDS 256x256 when there are enough large tiles (or K is long
-    // enough for split-K to fill the CUs); register-staged kernels otherwise
+    // direct-to-LDS 256x256 when there are enough large tiles (or K >= 8192,
+    // long enough for split-K over few tiles to fill the CUs in one round);
+    // register-staged kernels otherwise
     // (also when a short K leaves 128x128 tiles unsplit over more than one
     // round of block slots, and the large tiles alone cover over half the CUs)
     const bool dl = sizeof(T) == 2 && p.K % 64 == 0;
     const bool ragged128 = t256 > CUS / 2 && t128 > 2 * CUS && p.K <= 48 * 64;
-    if (dl && EPI != EPI_SGD && (t256 >= CUS || ragged128 || p.K >= 24576)) cfg = 4;
+    if (dl && EPI != EPI_SGD && (t256 >= CUS || ragged128 || p.K >= 8192)) cfg = 4;
     else if (dl) cfg = 6;
     else cfg = t256 >= 2 * CUS ? 1 : 3;
   }
