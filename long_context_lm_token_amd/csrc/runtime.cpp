@@ -440,7 +440,12 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       g.sA = (int64_t)M * zw; g.sB = sbgu; g.sC = (int64_t)M * d;
       c.gemm(EPI_STORE, true, g, B);
     }
-    // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ_t^T . n  (side stream)
+    // W_gate / W_up trainable rows: W^T[ht][d] -= eta * dZ_t^T . n. On the
+    // side stream, except for the first tail block: its update is the last
+    // one the next chunk waits for, so it runs on this stream at once rather
+    // than behind the side stream's queue. With one sequence the gate and up
+    // parts are one launch batched over the part (the part index then also
+    // separates their stochastic-rounding streams).
     if (!mnw) {
       c.transpose(m->tn[j], M, d, d, m->Tn[j], M, B, (int64_t)M * d, (int64_t)d * M);
       for (int part = 0; part < mg; ++part) {
@@ -448,26 +453,28 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
         c.transpose(off(dz, (int64_t)part * hf, es), M, ht, zw, tdz, M, B, (int64_t)M * zw, (int64_t)ht * M);
       }
     }
-    c.order(c.st, m->side, m->ev[2 * j + 1]);
-    for (int part = 0; part < mg; ++part) {
+    hipStream_t gu_st = j == 0 ? nullptr : m->side;
+    if (j > 0) c.order(c.st, m->side, m->ev[2 * j + 1]);
+    const bool by_part = B == 1 && mg > 1;
+    for (int part = 0; part < (by_part ? 1 : mg); ++part) {
       const int64_t zoff = (int64_t)part * hf;      // column of dZ / row of the forward copy
       const int64_t moff = (int64_t)part * ht * d;  // row block of the master
       void* fcopy = master ? off(m->f_gu[j], zoff * d, es) : nullptr;
       if (mnw) {
         g = ga(off(dz, zoff, es), zw, m->tn[j], d, fcopy, d, ht, d, M);
-        g.sA = (int64_t)M * zw; g.sB = (int64_t)M * d; g.mn = 1;
+        g.sA = by_part ? (int64_t)hf : (int64_t)M * zw; g.sB = by_part ? 0 : (int64_t)M * d; g.mn = 1;
       } else {
         void* tdz = off(m->Tdz[j], (int64_t)part * B * ht * M, es);
         g = ga(tdz, M, m->Tn[j], M, fcopy, d, ht, d, M);
-        g.sA = (int64_t)ht * M; g.sB = (int64_t)d * M;
+        g.sA = (int64_t)ht * M; g.sB = by_part ? 0 : (int64_t)d * M;
       }
-      g.sC = sgu;
+      g.sC = by_part ? (int64_t)hf * d : sgu;
       g.Wm = master ? m->m_gu[j] + moff : reinterpret_cast<float*>(off(m->f_gu[j], zoff * d, es));
-      g.ldw = d; g.sW = master ? smgu : sgu;
-      g.C2 = off(m->fb_gu[j], zoff, es); g.ldc2 = zw; g.sC2 = sbgu;
+      g.ldw = d; g.sW = by_part ? (int64_t)(master ? ht : hf) * d : (master ? smgu : sgu);
+      g.C2 = off(m->fb_gu[j], zoff, es); g.ldc2 = zw; g.sC2 = by_part ? (int64_t)hf : sbgu;
       g.lr = m->cfg.lr;
       g.sr_seed = sr_seed(P0 / m->cfg.mini_batch, j, part);
-      c.gemm(EPI_SGD, false, g, B, m->side);
+      c.gemm(EPI_SGD, false, g, by_part ? mg : B, gu_st);
     }
     if (j == 0) break;
     c.chk(rmsnorm_bwd_launch(m->ty[j], m->tr2[j], m->g_mlp[l], m->dn, R, d, m->dres, m->dres_c, true, m->dt,
