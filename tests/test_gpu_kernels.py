@@ -90,6 +90,20 @@ def test_gemm_direct_to_lds(tile, epi, shape, ws):
     assert err < 4e-5 * math.sqrt(K), err
 
 
+@pytest.mark.parametrize("epi,shape,ws", [
+    (0, (1024, 8448, 192), 0),        # 128x128 tiles would take more than one round: 256x256, unsplit
+    (0, (256, 384, 8192), 1 << 22),   # long K over few tiles: 256x256 split over K to fill the CUs
+    (1, (300, 520, 8256), 1 << 22),   # the same with ragged M / N, an uneven split and the residual
+])
+def test_gemm_automatic_tile_rules(epi, shape, ws):
+    """The automatic tile choice at the shapes whose rules the chunk loop's
+    products (Q/K/V, dn, dx, MLP down) fall under."""
+    M, N, K = shape
+    ref, got, _, _ = run_gemm(torch.bfloat16, epi, M, N, K, tile=0, ws_elems=ws)
+    err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err < 4e-5 * math.sqrt(K), err
+
+
 @pytest.mark.parametrize("N", [640, 645, 40001])
 @pytest.mark.parametrize("M", [1, 3, 8])
 @pytest.mark.parametrize("epi,out_f32", [(0, True), (0, False), (1, True), (3, False), (4, True)])
