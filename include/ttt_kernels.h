@@ -83,7 +83,9 @@ int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc,
 
 /* Test hook: 0 runs bf16 head-dim-128 attention (forward, dQ, dK/dV) on the
  * register-staged kernels (those of the other head dims), 1 (default) on the
- * direct-to-LDS ones. Process-wide. */
+ * direct-to-LDS ones, with the forward of at most 8 queries per sequence on
+ * the one-query streaming kernel; 2 as 1 but the forward always on the
+ * direct-to-LDS tile kernel. Process-wide. */
 void ttt_k_attn_fwd_kernel(int32_t dl);
 
 /* The library's choice of key-range splits for M queries per sequence. */

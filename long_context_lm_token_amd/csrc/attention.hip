@@ -634,6 +634,111 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
   }
 }
 
+// Forward for a few queries (decode; the last rows of a prefill), bf16, head
+// dim 128: one workgroup per (query, head, sequence, key split) streams the
+// split's K and V rows from the ring once. A row is 256 bytes, one 16-byte
+// load per lane of a 16-lane group, so a wave reads 4 keys per instruction
+// and the 16 groups of a workgroup take keys jb + g, jb + g + 16, ... Each
+// group keeps its own online softmax (max in log2 units, sum, 128 output
+// columns over its 16 lanes); the groups are merged through LDS at the end.
+// Outputs as the tile kernels: o and lse, or the split partials (normalised
+// O, max, sum) that attn_combine_kernel merges.
+constexpr int ONE_MAXM = 8;  // queries per sequence served by this kernel
+constexpr int ONE_U = 4;     // keys per group with loads in flight
+__global__ __launch_bounds__(256) void attn_fwd_one_kernel(AttnArgs a) {
+  __shared__ float gm[16], gl[16];
+  __shared__ float go[16][FD_HD];
+  const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
+  const Blk bk = blk();
+  const int s = bk.z / nsplit, sp = bk.z % nsplit, h = bk.y, q = bk.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = w * 4 + (lane >> 4);  // key group
+  const int c8 = (lane & 15) * 8;     // this lane's 8 columns
+  const int pq = (int)a.pos0 + q;     // positions fit in 31 bits
+  const int win = a.window;
+  int jb, je;
+  split_range(max(0, pq - win + 1) & ~(BKEY - 1), pq, nsplit, sp, &jb, &je);
+  const float c2 = a.scale * LOG2E;
+  float qf[8];
+  {
+    const bf16x8 qv =
+        *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.q) + ((int64_t)s * a.M + q) * a.ldq +
+                                         h * FD_HD + c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[e] = (float)qv[e] * c2;
+  }
+  const bf16* Kc = reinterpret_cast<const bf16*>(a.kc) + s * a.seq_stride + h * FD_HD + c8;
+  const bf16* Vc = reinterpret_cast<const bf16*>(a.vc) + s * a.seq_stride + h * FD_HD + c8;
+  float m = NEG_BIG, l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  // ring slot of this group's next key (cap is a multiple of 64)
+  int slot = (jb + g) % a.cap;
+  for (int j0 = jb + g; j0 < je; j0 += 16 * ONE_U) {
+    bf16x8 kv[ONE_U], vv[ONE_U];
+#pragma unroll
+    for (int u = 0; u < ONE_U; ++u) {
+      if (j0 + 16 * u < je) {
+        kv[u] = *reinterpret_cast<const bf16x8*>(Kc + (int64_t)slot * a.ldk);
+        vv[u] = *reinterpret_cast<const bf16x8*>(Vc + (int64_t)slot * a.ldk);
+      }
+      slot += 16;
+      if (slot >= a.cap) slot -= a.cap;
+    }
+#pragma unroll
+    for (int u = 0; u < ONE_U; ++u) {
+      const int j = j0 + 16 * u;
+      if (j >= je) break;  // uniform over the 16 lanes of a group
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qf[e], (float)kv[u][e], d);
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      d += __shfl_xor(d, 4, 64);
+      d += __shfl_xor(d, 8, 64);
+      // visible iff pq - win < j <= pq
+      const float sc = (unsigned)(pq - j) < (unsigned)win ? d : -INFINITY;
+      const float mn = fmaxf(m, sc);
+      const float al = ex2(m - mn), p = ex2(sc - mn);
+      l = fmaf(l, al, p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(o[e], al, p * (float)vv[u][e]);
+      m = mn;
+    }
+  }
+  if ((lane & 15) == 0) {
+    gm[g] = m;
+    gl[g] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) go[g][c8 + e] = o[e];
+  __syncthreads();
+  const int c = threadIdx.x;
+  if (c >= FD_HD) return;
+  float mx = NEG_BIG;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, gm[i]);
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float wg = ex2(gm[i] - mx);
+    L = fmaf(gl[i], wg, L);
+    acc = fmaf(go[i][c], wg, acc);
+  }
+  const int64_t row = (int64_t)s * a.M + q;
+  if (nsplit == 1) {
+    reinterpret_cast<bf16*>(a.o)[row * a.ldo + h * FD_HD + c] = (bf16)(acc / L);
+    if (c == 0) a.lse[((int64_t)s * a.H + h) * a.M + q] = mx * LN2 + logf(L);
+  } else {
+    a.part_o[((int64_t)sp * a.B * a.M + row) * a.ldo + h * FD_HD + c] = L > 0.f ? acc / L : 0.f;
+    if (c == 0) {
+      const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * a.M + q;
+      a.part_m[li] = mx;
+      a.part_l[li] = L;
+    }
+  }
+}
+
 // merge split partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - m).
 // One workgroup per row: the normalised weights of every (split, head) go to
 // LDS first, then each thread combines 4 consecutive columns.
@@ -670,6 +775,45 @@ __global__ void attn_combine_kernel(AttnArgs a) {
       acc[0] += w * v.x; acc[1] += w * v.y; acc[2] += w * v.z; acc[3] += w * v.w;
     }
     T* o = reinterpret_cast<T*>(a.o) + row * a.ldo + c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = from_f32<T>(acc[k]);
+  }
+}
+
+// The same merge for a few rows (decode): one wave per (row, head), so the
+// split partials of a row are read by many workgroups at once.
+template <typename T>
+__global__ __launch_bounds__(64) void attn_combine_head_kernel(AttnArgs a) {
+  const int64_t row = blockIdx.x;  // s*M + q
+  const int h = blockIdx.y;
+  const int s = row / a.M, q = row % a.M;
+  float m = NEG_BIG;
+  for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part_m[(((int64_t)sp * a.B + s) * a.H + h) * a.M + q]);
+  float wgt[16];
+  float wsum = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < 16; ++sp) {
+    wgt[sp] = 0.f;
+    if (sp < a.nsplit) {
+      const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * a.M + q;
+      wgt[sp] = a.part_l[li] * ex2(a.part_m[li] - m);
+      wsum += wgt[sp];
+    }
+  }
+  const float inv = 1.f / wsum;
+  if (threadIdx.x == 0) a.lse[((int64_t)s * a.H + h) * a.M + q] = m * LN2 + logf(wsum);
+  for (int c = threadIdx.x * 4; c < a.hd; c += 64 * 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp) {
+      if (sp < a.nsplit) {
+        const float4 v =
+            *reinterpret_cast<const float4*>(a.part_o + ((int64_t)sp * a.B * a.M + row) * a.ldo + h * a.hd + c);
+        const float w = wgt[sp] * inv;
+        acc[0] += w * v.x; acc[1] += w * v.y; acc[2] += w * v.z; acc[3] += w * v.w;
+      }
+    }
+    T* o = reinterpret_cast<T*>(a.o) + row * a.ldo + h * a.hd + c;
 #pragma unroll
     for (int k = 0; k < 4; ++k) o[k] = from_f32<T>(acc[k]);
   }
@@ -1303,14 +1447,20 @@ hipError_t fwd_t(const AttnArgs& a, hipStream_t st) {
   const int ns = a.nsplit > 0 ? a.nsplit : 1;
   dim3 grid((a.M + QB - 1) / QB, a.H, a.B * ns);
   const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-  if (sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
-      a.seq_stride % 8 == 0)
+  const bool dl = sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
+                  a.seq_stride % 8 == 0;
+  if (dl && g_attn_dl == 1 && a.M <= ONE_MAXM && al16(a.q) && a.ldq % 8 == 0)
+    hipLaunchKernelGGL(attn_fwd_one_kernel, dim3(a.M, a.H, a.B * ns), dim3(256), 0, st, a);
+  else if (dl)
     hipLaunchKernelGGL(attn_fwd_dl_kernel, grid, dim3(NT), 0, st, a);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<T>), dim3(a.B * a.M), dim3(256), 0, st, a);
+  if (a.M <= ONE_MAXM)
+    hipLaunchKernelGGL((attn_combine_head_kernel<T>), dim3(a.B * a.M, a.H), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<T>), dim3(a.B * a.M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 template <typename T, int HD>

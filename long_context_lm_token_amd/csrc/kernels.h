@@ -83,7 +83,7 @@ struct AttnArgs {
 
 hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st);
 hipError_t attn_bwd_launch(const AttnArgs& a, int dt, hipStream_t st);
-void attn_force_fwd_kernel(int dl);  // test hook: 0 = register-staged forward for bf16 hd 128
+void attn_force_fwd_kernel(int dl);  // test hook: 0 register-staged, 1 default, 2 no one-query forward (bf16 hd 128)
 // number of key-range splits that keeps the CUs busy for M queries per sequence
 int attn_splits(int M, int H, int B, int64_t keys_per_query);
 
