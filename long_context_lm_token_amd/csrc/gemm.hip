@@ -745,7 +745,7 @@ __global__ void gemm_reduce(GemmArgs p, int splits, int batch, const float* __re
 // 16-byte loads per lane and forms the M dot products against the rows of A
 // (small, cache-resident), then reduces them across the wave. SwiGLU: a wave
 // takes one hidden unit, i.e. its interleaved gate and up rows.
-constexpr int GV_MAXM = 8;
+constexpr int GV_MAXM = GEMV_MAX_ROWS;
 TTT_DEV float dot8(bf16x8 a, bf16x8 b) {
   float s = 0.f;
 #pragma unroll
@@ -788,6 +788,24 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
   const int lane = threadIdx.x & 63;
   const int nw = gridDim.x * 4;
   const int nout = GLU ? p.N / 2 : p.N;
+  // RMSNorm folded into the A operand: each wave takes its rows' 1/rms itself
+  const float* X = p.nx ? p.nx + z * p.snx : nullptr;
+  const bf16* G = reinterpret_cast<const bf16*>(p.ng);
+  float rs[GV_MAXM];
+#pragma unroll
+  for (int m = 0; m < GV_MAXM; ++m) {
+    rs[m] = 0.f;
+    if (X && m < p.M) {
+      float ss = 0.f;
+      for (int k = lane * 8; k < p.K; k += 512) {
+        const float4 x0 = *reinterpret_cast<const float4*>(X + m * p.ldnx + k);
+        const float4 x1 = *reinterpret_cast<const float4*>(X + m * p.ldnx + k + 4);
+        ss += x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w;
+        ss += x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
+      }
+      rs[m] = rsqrtf(wave_sum(ss) / p.K + p.neps);
+    }
+  }
   for (int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * GV_ROWS; o0 < nout; o0 += nw * GV_ROWS) {
     const bf16* brow[NB];
 #pragma unroll
@@ -806,10 +824,21 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
       bf16x8 bv[NB];
 #pragma unroll
       for (int q = 0; q < NB; ++q) bv[q] = *reinterpret_cast<const bf16x8*>(brow[q] + k);
+      bf16x8 gv;
+      if (X) gv = *reinterpret_cast<const bf16x8*>(G + k);
 #pragma unroll
       for (int m = 0; m < GV_MAXM; ++m) {
         if (m < p.M) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(A + (int64_t)m * p.lda + k);
+          bf16x8 av;
+          if (X) {
+            const float4 x0 = *reinterpret_cast<const float4*>(X + m * p.ldnx + k);
+            const float4 x1 = *reinterpret_cast<const float4*>(X + m * p.ldnx + k + 4);
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = (bf16)(xv[e] * (rs[m] * (float)gv[e]));
+          } else {
+            av = *reinterpret_cast<const bf16x8*>(A + (int64_t)m * p.lda + k);
+          }
 #pragma unroll
           for (int q = 0; q < NB; ++q) acc[q][m] += dot8(av, bv[q]);
         }
@@ -843,6 +872,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs p) {
 
 template <int EPI, typename OutT>
 hipError_t launch_gemv(const GemmArgs& p, int batch, hipStream_t st) {
+  if (p.nx && (p.ldnx % 4 || p.snx % 4 || !p.ng || reinterpret_cast<uintptr_t>(p.nx) % 16 ||
+               reinterpret_cast<uintptr_t>(p.ng) % 16))
+    return hipErrorInvalidValue;
   const int nout = (EPI == EPI_SWIGLU || EPI == EPI_ROPE) ? p.N / 2 : p.N;
   const int blocks = std::min((nout + 7) / 8, 4096);  // 4 waves of 2 outputs
   hipLaunchKernelGGL((gemv_kernel<EPI, OutT>), dim3(blocks, 1, batch), dim3(256), 0, st, p);
@@ -939,7 +971,7 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
   if constexpr (sizeof(T) == 2 && (EPI == EPI_SGD || EPI == EPI_STORE)) {
     if (p.mn) {
       const auto al = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
-      if (p.M % 128 || p.N % 128 || p.K % 64 || p.lda % 8 || p.ldb % 8 || p.sA % 8 || p.sB % 8 || !al(p.A) ||
+      if (p.nx || p.M % 128 || p.N % 128 || p.K % 64 || p.lda % 8 || p.ldb % 8 || p.sA % 8 || p.sB % 8 || !al(p.A) ||
           !al(p.B))
         return hipErrorInvalidValue;
       return launch_dl<128, 128, 2, 2, 64, 2, EPI, OutT, true>(p, batch, 1, nullptr, st);
@@ -951,6 +983,7 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
     // a few rows of A (decode): one streaming pass over B
     if (!cfg && p.M <= GV_MAXM) return launch_gemv<EPI, OutT>(p, batch, st);
   }
+  if (p.nx) return hipErrorInvalidValue;  // a folded RMSNorm needs the skinny kernel
   if (!cfg) {
     // direct-to-LDS 256x256 when there are enough large tiles (or K >= 8192,
     // long enough for split-K over few tiles to fill the CUs in one round);

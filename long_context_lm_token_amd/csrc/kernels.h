@@ -51,7 +51,16 @@ struct GemmArgs {
   // bf16 only: A and B stored MN-major, element (m, k) at A[k * lda + m] and
   // (n, k) at B[k * ldb + n] (M, N multiples of 128, K of 64; no split)
   int mn;
+  // skinny products only (bf16, at most GEMV_MAX_ROWS rows of A, not SGD):
+  // if nx is set, A is not read; row m of batch z is the RMSNorm of the fp32
+  // row nx[z * snx + m * ldnx ..] with gain ng (compute dtype) rounded to the
+  // compute dtype, as rmsnorm_fwd_launch writes it. Other kernels reject it.
+  const float* nx;
+  int64_t ldnx, snx;
+  const void* ng;
+  float neps;
 };
+constexpr int GEMV_MAX_ROWS = 8;  // products with at most this many rows of A stream B once
 
 // ws: fp32 split-K workspace of ws_elems elements (may be null: no split)
 hipError_t gemm_launch(const GemmArgs& p, int dt, int epi, bool out_f32, int batch, float* ws,

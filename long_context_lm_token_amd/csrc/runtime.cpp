@@ -260,22 +260,34 @@ inline uint32_t sr_seed(int64_t chunk, int j, int mat) {
   return (uint32_t)(chunk * 64 + j * 4 + mat) * 2654435761u | 1u;
 }
 
+// The RMSNorm of fp32 rows x (gain gn) as the A operand of a skinny product,
+// computed inside it: forward-only passes of at most GEMV_MAX_ROWS rows per
+// product (bf16) skip the norm kernel and its output
+void fold_norm(GemmArgs& g, const float* x, int64_t ldx, int64_t sx, const void* gn, float eps) {
+  g.nx = x; g.ldnx = ldx; g.snx = sx; g.ng = gn; g.neps = eps;
+}
+
 // Q/K/V of block l for R = B*S rows (positions p0.. of each sequence): q into
 // q_out, k and v into the block's ring caches (slot pos % cap), RoPE applied;
-// in one product with the rotation in its epilogue, or through fp32 qkv
-void qkv(Ctx& c, const void* u, int l, int R, int S, int64_t p0, float* qkv32, void* q_out, int cap) {
+// in one product with the rotation in its epilogue, or through fp32 qkv. With
+// nx set, A is the RMSNorm of nx (gain ng) instead of u.
+void qkv(Ctx& c, const void* u, int l, int R, int S, int64_t p0, float* qkv32, void* q_out, int cap,
+         const float* nx = nullptr, const void* ng = nullptr) {
   ttt_model* m = c.m;
   const int d = m->d, HD = m->HD;
   const float2* tab = m->cfg.rope ? m->rope : nullptr;
   if (m->qkv_rope) {
     GemmArgs g = ga(u, d, m->wqkv_t[l], d, nullptr, 0, R, 3 * HD, d);
+    if (nx) fold_norm(g, nx, d, 0, ng, m->cfg.norm_eps);
     g.rope.q = q_out; g.rope.kc = m->kc[l]; g.rope.vc = m->vc[l]; g.rope.tab = tab;
     g.rope.ldq = HD; g.rope.seq_stride = (int64_t)cap * HD; g.rope.p0 = p0;
     g.rope.cap = cap; g.rope.S = S; g.rope.H = m->H; g.rope.hd = m->hd;
     c.gemm(EPI_ROPE, false, g);
     return;
   }
-  c.gemm(EPI_STORE, true, ga(u, d, m->wqkv_t[l], d, qkv32, 3 * HD, R, 3 * HD, d));
+  GemmArgs g = ga(u, d, m->wqkv_t[l], d, qkv32, 3 * HD, R, 3 * HD, d);
+  if (nx) fold_norm(g, nx, d, 0, ng, m->cfg.norm_eps);
+  c.gemm(EPI_STORE, true, g);
   c.chk(rope_split_launch(qkv32, R, S, m->H, m->hd, p0, tab, q_out, m->kc[l], m->vc[l], cap, (int64_t)cap * HD,
                           m->dt, c.st),
         "rope");
@@ -287,9 +299,11 @@ void span_pass(Ctx& c, int64_t p0, int S) {
   const int B = m->cfg.batch, d = m->d, HD = m->HD, R = B * S;
   const size_t es = m->es;
   c.chk(embed_launch(m->ids, m->maxpos, p0, S, B, m->embed, d, m->V, m->sX, m->dt, c.st), "embed");
+  const bool fold = m->dt == 1 && R <= GEMV_MAX_ROWS;  // norms inside the skinny products
   for (int l = 0; l <= m->t0; ++l) {
-    c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_attn[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
-    qkv(c, m->sU, l, R, S, p0, m->sQKV, m->sQ, m->cap_s);
+    if (!fold)
+      c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_attn[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
+    qkv(c, m->sU, l, R, S, p0, m->sQKV, m->sQ, m->cap_s, fold ? m->sX : nullptr, m->g_attn[l]);
     AttnArgs a;
     memset(&a, 0, sizeof(a));
     a.q = m->sQ; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
@@ -314,11 +328,14 @@ void span_pass(Ctx& c, int64_t p0, int S) {
     g.R = m->sX; g.ldr = d;
     c.gemm(EPI_ADD, true, g);
     if (l == m->t0) break;
-    c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_mlp[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
+    if (!fold)
+      c.chk(rmsnorm_fwd_launch(m->sX, R, d, m->g_mlp[l], m->cfg.norm_eps, m->sU, m->sR, m->dt, c.st), "norm");
     // up-projection with the activation in its epilogue (SwiGLU weights are
     // stored with gate / up rows interleaved in blocks of 32)
     const int h = m->h, zw = m->mg * h;
-    c.gemm(m->mg == 2 ? EPI_SWIGLU : EPI_GELU, false, ga(m->sU, d, m->wgu_t[l], d, m->sA, h, R, zw, d));
+    GemmArgs gu = ga(m->sU, d, m->wgu_t[l], d, m->sA, h, R, zw, d);
+    if (fold) fold_norm(gu, m->sX, d, 0, m->g_mlp[l], m->cfg.norm_eps);
+    c.gemm(m->mg == 2 ? EPI_SWIGLU : EPI_GELU, false, gu);
     g = ga(m->sA, h, m->wd_t[l], h, m->sX, d, R, d, h);
     g.R = m->sX; g.ldr = d;
     c.gemm(EPI_ADD, true, g);
@@ -335,6 +352,10 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
   const int hf = m->hf, ht = m->ht, mg = m->mg, zw = mg * hf;
   const size_t es = m->es;
   const float eps = m->cfg.norm_eps;
+  // forward-only passes of few rows take their norms inside the skinny
+  // products (the backward would read the norms' outputs)
+  const bool fold_r = !bwd && m->dt == 1 && R <= GEMV_MAX_ROWS;  // one product over all rows
+  const bool fold_m = !bwd && m->dt == 1 && M <= GEMV_MAX_ROWS;  // batched over the sequences
   const int64_t sgu = (int64_t)zw * d, sd = (int64_t)d * hf;        // per-seq fast strides
   const int64_t smgu = (int64_t)mg * ht * d, smd = (int64_t)d * ht;  // per-seq master strides
 
@@ -344,8 +365,8 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     float* y = m->tx[j];  // block t0: the residual after its attention
     if (j >= 1) {
       y = m->ty[j];
-      c.chk(rmsnorm_fwd_launch(m->tx[j], R, d, m->g_attn[l], eps, m->tU, m->tr1[j], m->dt, c.st), "norm");
-      qkv(c, m->tU, l, R, M, P0, m->tQKV, m->tq[j], m->cap_t);
+      if (!fold_r) c.chk(rmsnorm_fwd_launch(m->tx[j], R, d, m->g_attn[l], eps, m->tU, m->tr1[j], m->dt, c.st), "norm");
+      qkv(c, m->tU, l, R, M, P0, m->tQKV, m->tq[j], m->cap_t, fold_r ? m->tx[j] : nullptr, m->g_attn[l]);
       AttnArgs a;
       memset(&a, 0, sizeof(a));
       a.q = m->tq[j]; a.ldq = HD; a.kc = m->kc[l]; a.vc = m->vc[l]; a.ldk = HD;
@@ -365,9 +386,10 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       g.R = m->tx[j]; g.ldr = d;
       c.gemm(EPI_ADD, true, g);
     }
-    c.chk(rmsnorm_fwd_launch(y, R, d, m->g_mlp[l], eps, m->tn[j], m->tr2[j], m->dt, c.st), "norm");
+    if (!fold_m) c.chk(rmsnorm_fwd_launch(y, R, d, m->g_mlp[l], eps, m->tn[j], m->tr2[j], m->dt, c.st), "norm");
     GemmArgs g = ga(m->tn[j], d, m->f_gu[j], d, m->tz[j], zw, M, zw, d);
     g.sA = (int64_t)M * d; g.sB = sgu; g.sC = (int64_t)M * zw;
+    if (fold_m) fold_norm(g, y, d, (int64_t)M * d, m->g_mlp[l], eps);
     c.gemm(EPI_STORE, true, g, B);
     c.chk(act_fwd_launch(m->tz[j], R, hf, zw, mg == 2, m->ta[j], hf, m->dt, c.st), "act");
     float* xo = (j + 1 < m->nt) ? m->tx[j + 1] : m->txL;
@@ -376,8 +398,12 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     g.R = y; g.ldr = d; g.sR = (int64_t)M * d;
     c.gemm(EPI_ADD, true, g, B);
   }
-  c.chk(rmsnorm_fwd_launch(m->txL, R, d, m->gfin, eps, m->tf, m->trf, m->dt, c.st), "norm");
-  c.gemm(EPI_STORE, true, ga(m->tf, d, m->wout_t, d, m->tlog, V, R, V, d));
+  if (!fold_r) c.chk(rmsnorm_fwd_launch(m->txL, R, d, m->gfin, eps, m->tf, m->trf, m->dt, c.st), "norm");
+  {
+    GemmArgs g = ga(m->tf, d, m->wout_t, d, m->tlog, V, R, V, d);
+    if (fold_r) fold_norm(g, m->txL, d, 0, m->gfin, eps);
+    c.gemm(EPI_STORE, true, g);
+  }
   {
     CEArgs a;
     memset(&a, 0, sizeof(a));
