@@ -642,7 +642,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
 // group keeps its own online softmax (max in log2 units, sum, 128 output
 // columns over its 16 lanes); the groups are merged through LDS at the end.
 // Outputs as the tile kernels: o and lse, or the split partials (normalised
-// O, max, sum) that attn_combine_kernel merges.
+// O, max, sum) that attn_combine_head_kernel merges.
 constexpr int ONE_MAXM = 8;  // queries per sequence served by this kernel
 constexpr int ONE_U = 4;     // keys per group with loads in flight
 __global__ __launch_bounds__(256) void attn_fwd_one_kernel(AttnArgs a) {
