@@ -296,6 +296,21 @@ TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, 
         const int e1 = ((cb % hd) / 64) * 32 + (lane & 31);
         OutT* const qb = reinterpret_cast<OutT*>(ro.q) + h * hd + e1;
         OutT* const cb_ = reinterpret_cast<OutT*>(part == 1 ? ro.kc : ro.vc) + h * hd + e1;
+        // the block's 16 cos/sin pairs are loaded before any store: a load
+        // after a store that may alias it cannot be hoisted, which would make
+        // the 16 loads 16 round trips one after the other
+        const bool rot = part < 2 && ro.tab;
+        float2 cs[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int row = rb + rr;
+          cs[r] = make_float2(1.f, 0.f);
+          if (rot && !(CHECK && row >= p.M)) {
+            const int pos = runs ? pos0 + rr : (int)ro.p0 + row % S;
+            cs[r] = ro.tab[(int64_t)pos * half + e1];
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row within the block
@@ -312,12 +327,12 @@ TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, 
             pos = (int)ro.p0 + row % S;
             slot = pos % cap;
           }
+          (void)pos;
           float y1 = acc[i][2 * jj][r], y2 = acc[i][2 * jj + 1][r];
-          if (part < 2 && ro.tab) {
-            const float2 cs = ro.tab[(int64_t)pos * half + e1];
+          if (rot) {
             const float a = y1, b = y2;
-            y1 = a * cs.x - b * cs.y;
-            y2 = a * cs.y + b * cs.x;
+            y1 = a * cs[r].x - b * cs[r].y;
+            y2 = a * cs[r].y + b * cs[r].x;
           }
           OutT* dst = part == 0 ? qb + (int64_t)row * ro.ldq : cb_ + sq * ro.seq_stride + (int64_t)slot * HDm;
           dst[0] = from_f32<OutT>(y1);
