@@ -781,41 +781,49 @@ __global__ void attn_combine_kernel(AttnArgs a) {
 }
 
 // The same merge for a few rows (decode): one wave per (row, head), so the
-// split partials of a row are read by many workgroups at once.
+// split partials of a row are read by many workgroups at once. Every load
+// (split maxima, sums and this thread's partial rows) is issued before any
+// arithmetic, in one round trip.
 template <typename T>
 __global__ __launch_bounds__(64) void attn_combine_head_kernel(AttnArgs a) {
   const int64_t row = blockIdx.x;  // s*M + q
   const int h = blockIdx.y;
   const int s = row / a.M, q = row % a.M;
-  float m = NEG_BIG;
-  for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part_m[(((int64_t)sp * a.B + s) * a.H + h) * a.M + q]);
-  float wgt[16];
-  float wsum = 0.f;
+  for (int c0 = 0; c0 < a.hd; c0 += 64 * 4) {
+    const int c = c0 + threadIdx.x * 4;
+    const bool col = c < a.hd;
+    float pm[16], pl[16];
+    float4 v[16];
 #pragma unroll
-  for (int sp = 0; sp < 16; ++sp) {
-    wgt[sp] = 0.f;
-    if (sp < a.nsplit) {
-      const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * a.M + q;
-      wgt[sp] = a.part_l[li] * ex2(a.part_m[li] - m);
-      wsum += wgt[sp];
+    for (int sp = 0; sp < 16; ++sp) {
+      pm[sp] = NEG_BIG;
+      pl[sp] = 0.f;
+      v[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (sp < a.nsplit) {
+        const int64_t li = (((int64_t)sp * a.B + s) * a.H + h) * a.M + q;
+        pm[sp] = a.part_m[li];
+        pl[sp] = a.part_l[li];
+        if (col) v[sp] = *reinterpret_cast<const float4*>(a.part_o + ((int64_t)sp * a.B * a.M + row) * a.ldo + h * a.hd + c);
+      }
     }
-  }
-  const float inv = 1.f / wsum;
-  if (threadIdx.x == 0) a.lse[((int64_t)s * a.H + h) * a.M + q] = m * LN2 + logf(wsum);
-  for (int c = threadIdx.x * 4; c < a.hd; c += 64 * 4) {
+    float m = NEG_BIG;
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp) m = fmaxf(m, pm[sp]);
+    float wsum = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sp = 0; sp < 16; ++sp) {
-      if (sp < a.nsplit) {
-        const float4 v =
-            *reinterpret_cast<const float4*>(a.part_o + ((int64_t)sp * a.B * a.M + row) * a.ldo + h * a.hd + c);
-        const float w = wgt[sp] * inv;
-        acc[0] += w * v.x; acc[1] += w * v.y; acc[2] += w * v.z; acc[3] += w * v.w;
-      }
+      const float w = pl[sp] * ex2(pm[sp] - m);  // 0 for the absent splits
+      wsum += w;
+      acc[0] += w * v[sp].x; acc[1] += w * v[sp].y; acc[2] += w * v[sp].z; acc[3] += w * v[sp].w;
     }
-    T* o = reinterpret_cast<T*>(a.o) + row * a.ldo + h * a.hd + c;
+    const float inv = 1.f / wsum;
+    if (c0 == 0 && threadIdx.x == 0) a.lse[((int64_t)s * a.H + h) * a.M + q] = m * LN2 + logf(wsum);
+    if (col) {
+      T* o = reinterpret_cast<T*>(a.o) + row * a.ldo + h * a.hd + c;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = from_f32<T>(acc[k]);
+      for (int k = 0; k < 4; ++k) o[k] = from_f32<T>(acc[k] * inv);
+    }
   }
 }
 
