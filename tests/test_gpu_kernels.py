@@ -340,7 +340,8 @@ def attn_case(dtype, B, M, H, hd, pos0, window, seed=0):
                                                       (1, 1, 2, 2000, 1024, 8), (1, 100, 2, 0, 128, 2),
                                                       (1, 1, 3, 4000, 2048, 16), (2, 33, 2, 3000, 2048, 16),
                                                       (2, 5, 3, 3000, 2048, 4), (1, 8, 2, 70, 1024, 1),
-                                                      (1, 3, 2, 200, 64, 2), (1, 1, 2, 0, 64, 1)])
+                                                      (1, 3, 2, 200, 64, 2), (1, 1, 2, 0, 64, 1),
+                                                      (1, 2, 2, 10, 64, 4), (2, 1, 2, 40, 128, 16)])
 def test_attention_fwd_bwd(dtype, hd, dl, B, M, H, pos0, window, nsplit):
     """dl: forward kernels of bf16 head dim 128 (1 default: direct-to-LDS tiles,
     the one-query kernel for at most 8 queries; 2 direct-to-LDS tiles for any
