@@ -45,11 +45,13 @@ Readings of points the pages leave open (each is listed in the design doc):
 
 bf16 operand mode (static_losses(..., operands="bf16")): the bf16 runs compute
 every matrix product from bf16 operands with wider accumulation. In this mode
-the forward rounds each operand that is not a stored weight (normalised
-activations, q / k after RoPE, v, the unnormalised softmax weights, the
-attention output, the MLP activation, the final normalised state) to bf16 -
-an fp32 value rounded to nearest even - and keeps everything else in fp64.
-It isolates what bf16 operands alone do to the losses; it is not used for
+the forward rounds each operand of a matrix product that is not a stored
+weight to bf16 - an fp32 value rounded to nearest even - and keeps everything
+else in fp64. Those operands are the normalised activations, q and k after
+RoPE, v, the attention weights P = softmax(q k^T / sqrt(hd)) (the operand of
+the P v product), the attention output, the MLP activation and the final
+normalised state. It measures what bf16 operands alone do to the losses (a
+diagnostic; no parity bound is derived from it) and is not used for
 gradients.
 """
 from __future__ import annotations
@@ -148,8 +150,8 @@ def window_attention(q, K, V, qpos, kpos, window, rnd=None):
     """Softmax attention per head restricted to the window.
 
     q [m][H][hd], K/V [n][H][hd]; returns o [m][H][hd] and P [H][m][n].
-    With rnd (bf16 operand mode) the product with V takes rnd(exp(s - max))
-    and the normalisation by the exact sum follows it; P is then None.
+    With rnd (bf16 operand mode) the product with V takes rnd(P); P is then
+    None.
     """
     hd = q.shape[-1]
     mask = window_mask(qpos, kpos, window)
@@ -158,10 +160,9 @@ def window_attention(q, K, V, qpos, kpos, window, rnd=None):
     s = np.where(mask[None], s, -np.inf)
     s = s - s.max(axis=-1, keepdims=True)
     e = np.exp(s)
-    if rnd is not None:
-        o = ((rnd(e) @ Vh) / e.sum(axis=-1, keepdims=True)).transpose(1, 0, 2)
-        return o, None
     P = e / e.sum(axis=-1, keepdims=True)
+    if rnd is not None:
+        return (rnd(P) @ Vh).transpose(1, 0, 2), None
     o = (P @ Vh).transpose(1, 0, 2)                           # [m][H][hd]
     return o, P
 

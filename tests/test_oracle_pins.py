@@ -197,8 +197,9 @@ def torch_forward(cfg, w, ids, p0, Kc, Vc, Wfast, bf=False):
     """Independent forward from torch library ops; returns logits, new K/V.
 
     bf: round every activation operand of a matrix product with torch's own
-    bf16 cast (through fp32), attention written out so that the unnormalised
-    softmax weights can be rounded (forward only)."""
+    bf16 cast (through fp32), attention written out so that its weights (the
+    softmax probabilities, operand of the product with V) can be rounded
+    (forward only)."""
     rb = (lambda a: a.float().bfloat16().double()) if bf else (lambda a: a)
     d, H, hd, eps, win = cfg["d_model"], cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"], cfg["window"]
     t0 = cfg["n_blocks"] - cfg["n_ttt_blocks"]
@@ -240,8 +241,7 @@ def torch_forward(cfg, w, ids, p0, Kc, Vc, Wfast, bf=False):
         if bf:
             sc = q.transpose(0, 1) @ Kw.transpose(0, 1).transpose(1, 2) / math.sqrt(hd)
             sc = sc.masked_fill(~mask, float("-inf"))
-            e = torch.exp(sc - sc.amax(-1, keepdim=True))
-            a = (rb(e) @ Vw.transpose(0, 1)) / e.sum(-1, keepdim=True)
+            a = rb(torch.softmax(sc, dim=-1)) @ Vw.transpose(0, 1)
         else:
             a = F.scaled_dot_product_attention(q.transpose(0, 1), Kw.transpose(0, 1), Vw.transpose(0, 1),
                                                attn_mask=mask)
