@@ -28,6 +28,12 @@
  *     calls except ttt_reset / ttt_model_destroy / ttt_last_error return
  *     TTT_ESTATE until ttt_reset succeeds. ttt_last_error() returns a
  *     thread-local message for the last failure.
+ *   - Non-finite values: the cross-entropy kernel raises a device status flag
+ *     when a logit row's log-sum-exp or a loss is not finite (the fast
+ *     weights or the initial weights then hold non-finite values). The next
+ *     ttt_prefill / ttt_decode reads the flag, poisons the model and returns
+ *     TTT_ESTATE; the losses of the call that produced them are already in
+ *     the caller's buffer.
  *   - Matrices passed in are row-major [in][out] (y = x @ W).
  */
 #ifndef TTT_H
@@ -121,8 +127,11 @@ typedef struct ttt_model ttt_model;
  * caller's weight buffers may be freed afterwards. Every sequence starts from
  * a fresh copy of the initial fast weights (review, Algorithm 1 step 1).
  * Errors: TTT_EINVAL (k < b, d_model or n_heads or head_dim < 1, n_ttt_blocks
- * not in [1, n_blocks], odd head_dim with rope, NULL pointers), TTT_ENOMEM,
- * TTT_EHIP. On error *out is NULL. */
+ * not in [1, n_blocks], odd head_dim with rope, mini_batch not a multiple of
+ * 8 (bf16) or 4 (fp32) - the weight-gradient products contract over the b
+ * positions of a chunk -, NULL pointers), TTT_ENOMEM (a device allocation
+ * failed, or the model would need more than max_device_bytes), TTT_EHIP.
+ * On error *out is NULL and nothing stays allocated. */
 int ttt_model_create(const ttt_config* cfg, const ttt_weights* init, void* stream,
                      ttt_model** out);
 
@@ -137,9 +146,13 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* init, void* strea
  * [c*b, (c+1)*b) has all of its labels (ids up to (c+1)*b), the library runs
  * the chunk's backward and SGD step. Positions of an incomplete chunk are
  * scored at the current W and wait for the rest of their chunk.
- * Errors: TTT_EINVAL (n < 1, stream would exceed max_positions; token ids are
- * not read on the host, ids outside [0, V) are clamped by the kernels),
- * TTT_ESTATE (poisoned), TTT_EHIP. */
+ * Validation reads the n new ids of every sequence back to the host, so the
+ * call waits for `stream` to reach it (earlier work on `stream`, such as the
+ * kernel that wrote `tokens`, completes first); everything after the check is
+ * enqueued asynchronously.
+ * Errors: TTT_EINVAL (n < 1, stream would exceed max_positions, an id outside
+ * [0, vocab): nothing is enqueued and the model is unchanged), TTT_ESTATE
+ * (poisoned, or an earlier call produced non-finite logits), TTT_EHIP. */
 int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t n, float* losses, void* stream);
 
 /* Greedy decode with periodic adaptation (review, section 7, Algorithm 3;
@@ -150,13 +163,20 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t n, float* losses, v
  * chunk's SGD step runs before the next position is computed.
  * tokens_out: device int32 [batch][n_new]. losses: device float
  * [batch][n_new] or NULL; entry i = -log p(chosen id i).
- * Errors: TTT_ESTATE (no prefill yet, or poisoned), TTT_EINVAL (n_new < 1,
- * exceeds max_positions), TTT_EHIP. */
+ * Waits for `stream` to reach the call (to read the non-finite status flag);
+ * the generation itself is enqueued asynchronously. A row whose logits have
+ * no finite maximum yields id 0 and raises the status flag.
+ * Errors: TTT_ESTATE (no prefill yet, poisoned, or an earlier call produced
+ * non-finite logits), TTT_EINVAL (n_new < 1, exceeds max_positions),
+ * TTT_EHIP. */
 int ttt_decode(ttt_model* m, int64_t n_new, int32_t* tokens_out, float* losses, void* stream);
 
 /* Copy the current fp32 fast weights of one trainable matrix of one sequence
  * into dst (device float, row-major [in][out]: UP/GATE [d][ttt_hidden],
- * DOWN [ttt_hidden][d]). Async on `stream`. Reflects every completed chunk.
+ * DOWN [ttt_hidden][d]). Async on `stream`. Reflects every completed chunk:
+ * the adapted weights W that the review's section 7, Algorithm 1 returns
+ * after its last update (the summary's W_{T/b}, "Test-Time Training (Inner
+ * Loop)"); an incomplete chunk has not changed them.
  * Errors: TTT_EINVAL (seq out of range, block not a tail block, GATE without
  * SwiGLU, dst NULL). */
 int ttt_get_weights(const ttt_model* m, int32_t seq, int32_t block, int32_t mat, float* dst,

@@ -41,6 +41,24 @@ int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N
                void* C2, int64_t ldc2, int64_t sC2, const float* R, int64_t ldr, int64_t sR, float* Wm, int64_t ldw,
                int64_t sW, float lr, uint32_t sr_seed, int32_t batch, float* ws, int64_t ws_elems, void* stream);
 
+/* bf16 Q/K/V projection of an attention block with the rotary embedding
+ * (RoPE: pairs (i, i + hd/2) rotated by angle pos * theta^(-2i/hd); the
+ * positions are absolute, as the sliding-window attention of the technical
+ * review's section 5 keys its cache by position) applied to the fp32
+ * accumulators, and the split into q and the K/V ring caches.
+ * A: [rows][K] bf16 (ld lda); row r = s*S + i is position p0 + i of
+ * sequence s. Bp: [3*H*hd][K] bf16, the rows (output columns) of W_q, W_k,
+ * W_v (each [K][H*hd] as y = x W) transposed, each head's hd rows permuted
+ * in 32-row blocks into the order [0, nb/2, 1, nb/2 + 1, ...] with
+ * nb = hd/32 (hd a multiple of 64). tab: device float2 [p0 + S][hd/2]
+ * (cos, sin) of the angles, or NULL for no rotation. Outputs (bf16, each
+ * rounded once after the rotation): q [rows][H*hd]; k and v of position p of
+ * sequence s at kc / vc + s*cap*H*hd + (p % cap)*H*hd (cap a multiple of 64,
+ * >= S). */
+int ttt_k_qkv_rope(int32_t rows, int32_t S, int32_t H, int32_t hd, int32_t K, const void* A, int64_t lda,
+                   const void* Bp, const void* tab, int64_t p0, void* q, void* kc, void* vc, int32_t cap,
+                   void* stream);
+
 /* Test hook: force the GEMM block tile (0 automatic, 1 = 256x256, 2 = 256x128,
  * 3 = 128x128, 4 = 256x256 with operands loaded straight into a two-stage LDS
  * ring (bf16, K a multiple of 64, not epi 2), 5 = the same with a four-stage

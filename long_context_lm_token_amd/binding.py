@@ -79,6 +79,8 @@ def load():
     lib.ttt_k_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
                                c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
                                c_f32, ctypes.c_uint32, c_i32, c_vp, c_i64, c_vp]
+    lib.ttt_k_qkv_rope.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp,
+                                   c_vp, c_i32, c_vp]
     lib.ttt_k_gemm_tile.argtypes = [c_i32]
     lib.ttt_k_gemm_tile.restype = None
     lib.ttt_k_gemm_operands.argtypes = [c_i32]

@@ -366,9 +366,11 @@ __global__ __launch_bounds__(CE_NT) void ce_kernel(CEArgs a) {
     label = label < 0 ? 0 : (label >= a.V ? a.V - 1 : label);
   }
   if (threadIdx.x == 0) {
+    const float loss = has_label ? lse - z[label] : 0.f;
+    if (a.status && !(isfinite(lse) && isfinite(loss))) a.status[0] = 1;
     if (has_label && a.losses) {
       const int64_t li = pos - a.loss_base;
-      if (li >= 0 && li < a.loss_n) a.losses[s * a.loss_ld + li] = lse - z[label];
+      if (li >= 0 && li < a.loss_n) a.losses[s * a.loss_ld + li] = loss;
     }
     if (pos == a.n_ids - 1 && a.last_lse) {
       a.last_lse[s] = lse;
@@ -464,12 +466,16 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
     p[i] = v;
 }
 
-__global__ void decode_emit_kernel(const int32_t* next, const float* lse, const float* mx, int B,
+__global__ void decode_emit_kernel(const int32_t* next, const float* lse, const float* mx, int B, int vocab,
                                    int32_t* ids, int64_t ids_ss, int64_t pos, int32_t* out,
-                                   int64_t out_ld, int64_t i, float* losses) {
+                                   int64_t out_ld, int64_t i, float* losses, int32_t* status) {
   const int s = threadIdx.x;
   if (s >= B) return;
-  const int32_t t = next[s];
+  int32_t t = next[s];
+  if (t < 0 || t >= vocab) {
+    t = 0;
+    if (status) status[0] = 2;
+  }
   ids[s * ids_ss + pos] = t;
   if (out) out[s * out_ld + i] = t;
   if (losses) losses[s * out_ld + i] = lse[s] - mx[s];
@@ -620,10 +626,10 @@ hipError_t fill_f32_launch(float* p, int64_t n, float v, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t decode_emit_launch(const int32_t* next, const float* lse, const float* mx, int B, int32_t* ids,
-                              int64_t ids_ss, int64_t pos, int32_t* out, int64_t out_ld, int64_t i,
-                              float* losses, hipStream_t st) {
-  hipLaunchKernelGGL(decode_emit_kernel, dim3(1), dim3(((B + 63) / 64) * 64), 0, st, next, lse, mx, B, ids,
-                     ids_ss, pos, out, out_ld, i, losses);
+hipError_t decode_emit_launch(const int32_t* next, const float* lse, const float* mx, int B, int vocab,
+                              int32_t* ids, int64_t ids_ss, int64_t pos, int32_t* out, int64_t out_ld, int64_t i,
+                              float* losses, int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(decode_emit_kernel, dim3(1), dim3(((B + 63) / 64) * 64), 0, st, next, lse, mx, B, vocab, ids,
+                     ids_ss, pos, out, out_ld, i, losses, status);
   return hipGetLastError();
 }

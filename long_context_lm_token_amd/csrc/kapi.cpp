@@ -47,6 +47,22 @@ int ttt_k_gemm(int32_t dtype, int32_t epi, int32_t out_f32, int32_t M, int32_t N
   return kdone(gemm_launch(g, dtype, epi, out_f32 != 0, batch, ws, ws_elems, static_cast<hipStream_t>(stream)));
 }
 
+int ttt_k_qkv_rope(int32_t rows, int32_t S, int32_t H, int32_t hd, int32_t K, const void* A, int64_t lda,
+                   const void* Bp, const void* tab, int64_t p0, void* q, void* kc, void* vc, int32_t cap,
+                   void* stream) {
+  if (rows < 1 || S < 1 || rows % S || H < 1 || hd % 64 || K < 8 || K % 8 || lda < K || cap < S || cap % 64 ||
+      p0 < 0 || !A || !Bp || !q || !kc || !vc)
+    return kfail(TTT_EINVAL, "bad rotary Q/K/V arguments");
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  const int64_t HD = (int64_t)H * hd;
+  g.A = A; g.lda = lda; g.B = Bp; g.ldb = K; g.M = rows; g.N = (int)(3 * HD); g.K = K;
+  g.rope.q = q; g.rope.kc = kc; g.rope.vc = vc; g.rope.tab = static_cast<const float2*>(tab);
+  g.rope.ldq = HD; g.rope.seq_stride = (int64_t)cap * HD; g.rope.p0 = p0; g.rope.cap = cap; g.rope.S = S;
+  g.rope.H = H; g.rope.hd = hd;
+  return kdone(gemm_launch(g, 1, EPI_ROPE, false, 1, nullptr, 0, static_cast<hipStream_t>(stream)));
+}
+
 void ttt_k_gemm_tile(int32_t cfg) { gemm_force_tile(cfg); }
 
 void ttt_k_gemm_operands(int32_t mn) { g_gemm_mn = mn != 0; }

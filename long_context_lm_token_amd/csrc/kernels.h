@@ -127,6 +127,7 @@ struct CEArgs {
   void* dz; float dz_scale;            // NULL: no gradient
   float* losses; int64_t loss_base, loss_ld, loss_n;  // losses[s*loss_ld + (p - loss_base)]
   float* last_lse; float* last_max; int32_t* last_arg;  // per sequence, row of position n_ids-1
+  int32_t* status;                     // if set: *status = 1 when a row's lse or loss is not finite
 };
 hipError_t ce_launch(const CEArgs& a, int dt, hipStream_t st);
 
@@ -137,6 +138,9 @@ hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, in
 hipError_t copy_rows_f32_launch(const float* src, int64_t src_seq_stride, float* dst,
                                 int64_t dst_seq_stride, int S, int d, int B, hipStream_t st);
 hipError_t fill_f32_launch(float* p, int64_t n, float v, hipStream_t st);
-hipError_t decode_emit_launch(const int32_t* next, const float* lse, const float* mx, int B,
+// Appends the greedy ids next[s] at position pos; an id outside [0, vocab)
+// (the argmax of a row with no finite maximum) is written as 0 and sets
+// *status |= 2.
+hipError_t decode_emit_launch(const int32_t* next, const float* lse, const float* mx, int B, int vocab,
                               int32_t* ids, int64_t ids_seq_stride, int64_t pos, int32_t* tokens_out,
-                              int64_t out_ld, int64_t i, float* losses, hipStream_t st);
+                              int64_t out_ld, int64_t i, float* losses, int32_t* status, hipStream_t st);

@@ -93,6 +93,9 @@ struct ttt_model {
   int64_t chunk = 0;
   float *last_lse = nullptr, *last_max = nullptr;
   int32_t* last_arg = nullptr;
+  // device status word: non-zero once a logit row was non-finite (CE) or a
+  // greedy id was not a valid id; read at the start of the next call
+  int32_t* status = nullptr;
 
   // span-pass workspace (rows = B * span)
   float *sX = nullptr, *sR = nullptr, *sL = nullptr;
@@ -412,6 +415,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     a.dz = bwd ? m->tdz : nullptr; a.dz_scale = 1.f / m->cfg.mini_batch;
     a.losses = losses; a.loss_base = loss_base; a.loss_ld = loss_n; a.loss_n = loss_n;
     a.last_lse = m->last_lse; a.last_max = m->last_max; a.last_arg = m->last_arg;
+    a.status = m->status;
     hipEvent_t e0;
     prof_begin(m, TTT_PROF_CE, c.st, &e0);
     c.chk(ce_launch(a, m->dt, c.st), "ce");
@@ -541,6 +545,31 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
   c.order(m->side, c.st, m->ev[2 * m->nt]);
 }
 
+// Wait for `st` and read the status word the kernels of earlier calls set.
+// A non-finite logit row means the fast weights (or the inputs) hold
+// non-finite values: the model is poisoned until ttt_reset.
+int check_status(ttt_model* m, hipStream_t st, std::vector<int32_t>* ids_out = nullptr,
+                 const int32_t* ids_dev = nullptr, int64_t n_ids = 0) {
+  int32_t flag = 0;
+  hipError_t e = hipSuccess;
+  if (ids_out) {
+    ids_out->resize((size_t)n_ids);
+    e = hipMemcpyAsync(ids_out->data(), ids_dev, n_ids * 4, hipMemcpyDeviceToHost, st);
+  }
+  if (e == hipSuccess) e = hipMemcpyAsync(&flag, m->status, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TTT_EHIP, std::string("reading the ids / status: ") + hipGetErrorString(e));
+  }
+  if (flag) {
+    m->poisoned = true;
+    return fail(TTT_ESTATE, flag & 2 ? "an earlier call produced a greedy id from non-finite logits; call ttt_reset"
+                                     : "an earlier call produced non-finite logits; call ttt_reset");
+  }
+  return TTT_OK;
+}
+
 int finish(Ctx& c) {
   if (c.err != hipSuccess) {
     c.m->poisoned = true;
@@ -556,6 +585,11 @@ int validate(const ttt_config* c) {
   if (c->n_ttt_blocks < 1 || c->n_ttt_blocks > c->n_blocks) return fail(TTT_EINVAL, "n_ttt_blocks out of range");
   if (c->window < c->mini_batch) return fail(TTT_EINVAL, "window k must be >= mini_batch b");
   if (c->mini_batch < 1) return fail(TTT_EINVAL, "mini_batch must be >= 1");
+  // the weight-gradient products contract over the chunk's b positions (K = b)
+  if (c->dtype == TTT_BF16 && c->mini_batch % 8)
+    return fail(TTT_EINVAL, "mini_batch must be a multiple of 8 for bf16 (K of the weight-gradient products)");
+  if (c->dtype == TTT_FP32 && c->mini_batch % 4)
+    return fail(TTT_EINVAL, "mini_batch must be a multiple of 4 for fp32 (K of the weight-gradient products)");
   if (c->dtype != TTT_FP32 && c->dtype != TTT_BF16) return fail(TTT_EINVAL, "dtype");
   if (c->mlp_kind != TTT_GELU && c->mlp_kind != TTT_SWIGLU) return fail(TTT_EINVAL, "mlp_kind");
   if (c->batch < 1 || c->max_positions < 2) return fail(TTT_EINVAL, "batch / max_positions");
@@ -633,6 +667,7 @@ static int reset_state(ttt_model* m, hipStream_t st) {
     ck(hipMemsetAsync(m->kc[l], 0, n * m->es, st));
     ck(hipMemsetAsync(m->vc[l], 0, n * m->es, st));
   }
+  ck(hipMemsetAsync(m->status, 0, 4, st));
   ck(hipStreamSynchronize(st));
   m->n_ids = 0;
   m->chunk = 0;
@@ -741,6 +776,7 @@ int ttt_model_create(const ttt_config* cfg, const ttt_weights* w, void* stream, 
   if (cfg->rope) m->rope = static_cast<float2*>(A.get(m->maxpos * (m->hd / 2) * 8));
   m->last_lse = A.f32(B); m->last_max = A.f32(B);
   m->last_arg = static_cast<int32_t*>(A.get(B * 4));
+  m->status = static_cast<int32_t*>(A.get(4));
   // span workspace
   const int64_t Rs = (int64_t)B * span;
   m->sX = A.f32(Rs * d); m->sR = A.f32(Rs); m->sL = A.f32(Rs * m->H);
@@ -933,8 +969,19 @@ int ttt_prefill(ttt_model* m, const int32_t* tokens, int64_t n, float* losses, v
   if (!tokens || n < 1) return fail(TTT_EINVAL, "tokens NULL or n < 1");
   if (m->n_ids + n > m->maxpos) return fail(TTT_EINVAL, "stream would exceed max_positions");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Ctx c{m, st};
   const int B = m->cfg.batch, b = m->cfg.mini_batch;
+  {
+    // the new ids are read back once the caller's stream reaches this call,
+    // and checked before any work is enqueued
+    std::vector<int32_t> h;
+    int rc = check_status(m, st, &h, tokens, (int64_t)B * n);
+    if (rc) return rc;
+    for (size_t i = 0; i < h.size(); ++i)
+      if (h[i] < 0 || h[i] >= m->V)
+        return fail(TTT_EINVAL, "token id " + std::to_string(h[i]) + " of sequence " + std::to_string(i / n) +
+                                    " at new position " + std::to_string(i % n) + " is outside [0, vocab)");
+  }
+  Ctx c{m, st};
   const int64_t n0 = m->n_ids;
   c.chk(hipMemcpy2DAsync(m->ids + n0, m->maxpos * 4, tokens, n * 4, n * 4, B, hipMemcpyDeviceToDevice, st),
         "copy ids");
@@ -996,12 +1043,16 @@ int ttt_decode(ttt_model* m, int64_t n_new, int32_t* tokens_out, float* losses, 
   if (n_new < 1) return fail(TTT_EINVAL, "n_new < 1");
   if (m->n_ids + n_new > m->maxpos) return fail(TTT_EINVAL, "decode would exceed max_positions");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  {
+    int rc = check_status(m, st);
+    if (rc) return rc;
+  }
   Ctx c{m, st};
   const int B = m->cfg.batch, b = m->cfg.mini_batch;
   for (int64_t i = 0; i < n_new && c.err == hipSuccess; ++i) {
     const int64_t pos = m->n_ids;  // the new id lands here
-    c.chk(decode_emit_launch(m->last_arg, m->last_lse, m->last_max, B, m->ids, m->maxpos, pos, tokens_out, n_new,
-                             i, losses, st),
+    c.chk(decode_emit_launch(m->last_arg, m->last_lse, m->last_max, B, m->V, m->ids, m->maxpos, pos, tokens_out,
+                             n_new, i, losses, m->status, st),
           "emit");
     m->n_ids = pos + 1;
     const int64_t n_lab = m->n_ids - 1;

@@ -59,3 +59,27 @@ def test_config_validation_errors_without_gpu():
     assert not h.value
     assert lib.ttt_prefill(None, None, 1, None, None) == -1
     assert lib.ttt_decode(None, 1, None, None, None) == -1
+
+
+def test_mini_batch_alignment_rejected_at_create():
+    """A chunk size the weight-gradient products cannot contract over (K = b:
+    a multiple of 8 for bf16, of 4 for fp32) is rejected before any device
+    work, not at the first complete chunk."""
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.skip("library not built")
+    from long_context_lm_token_amd import synth
+    lib = bd.load()
+    w = bd.TTTWeights()
+    h = ctypes.c_void_p()
+    for dtype, b in [("bf16", 12), ("bf16", 1), ("fp32", 6), ("fp32", 1)]:
+        cfg = synth.get_config("tiny", dtype=dtype, mini_batch=b, window=64)
+        c = bd.make_config(cfg)
+        rc = lib.ttt_model_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(h))
+        assert rc == -1 and b"mini_batch" in lib.ttt_last_error(), (dtype, b, lib.ttt_last_error())
+        assert not h.value
+    # aligned sizes pass this check and fail later, on the NULL weights
+    for dtype, b in [("bf16", 40), ("fp32", 4)]:
+        c = bd.make_config(synth.get_config("tiny", dtype=dtype, mini_batch=b, window=64))
+        assert lib.ttt_model_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(h)) == -1
+        assert b"NULL" in lib.ttt_last_error()
+

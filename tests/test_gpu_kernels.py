@@ -463,3 +463,68 @@ def test_rmsnorm(dtype, d):
     np.testing.assert_allclose(r.cpu().numpy(), r_r[:, 0], rtol=1e-5)
     dx_r = O.rmsnorm_bwd(x, g, r_r, dn) + res0
     np.testing.assert_allclose(res.cpu().numpy(), dx_r, rtol=1e-4, atol=1e-4)
+
+
+# ------------------------ rotary Q/K/V projection -----------------------------
+
+def _permute_qkv_rows(Wt, H, hd):
+    """Rows [3*H*hd][K] of W^T, each head's hd rows reordered in 32-row blocks
+    as [0, nb/2, 1, nb/2 + 1, ...] (the layout ttt_k_qkv_rope documents)."""
+    nb = hd // 32
+    order = []
+    for b in range(nb // 2):
+        order += [b, nb // 2 + b]
+    out = np.empty_like(Wt)
+    for part in range(3):
+        for h in range(H):
+            base = (part * H + h) * hd
+            for k, b in enumerate(order):
+                out[base + 32 * k: base + 32 * k + 32] = Wt[base + 32 * b: base + 32 * b + 32]
+    return out
+
+
+@pytest.mark.parametrize("rows,S,p0,cap,rope", [(200, 100, 0, 192, True),     # tiles, two sequences
+                                                (3, 3, 131000, 64, True),     # skinny product, ring wrap
+                                                (256, 256, 4100, 320, True),  # slots wrap inside the block
+                                                (130, 130, 7, 192, False)])   # no rotation
+@pytest.mark.parametrize("hd", [64, 128])
+def test_qkv_rope_epilogue(rows, S, p0, cap, rope, hd):
+    """The Q/K/V product with RoPE applied to its fp32 accumulators and k / v
+    written to ring-cache slots, against the oracle's rope of the fp64
+    product (bf16 outputs rounded once)."""
+    lib = bd.load()
+    H, K, theta = 3, 256, 10000.0
+    HD = H * hd
+    B = rows // S
+    A, Ad = rnd((rows, K), 11, torch.bfloat16)
+    W, _ = rnd((K, 3 * HD), 12, torch.bfloat16, scale=0.05)
+    Bp = torch.as_tensor(_permute_qkv_rows(np.ascontiguousarray(W.T), H, hd), dtype=torch.float32)
+    Bp = Bp.to(torch.bfloat16).cuda()
+    tab = None
+    if rope:
+        ang = O.rope_angles(np.arange(p0 + S), hd, theta)
+        t = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+        tab = torch.as_tensor(t).cuda()
+    q = torch.zeros((rows, HD), dtype=torch.bfloat16, device="cuda")
+    kc = torch.full((B, cap, HD), 7.0, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((B, cap, HD), 7.0, dtype=torch.bfloat16, device="cuda")
+    bd.check(lib.ttt_k_qkv_rope(rows, S, H, hd, K, bd.ptr(Ad), K, bd.ptr(Bp), bd.ptr(tab), p0, bd.ptr(q),
+                                bd.ptr(kc), bd.ptr(vc), cap, bd.stream_ptr()), kernel=True)
+    sync()
+    z = A @ W
+    pos = np.tile(np.arange(p0, p0 + S), B)
+    qr = z[:, :HD].reshape(rows, H, hd)
+    kr = z[:, HD:2 * HD].reshape(rows, H, hd)
+    vr = z[:, 2 * HD:].reshape(rows, H, hd)
+    if rope:
+        qr, kr = O.rope(qr, pos, theta), O.rope(kr, pos, theta)
+    tol = 2 ** -8 * np.abs(z).max()
+    np.testing.assert_allclose(q.float().cpu().numpy(), qr.reshape(rows, HD), rtol=0, atol=tol)
+    kg, vg = kc.float().cpu().numpy(), vc.float().cpu().numpy()
+    slots = pos % cap
+    for s in range(B):
+        sl = slots[s * S:(s + 1) * S]
+        np.testing.assert_allclose(kg[s, sl], kr[s * S:(s + 1) * S].reshape(S, HD), rtol=0, atol=tol)
+        np.testing.assert_allclose(vg[s, sl], vr[s * S:(s + 1) * S].reshape(S, HD), rtol=0, atol=tol)
+        untouched = np.setdiff1d(np.arange(cap), sl)
+        assert (kg[s, untouched] == 7.0).all() and (vg[s, untouched] == 7.0).all()

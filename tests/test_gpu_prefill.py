@@ -188,3 +188,48 @@ def test_forward_only_is_the_static_model():
                 got = model.get_weights(s, l, name).cpu().numpy()
                 np.testing.assert_array_equal(got, wn[f"{l}.{name}"])
     model.close()
+
+
+@pytest.mark.parametrize("cuts", [None, [0, 37, 38, 150, 301]])
+def test_frozen_ring_wraps_over_many_spans_fp32(cuts):
+    """Frozen-prefix passes of 16 positions (about 19 of them, the prefix
+    stream running at most two ahead of the chunk loop) over a frozen-block
+    K/V ring of 64 slots (window 48 + span 16), which wraps four times; the
+    tail ring (48 + 16 -> 64 slots) wraps too. Whole stream and uneven pieces."""
+    cfg = small_cfg()
+    n = 301
+    model, wn, g, o, ors, _ = run_prefill(cfg, n, std=0.2, span=16, cuts=cuts)
+    check_losses(g, o, FP32_TOL["loss"])
+    compare_weights(cfg, model, ors, wn, FP32_TOL["w"], FP32_TOL["dw"])
+    model.close()
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_window_equal_to_chunk(dtype):
+    """k = b, the smallest window the method allows: the first query of a
+    chunk sees one key, the last sees b."""
+    kw = dict(window=16, mini_batch=16)
+    if dtype == "bf16":
+        kw.update(dtype="bf16", vocab=512, d_model=256, n_heads=2, head_dim=128, mlp_hidden=512,
+                  ttt_hidden=256, static_hidden=256, window=64, mini_batch=64, lr=0.05, span=32, period=256)
+    cfg = small_cfg(**kw)
+    b = cfg["mini_batch"]
+    model, wn, g, o, ors, _ = run_prefill(cfg, 5 * b + 3, std=0.2 if dtype == "fp32" else 0.05, span=b)
+    tol = FP32_TOL if dtype == "fp32" else BF16_TOL
+    check_losses(g, o, tol["loss"])
+    compare_weights(cfg, model, ors, wn, tol["w"], tol["dw"])
+    model.close()
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_bf16_chunk_not_a_multiple_of_64(hd):
+    """bf16 with b = 40: the weight-gradient products cannot read the
+    activations MN-major (b not a multiple of 64), so they take
+    token-contiguous transposed copies; ragged chunk-sized tiles everywhere."""
+    cfg = small_cfg(dtype="bf16", vocab=512, d_model=256, n_heads=256 // hd, head_dim=hd, mlp_hidden=512,
+                    ttt_hidden=256, static_hidden=256, n_blocks=4, n_ttt_blocks=2, window=80,
+                    mini_batch=40, lr=0.05, span=32, period=160)
+    model, wn, g, o, ors, _ = run_prefill(cfg, 6 * 40 + 7, batch=2, std=0.05, span=64)
+    check_losses(g, o, BF16_TOL["loss"])
+    compare_weights(cfg, model, ors, wn, BF16_TOL["w"], BF16_TOL["dw"])
+    model.close()
