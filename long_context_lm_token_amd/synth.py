@@ -46,6 +46,13 @@ CONFIGS = {
                mlp="swiglu", mlp_hidden=5632, n_ttt_blocks=6, ttt_hidden=2816,
                static_hidden=2816, rope=True, window=2048, mini_batch=1024, lr=0.01,
                dtype="bf16", seq_len=32768, span=512, period=4096),
+    # "TTT-E2E all layers MH" at the 125M shape: every block has its regular
+    # (static) GELU MLP of hidden 3072 beside a fast multi-head MLP of 12
+    # heads, each mapping its 64 columns through a hidden of 64 (768 in all)
+    "125m_mh": dict(_BASE, vocab=32000, d_model=768, n_blocks=12, n_heads=12, head_dim=64,
+                    mlp="gelu", mlp_hidden=3072, n_ttt_blocks=12, ttt_hidden=768,
+                    static_hidden=3072, mh_heads=12, rope=True, window=1024, mini_batch=512,
+                    lr=0.01, dtype="bf16", seq_len=8192, span=256, period=2048),
     # 3B-shape bf16 prefill, 1 x 128K
     "3b": dict(_BASE, vocab=32000, d_model=3072, n_blocks=28, n_heads=24, head_dim=128,
                mlp="swiglu", mlp_hidden=8192, n_ttt_blocks=7, ttt_hidden=4096,
@@ -87,10 +94,19 @@ def weight_shapes(cfg: dict) -> dict:
         shapes[p + "wo"] = (hq, d)
         shapes[p + "mlp_norm"] = (d,)
         h = cfg["ttt_hidden"] if l >= t0 else cfg["mlp_hidden"]
-        shapes[p + "w_up"] = (d, h)
-        if glu:
-            shapes[p + "w_gate"] = (d, h)
-        shapes[p + "w_down"] = (h, d)
+        nh = cfg.get("mh_heads", 0)
+        if l >= t0 and nh > 1:
+            # multi-head fast MLP: [head][in][out] per head
+            dh, hh = d // nh, h // nh
+            shapes[p + "w_up"] = (nh, dh, hh)
+            if glu:
+                shapes[p + "w_gate"] = (nh, dh, hh)
+            shapes[p + "w_down"] = (nh, hh, dh)
+        else:
+            shapes[p + "w_up"] = (d, h)
+            if glu:
+                shapes[p + "w_gate"] = (d, h)
+            shapes[p + "w_down"] = (h, d)
         if l >= t0:
             hs = cfg["static_hidden"]
             shapes[p + "s_up"] = (d, hs)

@@ -24,6 +24,13 @@ Context":
     (summary, "Implementation Details for TTT"; review section 6);
   * decoding updates only after a full mini-batch of generated tokens
     (summary, "Decoding Multiple Tokens"; review section 7, Algorithm 3).
+  * the "TTT-E2E all layers MH" variant (config key mh_heads > 1; summary,
+    "Alternative Derivation", step 4; review section 8, Table 1 and the
+    paragraph on splitting a width-D map into H heads): every block carries
+    a fast MLP split into mh_heads independent heads, each a small MLP from
+    its slice of the normalised state (width d / mh_heads, hidden
+    ttt_hidden / mh_heads) back to the same slice, trained by the same
+    next-token loss and inner update as the final design.
 
 Readings of points the pages leave open (each is listed in the design doc):
   * position p has input x_p and label x_{p+1}; chunk c is positions
@@ -42,6 +49,10 @@ Readings of points the pages leave open (each is listed in the design doc):
   * plain SGD (no momentum, decay or clipping), one joint step over all fast
     matrices; a chunk that is not yet complete is scored at the current W and
     never applied.
+  * all-layers MH variant: n_ttt_blocks = n_blocks; each block's fast
+    multi-head MLP sits beside its regular (static) MLP, sharing the pre-MLP
+    RMSNorm, both summed into the residual; per-head weights are stored
+    [head][in][out].
 
 bf16 operand mode (static_losses(..., operands="bf16")): the bf16 runs compute
 every matrix product from bf16 operands with wider accumulation. In this mode
@@ -213,6 +224,7 @@ class Oracle:
         L = cfg["n_blocks"]
         self.t0 = L - cfg["n_ttt_blocks"]
         self.glu = cfg["mlp"] == "swiglu"
+        self.mh = cfg.get("mh_heads", 0) > 1
         self.fast_names = ["w_up", "w_gate", "w_down"] if self.glu else ["w_up", "w_down"]
         self.reset()
 
@@ -278,7 +290,8 @@ class Oracle:
             nr = r(n)
             rec = None
             if l >= self.t0:
-                mt, mt_rec = self._mlp(nr, W[(l, "w_up")], W.get((l, "w_gate")), W[(l, "w_down")], r)
+                fast = self._mh_mlp if self.mh else self._mlp
+                mt, mt_rec = fast(nr, W[(l, "w_up")], W.get((l, "w_gate")), W[(l, "w_down")], r)
                 ms, ms_rec = self._mlp(nr, self.p(pre + "s_up"),
                                        self.p(pre + "s_gate") if self.glu else None,
                                        self.p(pre + "s_down"), r)
@@ -311,6 +324,47 @@ class Oracle:
             hg = None
             act = gelu(hu)
         return r(act) @ Wdown, dict(hu=hu, hg=hg, act=act)
+
+    def _mh_mlp(self, n, Wup, Wgate, Wdown, r=_same):
+        """Multi-head MLP: head i maps columns [i*dh, (i+1)*dh) of n through
+        its own MLP (Wup[i]: [dh][hh], Wdown[i]: [hh][dh]) back to the same
+        columns."""
+        nh, dh, _ = Wup.shape
+        m = n.shape[0]
+        nH = n.reshape(m, nh, dh).transpose(1, 0, 2)             # [nh][m][dh]
+        hu = nH @ Wup                                            # [nh][m][hh]
+        if self.glu:
+            hg = nH @ Wgate
+            act = hg * sigmoid(hg) * hu
+        else:
+            hg = None
+            act = gelu(hu)
+        out = (r(act) @ Wdown).transpose(1, 0, 2).reshape(m, nh * dh)
+        return out, dict(hu=hu, hg=hg, act=act)
+
+    def _mh_mlp_bwd(self, n, rec, Wup, Wgate, Wdown, dout, need_dn):
+        """Gradients of one multi-head MLP, head by head (the chain rule of
+        _mlp_bwd applied to each head's own slice)."""
+        nh, dh, _ = Wup.shape
+        m = n.shape[0]
+        nH = n.reshape(m, nh, dh).transpose(1, 0, 2)
+        doH = dout.reshape(m, nh, dh).transpose(1, 0, 2)         # [nh][m][dh]
+        dact = doH @ Wdown.transpose(0, 2, 1)                    # [nh][m][hh]
+        dWdown = rec["act"].transpose(0, 2, 1) @ doH             # [nh][hh][dh]
+        if self.glu:
+            hg, hu = rec["hg"], rec["hu"]
+            sg = sigmoid(hg)
+            dhu = dact * hg * sg
+            dhg = dact * hu * sg * (1.0 + hg * (1.0 - sg))
+            dWgate = nH.transpose(0, 2, 1) @ dhg                 # [nh][dh][hh]
+            dnH = (dhu @ Wup.transpose(0, 2, 1) + dhg @ Wgate.transpose(0, 2, 1)) if need_dn else None
+        else:
+            dhu = dact * gelu_grad(rec["hu"])
+            dWgate = None
+            dnH = (dhu @ Wup.transpose(0, 2, 1)) if need_dn else None
+        dWup = nH.transpose(0, 2, 1) @ dhu
+        dn = dnH.transpose(1, 0, 2).reshape(m, nh * dh) if need_dn else None
+        return dWup, dWgate, dWdown, dn
 
     def _mlp_bwd(self, n, rec, Wup, Wgate, Wdown, dout, need_dn):
         """Gradients of one MLP branch: (dWup, dWgate, dWdown, dn)."""
@@ -347,8 +401,9 @@ class Oracle:
             pre = f"{l}."
             # MLP sublayer: x_out = y + MLP_t(n) + MLP_s(n)
             need = l > self.t0
-            dWu, dWg, dWd, dn_t = self._mlp_bwd(rec["n"], rec["mt"], W[(l, "w_up")],
-                                                W.get((l, "w_gate")), W[(l, "w_down")], dx, need)
+            fast_bwd = self._mh_mlp_bwd if self.mh else self._mlp_bwd
+            dWu, dWg, dWd, dn_t = fast_bwd(rec["n"], rec["mt"], W[(l, "w_up")],
+                                           W.get((l, "w_gate")), W[(l, "w_down")], dx, need)
             G[(l, "w_up")] = dWu
             G[(l, "w_down")] = dWd
             if self.glu:
@@ -448,7 +503,8 @@ class Oracle:
         return loss
 
     def fast_weight(self, block, name):
-        """Current fast matrix in [in][out] layout (fp64)."""
+        """Current fast matrix in [in][out] layout (fp64); [head][in][out]
+        for the multi-head variant."""
         return self.W[(block, name)]
 
 

@@ -517,3 +517,123 @@ def test_elementary_ops_against_library():
             assert abs(np.sum(qr * kr) - ref) < 1e-12
         np.testing.assert_allclose(np.linalg.norm(qr), np.linalg.norm(q), rtol=1e-14)
         np.testing.assert_allclose(O.rope_inv(qr, [p], 10000.0), q, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# The "TTT-E2E all layers MH" variant (summary, "Alternative Derivation",
+# step 4; review section 8): a multi-head fast MLP in every block
+# --------------------------------------------------------------------------
+
+def mh_cfg(mlp="gelu", **kw):
+    base = dict(n_blocks=3, n_ttt_blocks=3, mh_heads=2, ttt_hidden=16, static_hidden=24, mlp=mlp)
+    base.update(kw)
+    return small_cfg(**base)
+
+
+def block_diag_weights(cfg, w):
+    """The same model with each multi-head fast matrix written as the dense
+    block-diagonal matrix it is (zeros between the heads)."""
+    dense = dict(w)
+    nh = cfg["mh_heads"]
+    for l in range(cfg["n_blocks"] - cfg["n_ttt_blocks"], cfg["n_blocks"]):
+        for name in ("w_up", "w_gate", "w_down"):
+            key = f"{l}.{name}"
+            if key not in w:
+                continue
+            blocks = w[key]
+            r, c = blocks.shape[1], blocks.shape[2]
+            full = np.zeros((nh * r, nh * c), dtype=blocks.dtype)
+            for h in range(nh):
+                full[h * r:(h + 1) * r, h * c:(h + 1) * c] = blocks[h]
+            dense[key] = full
+    return dense
+
+
+@pytest.mark.parametrize("mlp", ["gelu", "swiglu"])
+def test_mh_equals_block_diagonal_dense_model(mlp):
+    """One chunk (b = T): the multi-head fast MLP is the dense MLP whose
+    matrices are block diagonal, so the losses agree and its gradient is the
+    diagonal blocks of the dense gradient; the dense gradient between the
+    heads is not zero, so the two inner loops differ after an update."""
+    cfg = mh_cfg(mlp)
+    T = 24
+    cfg = dict(cfg, mini_batch=T, window=32)
+    w, ids = setup(cfg, T + 1)
+    dcfg = dict(cfg, mh_heads=0)
+    wd = block_diag_weights(cfg, w)
+    mh = O.Oracle(cfg, w)
+    dn = O.Oracle(dcfg, wd)
+    mh.ids = dn.ids = list(int(t) for t in ids)
+    l_mh, G_mh, _ = mh.chunk_objective(0)
+    l_dn, G_dn, _ = dn.chunk_objective(0)
+    np.testing.assert_allclose(l_mh, l_dn, rtol=1e-12, atol=1e-12)
+    nh = cfg["mh_heads"]
+    off = 0.0
+    for key, g in G_mh.items():
+        full = G_dn[key]
+        r, c = g.shape[1], g.shape[2]
+        for h in range(nh):
+            np.testing.assert_allclose(g[h], full[h * r:(h + 1) * r, h * c:(h + 1) * c], rtol=1e-10, atol=1e-14)
+        mask = np.ones_like(full, dtype=bool)
+        for h in range(nh):
+            mask[h * r:(h + 1) * r, h * c:(h + 1) * c] = False
+        off = max(off, np.abs(full[mask]).max())
+    assert off > 1e-6
+
+
+@pytest.mark.parametrize("mlp", ["gelu", "swiglu"])
+def test_mh_finite_differences(mlp):
+    """P1 for the multi-head variant: directional and per-entry central
+    differences of chunk 1's objective (the cache of chunk 0 held constant);
+    the gradient reaches block 0's fast MLP through every block above it."""
+    cfg = mh_cfg(mlp)
+    b = cfg["mini_batch"]
+    w, ids = setup(cfg, 3 * b + 1)
+    orc = O.Oracle(cfg, w)
+    orc.prefill(ids[: b + 1])
+    orc.ids = list(int(t) for t in ids)
+    _, G, _ = orc.chunk_objective(1)
+    assert (0, "w_up") in G and G[(0, "w_up")].shape == w["0.w_up"].shape
+    rng = np.random.default_rng(9)
+    D = {k: rng.standard_normal(v.shape) for k, v in orc.W.items()}
+
+    def A(W):
+        loss, _, _ = orc.chunk_objective(1, W=W)
+        return loss.mean()
+
+    eps = 1e-5
+    fd = (A({k: orc.W[k] + eps * D[k] for k in orc.W}) - A({k: orc.W[k] - eps * D[k] for k in orc.W})) / (2 * eps)
+    an = sum(np.sum(G[k] * D[k]) for k in G)
+    assert abs(an) > 1e-4
+    assert abs(fd - an) <= 1e-6 * abs(an)
+    for key in G:
+        idx = tuple(rng.integers(0, s) for s in G[key].shape)
+        Wp = {k: v.copy() for k, v in orc.W.items()}
+        Wm = {k: v.copy() for k, v in orc.W.items()}
+        Wp[key][idx] += eps
+        Wm[key][idx] -= eps
+        fde = (A(Wp) - A(Wm)) / (2 * eps)
+        assert abs(fde - G[key][idx]) <= 1e-6 * max(abs(G[key][idx]), 1e-4), key
+
+
+def test_mh_mean_of_per_token_gradients():
+    """P2 for the multi-head variant (Eq. 9: the chunk gradient is the mean of
+    the per-token gradients at W_{i-1})."""
+    cfg = mh_cfg("swiglu")
+    b = cfg["mini_batch"]
+    w, ids = setup(cfg, 2 * b + 1)
+    orc = O.Oracle(cfg, w)
+    orc.prefill(ids[: b + 1])
+    orc.ids = list(int(t) for t in ids)
+    _, G, _ = orc.chunk_objective(1)
+    z, tape = orc.forward(orc.ids[b:2 * b], b, keep=True)
+    _, dz = O.cross_entropy(z, np.asarray(orc.ids[b + 1:2 * b + 1]))
+    acc = {k: np.zeros_like(v) for k, v in G.items()}
+    for p in range(b):
+        one = np.zeros_like(dz)
+        one[p] = dz[p]
+        Gp = orc.backward(tape, one)
+        for k in acc:
+            acc[k] += Gp[k] / b
+    for k in G:
+        np.testing.assert_allclose(acc[k], G[k], rtol=1e-10, atol=1e-14)
