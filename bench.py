@@ -6,8 +6,12 @@ then 128 chunks of b = 1024 with forward, CE, tail backward and the fused SGD
 step). Inputs (weights, tokens) are resident in HBM before the timed region.
 
 Prints one JSON line (rank 0): tokens/s, ms per step, seconds per 1K tokens,
-the roofline of the dominant kernel measured with HIP events on the library's
-stream, and the CPU oracle timed on a bounded sample of the same workload.
+the roofline of the dominant kernel class (the one with the largest share of
+kernel time in a profiled step), measured with HIP events on the stream each
+launch runs on over the timed steps, every class's roofline fraction from the
+profiled step, the config-4 greedy decode (2048 tokens, two update pauses) and
+the CPU oracle timed on a bounded sample of the same workload beside the GPU
+on the same sample.
 """
 import argparse
 import hashlib
@@ -18,6 +22,8 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+MFMA_PEAK = 2.5e15   # MI355X dense bf16 MFMA, flop/s
+HBM_PEAK = 8.0e12    # MI355X HBM3E, bytes/s
 # HBM bytes per launch of the roofline kernel, measured with rocprofv3 counters
 # (FETCH_SIZE, WRITE_SIZE) and scaled by the same counters on a plain copy; the
 # record names the hash of the GEMM source it was taken on and is ignored once
@@ -82,17 +88,22 @@ def main():
                     help="rows per frozen-prefix pass (0: the library default)")
     ap.add_argument("--batch", type=int, default=1,
                     help="independent sequences per step (the length sweep: 16 x 8192, 4 x 32768)")
-    ap.add_argument("--prof-class", default="mlp_up",
-                    help="kernel class timed with HIP events during the timed steps")
+    ap.add_argument("--prof-class", default=None,
+                    help="kernel class timed with HIP events during the timed steps (default: the class "
+                         "with the largest share of kernel time in the profiled step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=None,
                     help="labelled positions of the CPU-oracle sample (default: one chunk)")
     ap.add_argument("--full-attention", action="store_true",
                     help="measure the static full-attention baseline instead: window = the stream, no "
                          "inner loop, the top blocks in 16K-row passes (same kernels)")
-    ap.add_argument("--decode", action="store_true",
-                    help="after the timed prefills, greedy-decode up to the next chunk boundary and "
-                         "through the update it triggers, timed separately (reported under 'decode')")
+    ap.add_argument("--decode", type=int, default=2048,
+                    help="after the timed prefills, greedy-decode this many tokens (0: none), timed in "
+                         "segments between the chunk updates it triggers (reported under 'decode')")
+    ap.add_argument("--sessions", default=None,
+                    help="comma-separated session counts S (e.g. 1,4,16): measure the serving budget M(S) "
+                         "and the prefill throughput of S concurrent sessions sharing one model's weights, "
+                         "each on its own stream, beside one lockstep batch of S sequences")
     ap.add_argument("--probe", action="store_true",
                     help="run only the roofline kernel and a plain copy (for rocprofv3 counters)")
     args = ap.parse_args()
@@ -102,6 +113,9 @@ def main():
         sys.exit(2)
     if args.probe:
         probe()
+        return
+    if args.sessions:
+        sessions_bench(args)
         return
 
     import numpy as np
@@ -120,7 +134,7 @@ def main():
     toks = torch.as_tensor(synth.make_batch(cfg, B, T + 1, seed=1)).to(dev)
     stream = torch.cuda.current_stream()
     # room for the decode measurement's tokens (up to one chunk) when asked
-    max_pos = T + 1 + (cfg["mini_batch"] if args.decode else 0)
+    max_pos = T + 1 + max(args.decode, 0)
     model = bd.TTTModel(cfg, w, batch=B, max_positions=max_pos, stream=stream, prefill_span=args.span,
                         forward_only=args.full_attention)
     log(f"[bench] model created, library device bytes {model.device_bytes() / 2**30:.1f} GiB")
@@ -137,7 +151,17 @@ def main():
         step()
         torch.cuda.synchronize()
         log(f"[bench] warmup {i} {time.time() - t0:.2f}s")
-    model.prof_begin(args.prof_class)
+    # one profiled step (outside the timed region): every launch under its class
+    model.prof_begin("all")
+    t0 = time.time()
+    step()
+    torch.cuda.synchronize()
+    prof_all = model.prof_end_classes()
+    log(f"[bench] profiled step {time.time() - t0:.2f}s")
+    classes = class_table(prof_all)
+    prof_class = args.prof_class or max(classes, key=lambda c: classes[c]["ms_per_step"])
+    log(f"[bench] roofline class: {prof_class}")
+    model.prof_begin(prof_class)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -145,45 +169,57 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] step {i} done")
     t1 = time.perf_counter()
-    k_ms, k_launch, k_work = model.prof_end()
+    timed = model.prof_end_classes()
+    k_ms = sum(v["ms"] for v in timed.values())
+    k_launch = sum(v["launches"] for v in timed.values())
+    k_flops = sum(v["flops"] for v in timed.values())
+    k_bytes = sum(v["bytes"] for v in timed.values())
     ms_step = (t1 - t0) * 1000 / args.steps
     tok = B * T
     value = tok / (ms_step / 1000)
 
-    # algorithmic work of the whole step (flops), for the step-level roofline
+    # algorithmic work of the whole step (flops), for the step-level roofline:
+    # forward of every block and the head; backward through the head and the
+    # tail blocks (attention only above the first tail block), the fast
+    # weights' gradients; a multi-head fast MLP costs 1/heads of a dense one
     d, V, L, nt = cfg["d_model"], cfg["vocab"], cfg["n_blocks"], cfg["n_ttt_blocks"]
     hq = cfg["n_heads"] * cfg["head_dim"]
     m = 3 if cfg["mlp"] == "swiglu" else 2
-    h, ht, b, k = cfg["mlp_hidden"], cfg["ttt_hidden"], cfg["mini_batch"], cfg["window"]
+    h, ht, hs, b, k = cfg["mlp_hidden"], cfg["ttt_hidden"], cfg["static_hidden"], cfg["mini_batch"], cfg["window"]
+    nh = cfg.get("mh_heads", 0)
+    ht_eff = ht / nh if nh > 1 else ht
     pairs = sum(min(p + 1, k) for p in range(T))
-    fwd = 2 * T * L * (2 * d * hq + 2 * d * hq + m * d * h) + 2 * T * V * d + 4 * hq * L * pairs
+    fwd = (2 * T * L * 4 * d * hq + 2 * T * (L - nt) * m * d * h + 2 * T * nt * m * d * (hs + ht_eff)
+           + 2 * T * V * d + 4 * hq * L * pairs)
     bwd = (2 * T * V * d + (nt - 1) * (8 * T * d * hq + 4 * hq * pairs + 2 * hq * T * (b + 1)
-                                       + 2 * T * m * d * h) + nt * 2 * T * m * d * ht + 2 * T * d * ht) * B
+                                       + 2 * T * m * d * (hs + ht_eff)) + nt * 2 * T * m * d * ht_eff
+           + 2 * T * d * ht_eff) * B
     step_flops = fwd * B + (0 if args.full_attention else bwd)
     peak_bf16 = 2.5e15
 
-    if args.prof_class == "ce":
-        achieved = k_work / (k_ms / 1000) / 1e9 if k_ms > 0 else 0.0
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                "frac": round(achieved / 8000.0, 4), "traffic": None}
+    if k_bytes / HBM_PEAK > k_flops / MFMA_PEAK:
+        achieved = k_bytes / (k_ms / 1000) / 1e9 if k_ms > 0 else 0.0
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic_bytes(prof_class)}
     else:
-        achieved = k_work / (k_ms / 1000) / 1e12 if k_ms > 0 else 0.0
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
-                "frac": round(achieved / 2500.0, 4), "traffic": traffic_bytes(args.prof_class)}
-    roof.update({"kernel": args.prof_class, "launches": k_launch,
+        achieved = k_flops / (k_ms / 1000) / 1e12 if k_ms > 0 else 0.0
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK / 1e12, "unit": "TFLOP/s",
+                "frac": round(achieved * 1e12 / MFMA_PEAK, 4), "traffic": traffic_bytes(prof_class)}
+    roof.update({"kernel": prof_class, "launches": k_launch,
                  "avg_launch_us": round(k_ms * 1000 / max(k_launch, 1), 2),
                  "step_frac": round(step_flops / peak_bf16 / (ms_step / 1000), 4),
                  # the span passes run concurrently with the chunk loop, so
                  # per-launch times include the shared GPU
-                 "overlapped": True})
+                 "overlapped": True,
+                 "share_of_kernel_time": classes.get(prof_class, {}).get("share")})
 
     dec = None
-    if args.decode:
-        dec = decode_timing(model, B, T + 1, cfg["mini_batch"])
+    if args.decode > 0:
+        dec = decode_timing(model, B, T + 1, cfg["mini_batch"], args.decode)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, w, toks, args.cpu_positions)
+        cpu = cpu_baseline(cfg, w, toks, args.cpu_positions, model)
 
     out = {
         "metric": "TTT-E2E prefill tokens/s + s per 1K tokens, 3B-shape 128K ctx, 1 GPU",
@@ -197,6 +233,7 @@ def main():
                                 f"{args.config}-shape TTT-E2E prefill, {B} x {T} tokens, b={b}, k={k}"),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "roofline": roof,
+        "classes": classes,
         "cpu_baseline": cpu,
     }
     if dec is not None:
@@ -205,32 +242,143 @@ def main():
     model.close()
 
 
-def decode_timing(model, B, n_ids, b):
-    """Greedy decode after a full prefill of n_ids ids: the tokens before the
-    next chunk boundary (forward of one position each), then the token whose
-    arrival completes a chunk (the chunk's backward and SGD step run before
-    its forward), each timed between synchronisations."""
+def sessions_bench(args):
+    """Serving S sessions (technical review, section 11.2, Eq. 13): S models
+    sharing one model's frozen and initial fast weights, each prefilling its
+    own stream of seq_len ids on its own HIP stream, all enqueued before one
+    synchronisation; memory by the terms of Eq. 13 from the library's own
+    accounting; beside it one model with a lockstep batch of S sequences."""
     import torch
-    n_lab = n_ids - 1
-    plain = b - 1 - (n_lab % b)  # decoded ids that complete no chunk
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if plain:
-        model.decode(plain)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    model.decode(1)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    log(f"[bench] decode: {plain} plain tokens {(t1 - t0) * 1000 / max(plain, 1):.2f} ms each, "
-        f"update token {(t2 - t1) * 1000:.2f} ms")
-    return {"batch": B, "plain_tokens": plain, "ms_per_token": round((t1 - t0) * 1000 / max(plain, 1), 3),
-            "update_token_ms": round((t2 - t1) * 1000, 3),
-            "ms_per_token_incl_update": round((t2 - t0) * 1000 / (plain + 1), 3)}
+    from long_context_lm_token_amd import binding as bd, synth
+    cfg = synth.get_config(args.config)
+    T = args.seq_len or 8192
+    counts = [int(x) for x in args.sessions.split(",")]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] sessions: config {args.config}, {T} ids per session, S in {counts}")
+    w = synth.make_weights(cfg, seed=0, device="cuda")
+    base = bd.TTTModel(cfg, w, batch=1, max_positions=T + 1, prefill_span=args.span)
+    del w
+    torch.cuda.empty_cache()
+    toks = torch.as_tensor(synth.make_batch(cfg, max(counts), T + 1, seed=1)).to(dev)
+    rows = []
+    for S in counts:
+        sess = [base] + [base.session(max_positions=T + 1, prefill_span=args.span) for _ in range(S - 1)]
+        streams = [torch.cuda.Stream() for _ in range(S)]
+        for x, st in zip(sess, streams):
+            x.stream = st
+        parts = {k: 0 for k in ("shared", "fast", "cache", "work")}
+        for i, x in enumerate(sess):
+            p = x.bytes_by_part()
+            for k in ("fast", "cache", "work"):
+                parts[k] += p[k]
+            parts["shared"] = p["shared"]
+
+        def run_all():
+            for i, (x, st) in enumerate(zip(sess, streams)):
+                with torch.cuda.stream(st):
+                    x.reset()
+                    x.prefill(toks[i:i + 1], want_losses=False)
+            torch.cuda.synchronize()
+
+        run_all()  # warm-up
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run_all()
+        dt = (time.perf_counter() - t0) / args.steps
+        for x in sess[1:]:
+            x.close()
+        base.stream = None
+        del sess
+        # the same S sequences as one lockstep batch
+        bat = base.session(batch=S, max_positions=T + 1, prefill_span=args.span)
+        bat.reset()
+        bat.prefill(toks[:S], want_losses=False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            bat.reset()
+            bat.prefill(toks[:S], want_losses=False)
+            torch.cuda.synchronize()
+        dtb = (time.perf_counter() - t0) / args.steps
+        pb = bat.bytes_by_part()
+        bat.close()
+        per = {k: parts[k] // S for k in ("fast", "cache", "work")}
+        row = {"S": S, "tokens_per_s": round(S * T / dt, 1), "s_per_step": round(dt, 4),
+               "M_S_GiB": round((parts["shared"] + parts["fast"] + parts["cache"] + parts["work"]) / 2**30, 3),
+               "M_shared_GiB": round(parts["shared"] / 2**30, 3),
+               "per_session_GiB": {k: round(v / 2**30, 3) for k, v in per.items()},
+               "batched_tokens_per_s": round(S * T / dtb, 1),
+               "batched_M_GiB": round(sum(pb.values()) / 2**30, 3)}
+        log(f"[bench] S={S}: {json.dumps(row)}")
+        rows.append(row)
+    base.close()
+    print(json.dumps({"metric": "TTT-E2E prefill tokens/s of S concurrent sessions and the serving budget M(S)",
+                      "config": {"workload": f"{args.config}-shape, {T} ids per session, b={cfg['mini_batch']}, "
+                                             f"k={cfg['window']}"},
+                      "sessions": rows}), flush=True)
 
 
-def cpu_baseline(cfg, w, toks, positions):
-    """The oracle (numpy fp64) on this host: the first chunk of the same stream."""
+def decode_timing(model, B, n_ids, b, n_new):
+    """Greedy decode of n_new ids after a full prefill of n_ids ids (the
+    technical review's Algorithm 3): segments of ids that complete no chunk
+    (forward of one position each) and the single ids whose arrival completes
+    a chunk (that chunk's backward and SGD step run before their forward),
+    each segment timed between synchronisations."""
+    import torch
+    segs = []
+    done, n_lab = 0, n_ids - 1
+    while done < n_new:
+        plain = min(b - 1 - (n_lab % b), n_new - done)   # ids that complete no chunk
+        if plain:
+            segs.append(("plain", plain))
+            done += plain
+            n_lab += plain
+        if done < n_new:
+            segs.append(("update", 1))
+            done += 1
+            n_lab += 1
+    times = []
+    torch.cuda.synchronize()
+    for kind, n in segs:
+        t0 = time.perf_counter()
+        model.decode(n, want_losses=False)
+        torch.cuda.synchronize()
+        times.append((kind, n, time.perf_counter() - t0))
+    plain_n = sum(n for k, n, _ in times if k == "plain")
+    plain_t = sum(t for k, _, t in times if k == "plain")
+    upd = [round(t * 1000, 3) for k, _, t in times if k == "update"]
+    total = sum(t for _, _, t in times)
+    log(f"[bench] decode {n_new}: {plain_t * 1000 / max(plain_n, 1):.2f} ms per plain token, update tokens {upd} ms")
+    return {"batch": B, "tokens": n_new, "ms_per_token": round(plain_t * 1000 / max(plain_n, 1), 3),
+            "update_token_ms": upd, "seconds": round(total, 3),
+            "tokens_per_s": round(B * n_new / total, 1),
+            "ms_per_token_incl_updates": round(total * 1000 / n_new, 3)}
+
+
+def class_table(prof):
+    """Per disjoint kernel class of one profiled step: time, share of kernel
+    time, achieved rates and the fraction of the class's roofline (the larger
+    of its algorithmic flops at the bf16 MFMA peak and its algorithmic bytes
+    at the HBM peak, over its measured time)."""
+    names = ["gemm_span", "gemm_chunk", "gemm_sgd", "attn_fwd", "attn_dq", "attn_dkdv", "ce", "norm", "other"]
+    tot = sum(prof[n]["ms"] for n in names) or 1.0
+    out = {}
+    for n in names:
+        v = prof[n]
+        t = v["ms"] / 1000
+        t_f, t_b = v["flops"] / MFMA_PEAK, v["bytes"] / HBM_PEAK
+        out[n] = {"ms_per_step": round(v["ms"], 2), "share": round(v["ms"] / tot, 4), "launches": v["launches"],
+                  "tflops": round(v["flops"] / t / 1e12, 1) if t > 0 else 0.0,
+                  "gbs": round(v["bytes"] / t / 1e9, 1) if t > 0 else 0.0,
+                  "bound": "mfma" if t_f >= t_b else "hbm",
+                  "frac": round(max(t_f, t_b) / t, 4) if t > 0 else 0.0}
+    return out
+
+
+def cpu_baseline(cfg, w, toks, positions, model):
+    """The oracle (numpy fp64) on this host: the first chunk of the same
+    stream; the GPU library timed on the same sample beside it."""
     import numpy as np
     import torch
     from long_context_lm_token_amd import synth
@@ -246,7 +394,19 @@ def cpu_baseline(cfg, w, toks, positions):
     orc.prefill(ids)
     dt = time.perf_counter() - t0
     log(f"[bench] cpu baseline {dt:.1f}s")
+    # the GPU on the same sample: reset + prefill of the same n+1 ids (median of 5)
+    part = toks[:, : n + 1].contiguous()
+    gt = []
+    for _ in range(6):
+        model.reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        model.prefill(part)
+        torch.cuda.synchronize()
+        gt.append(time.perf_counter() - t0)
+    g_dt = float(np.median(gt[1:]))
     return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "gpu_same_sample": round(n / g_dt, 1),
             "sample": f"oracle prefill of the first {n} labelled positions (one full chunk: forward of all "
                       f"blocks, CE, tail backward, SGD step) of the same {cfg['name']} stream",
             "seconds": round(dt, 2)}

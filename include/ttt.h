@@ -73,7 +73,15 @@ enum ttt_mat { TTT_UP = 0, TTT_GATE = 1, TTT_DOWN = 2 };
  * the initial weights and no backward or SGD step runs (the static model;
  * with window >= the stream length it is the full-attention Transformer whose
  * prefill time the technical review compares TTT-E2E with: its Figure 1 and
- * section 11). */
+ * section 11).
+ * mh_heads > 1 selects the "TTT-E2E all layers MH" variant (b-lab.team
+ * summary, "Alternative Derivation", step 4; technical review, section 8 and
+ * its Table 1): the fast MLP of each tail block is split into mh_heads
+ * independent heads, head i mapping columns [i*dh, (i+1)*dh) of the
+ * normalised state (dh = d_model / mh_heads) through its own MLP of hidden
+ * ttt_hidden / mh_heads back to the same columns; with n_ttt_blocks =
+ * n_blocks every block has one, beside its static MLP of hidden
+ * static_hidden. 0 or 1: the dense fast MLP of the final design. */
 typedef struct ttt_config {
   int32_t vocab, d_model, n_blocks, n_heads, head_dim;
   int32_t mlp_kind;          /* enum ttt_mlp */
@@ -88,6 +96,7 @@ typedef struct ttt_config {
   int32_t prefill_span;
   int64_t max_device_bytes;
   int32_t forward_only;
+  int32_t mh_heads;
 } ttt_config;
 
 /* Initial weights, all device pointers in cfg.dtype, row-major [in][out].
@@ -97,7 +106,9 @@ typedef struct ttt_config {
  *   wq[l], wk[l], wv[l]: [d][H*hd];  wo[l]: [H*hd][d]
  *   w_up[l], w_gate[l] (SwiGLU only, else NULL): [d][h];  w_down[l]: [h][d]
  *     with h = ttt_hidden for tail blocks (the fast, trainable branch) and
- *     mlp_hidden otherwise
+ *     mlp_hidden otherwise; with mh_heads = nh > 1 the tail blocks' fast
+ *     matrices are per head: w_up[l], w_gate[l] [nh][d/nh][h/nh], w_down[l]
+ *     [nh][h/nh][d/nh]
  *   s_up[l], s_gate[l], s_down[l]: static branch of tail blocks ([d][hs],
  *     [d][hs], [hs][d]); NULL (or ignored) for other blocks. */
 typedef struct ttt_weights {
@@ -134,6 +145,22 @@ typedef struct ttt_model ttt_model;
  * On error *out is NULL and nothing stays allocated. */
 int ttt_model_create(const ttt_config* cfg, const ttt_weights* init, void* stream,
                      ttt_model** out);
+
+/* Create a session of `base`: another model that shares base's frozen
+ * weights and initial fast weights (by reference, not copied) and has its own
+ * sequences, fast weights, attention caches, positions and workspace - the
+ * per-session terms of the serving budget of the technical review, section
+ * 11.2, Eq. 13, M(S) = M_shared + S (M_fast + M_local cache + M_update work).
+ * batch, max_positions, prefill_span and max_device_bytes (which caps only
+ * what this call allocates) are the session's own; every other configuration
+ * field is base's. Sessions are independent: each can be reset, fed and
+ * destroyed on its own, and each starts from a fresh copy of the initial
+ * fast weights (Algorithm 1 step 1). The shared part is freed with the last
+ * model that uses it, so base may be destroyed before its sessions.
+ * Synchronous on `stream`. Errors: TTT_EINVAL (base NULL, invalid sizes),
+ * TTT_ENOMEM, TTT_EHIP; on error *out is NULL. */
+int ttt_model_create_session(const ttt_model* base, int32_t batch, int64_t max_positions, int32_t prefill_span,
+                             int64_t max_device_bytes, void* stream, ttt_model** out);
 
 /* Prefill (review, section 7, Algorithm 1). Async.
  * tokens: device int32 [batch][n], the next n ids of every sequence.
@@ -173,7 +200,8 @@ int ttt_decode(ttt_model* m, int64_t n_new, int32_t* tokens_out, float* losses, 
 
 /* Copy the current fp32 fast weights of one trainable matrix of one sequence
  * into dst (device float, row-major [in][out]: UP/GATE [d][ttt_hidden],
- * DOWN [ttt_hidden][d]). Async on `stream`. Reflects every completed chunk:
+ * DOWN [ttt_hidden][d]; with mh_heads = nh > 1, [nh][d/nh][ttt_hidden/nh] and
+ * [nh][ttt_hidden/nh][d/nh]). Async on `stream`. Reflects every completed chunk:
  * the adapted weights W that the review's section 7, Algorithm 1 returns
  * after its last update (the summary's W_{T/b}, "Test-Time Training (Inner
  * Loop)"); an incomplete chunk has not changed them.
@@ -196,8 +224,19 @@ const char* ttt_last_error(void);
 /* Number of positions already in sequence streams (ids appended). */
 int64_t ttt_stream_length(const ttt_model* m);
 
-/* Library device memory in bytes currently allocated by the model. */
+/* Device memory in bytes the model uses: its own allocations plus the shared
+ * part (frozen weights and initial fast weights), which sessions of one base
+ * model hold in common. */
 int64_t ttt_device_bytes(const ttt_model* m);
+
+/* The same bytes by part, the terms of the review's Eq. 13 (section 11.2):
+ * out[0] the shared part (frozen weights and the initial fast weights; the
+ * same memory for every session of one base), out[1] the fast weights of the
+ * model's sequences (compute copies in both layouts and, for bf16, the fp32
+ * master), out[2] the local attention caches and stream state (K/V rings,
+ * ids, the residual hand-off of the frozen prefix, the RoPE table), out[3]
+ * the workspace of the forward and update passes. Errors: TTT_EINVAL. */
+int ttt_device_bytes_by_part(const ttt_model* m, int64_t* out);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(HERE, "libttt.so")
 TTT_FP32, TTT_BF16 = 0, 1
 TTT_GELU, TTT_SWIGLU = 0, 1
 TTT_UP, TTT_GATE, TTT_DOWN = 0, 1, 2
-PROF = {"gemm": 0, "attn_fwd": 1, "attn_bwd": 2, "ce": 3, "mlp_up": 4}
+PROF = {"gemm": 0, "attn_fwd": 1, "attn_bwd": 2, "ce": 3, "mlp_up": 4, "gemm_span": 5, "gemm_chunk": 6,
+        "gemm_sgd": 7, "attn_dq": 8, "attn_dkdv": 9, "norm": 10, "other": 11, "all": 12}
+PROF_NCLASS = 12
 
 c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -31,7 +33,7 @@ class TTTConfig(ctypes.Structure):
                 ("rope", c_i32), ("rope_theta", c_f32), ("norm_eps", c_f32), ("window", c_i32),
                 ("mini_batch", c_i32), ("lr", c_f32), ("dtype", c_i32), ("batch", c_i32),
                 ("max_positions", c_i64), ("prefill_span", c_i32), ("max_device_bytes", c_i64),
-                ("forward_only", c_i32)]
+                ("forward_only", c_i32), ("mh_heads", c_i32)]
 
 
 _PP = ctypes.POINTER(c_vp)
@@ -73,9 +75,12 @@ def load():
     lib.ttt_stream_length.restype = c_i64
     lib.ttt_device_bytes.argtypes = [c_vp]
     lib.ttt_device_bytes.restype = c_i64
+    lib.ttt_device_bytes_by_part.argtypes = [c_vp, c_vp]
+    lib.ttt_model_create_session.argtypes = [c_vp, c_i32, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(c_vp)]
     lib.ttt_prof_begin.argtypes = [c_vp, c_i32]
     lib.ttt_prof_end.argtypes = [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64),
                                  ctypes.POINTER(ctypes.c_double)]
+    lib.ttt_prof_end_classes.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]
     lib.ttt_k_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
                                c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64,
                                c_f32, ctypes.c_uint32, c_i32, c_vp, c_i64, c_vp]
@@ -128,7 +133,8 @@ def make_config(cfg: dict, batch=1, max_positions=None, prefill_span=0, max_devi
                      norm_eps=cfg["norm_eps"], window=cfg["window"], mini_batch=cfg["mini_batch"],
                      lr=cfg["lr"], dtype=TTT_BF16 if cfg["dtype"] == "bf16" else TTT_FP32,
                      batch=batch, max_positions=mp, prefill_span=prefill_span,
-                     max_device_bytes=max_device_bytes, forward_only=1 if forward_only else 0)
+                     max_device_bytes=max_device_bytes, forward_only=1 if forward_only else 0,
+                     mh_heads=cfg.get("mh_heads", 0))
 
 
 # ---------------------------------------------------------------------------
@@ -157,6 +163,13 @@ def ttt_model_create(cfg: TTTConfig, weights: dict, L: int, stream=None):
     h = c_vp()
     check(lib.ttt_model_create(ctypes.byref(cfg), ctypes.byref(w), stream_ptr(stream), ctypes.byref(h)))
     return h, arrays
+
+
+def ttt_model_create_session(base, batch, max_positions, prefill_span=0, max_device_bytes=0, stream=None):
+    h = c_vp()
+    check(load().ttt_model_create_session(base, batch, max_positions, prefill_span, max_device_bytes,
+                                          stream_ptr(stream), ctypes.byref(h)))
+    return h
 
 
 def ttt_prefill(h, tokens, n, losses, stream=None):
@@ -194,6 +207,25 @@ class TTTModel:
         self.h, self._keep = ttt_model_create(self.c, weights, cfg["n_blocks"], stream)
         self.stream = stream
 
+    def session(self, batch=1, max_positions=None, prefill_span=0, max_device_bytes=0, stream=None):
+        """A new model sharing this one's frozen and initial fast weights
+        (ttt_model_create_session), with its own sequences and state."""
+        obj = TTTModel.__new__(TTTModel)
+        obj.cfg = self.cfg
+        obj.batch = batch
+        obj.c = None
+        obj._keep = None
+        mp = max_positions if max_positions is not None else self.cfg["seq_len"] + 1
+        obj.h = ttt_model_create_session(self.h, batch, mp, prefill_span, max_device_bytes, stream)
+        obj.stream = stream
+        return obj
+
+    def bytes_by_part(self):
+        """{shared, fast, cache, work}: device bytes by the terms of Eq. 13."""
+        out = (c_i64 * 4)()
+        check(load().ttt_device_bytes_by_part(self.h, out))
+        return dict(zip(["shared", "fast", "cache", "work"], list(out)))
+
     def prefill(self, tokens: torch.Tensor, want_losses=True):
         tokens = tokens.to(torch.int32).contiguous()
         if tokens.dim() == 1:
@@ -215,6 +247,9 @@ class TTTModel:
         d, ht = self.cfg["d_model"], self.cfg["ttt_hidden"]
         code = {"w_up": TTT_UP, "w_gate": TTT_GATE, "w_down": TTT_DOWN}[mat]
         shape = (ht, d) if code == TTT_DOWN else (d, ht)
+        nh = self.cfg.get("mh_heads", 0)
+        if nh > 1:
+            shape = (nh, ht // nh, d // nh) if code == TTT_DOWN else (nh, d // nh, ht // nh)
         dst = torch.empty(shape, dtype=torch.float32, device="cuda")
         ttt_get_weights(self.h, seq, block, code, dst, self.stream)
         return dst
@@ -235,6 +270,15 @@ class TTTModel:
         ms, n, work = ctypes.c_double(), c_i64(), ctypes.c_double()
         check(load().ttt_prof_end(self.h, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(work)))
         return ms.value, n.value, work.value
+
+    def prof_end_classes(self):
+        """Per-class (ms, launches, flops, bytes) dicts keyed by class name."""
+        n = PROF_NCLASS
+        ms, fl, by = (ctypes.c_double * n)(), (ctypes.c_double * n)(), (ctypes.c_double * n)()
+        k = (c_i64 * n)()
+        check(load().ttt_prof_end_classes(self.h, n, ms, k, fl, by))
+        names = {v: kname for kname, v in PROF.items()}
+        return {names[c]: dict(ms=ms[c], launches=k[c], flops=fl[c], bytes=by[c]) for c in range(n)}
 
     def close(self):
         if self.h:

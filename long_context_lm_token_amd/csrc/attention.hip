@@ -1476,13 +1476,15 @@ hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
   const int ns = a.nsplit > 0 ? a.nsplit : 1;
   dim3 grid((a.M + QB - 1) / QB, a.H, a.B * ns);
   const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-  if (sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
-      a.seq_stride % 8 == 0)
-    hipLaunchKernelGGL(attn_bwd_dq_dl_kernel, grid, dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (a.parts != 2) {
+    if (sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
+        a.seq_stride % 8 == 0)
+      hipLaunchKernelGGL(attn_bwd_dq_dl_kernel, grid, dim3(NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.parts == 1) return e;
+  }
   dim3 grid2((a.M + QB - 1) / QB, a.H, a.B);
   const bool dl = sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && al16(a.q) &&
                   al16(a.dout) && a.ldk % 8 == 0 && a.seq_stride % 8 == 0 && a.ldq % 8 == 0 && a.lddo % 8 == 0;

@@ -65,6 +65,8 @@ __global__ void embed_kernel(const int32_t* ids, int64_t ids_ss, int64_t p0, int
                              int d, int vocab, float* x) {
   const int i = blockIdx.x, s = blockIdx.y;
   int id = ids[s * ids_ss + p0 + i];
+  // ids are checked on the host before any launch (TTT_EINVAL); the clamp
+  // only keeps a corrupted id from reading outside the table
   id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
   const T* e = E + (int64_t)id * d;
   float* o = x + ((int64_t)s * S + i) * d;
@@ -302,10 +304,13 @@ __global__ void attn_delta_kernel(const T* o, const T* dout, int H, int hd, int6
 }
 
 // -------------------------- cross entropy --------------------------------
-// One workgroup per row: max / argmax / sum-exp over V fp32 logits read
-// once into registers; loss = lse - z[label]; dz = (softmax - onehot)*scale.
+// One workgroup per row: max / argmax / sum-exp over V fp32 logits read once
+// into registers; loss = lse - z[label]; dz = (softmax - onehot)*scale.
+// Each thread owns runs of 8 consecutive logits (two 16-byte loads, one
+// 16-byte bf16 store of the gradient); the exponentials of the sum pass stay
+// in registers for the gradient.
 constexpr int CE_NT = 512;
-constexpr int CE_PER = 16;  // float4 per thread -> up to 32768 logits
+constexpr int CE_IT = 8;  // runs of 8 per thread -> up to 32768 logits
 
 template <typename T>
 __global__ __launch_bounds__(CE_NT) void ce_kernel(CEArgs a) {
@@ -315,19 +320,18 @@ __global__ __launch_bounds__(CE_NT) void ce_kernel(CEArgs a) {
   const int s = row / a.S, i = row % a.S;
   const int64_t pos = a.p0 + i;
   const float* z = a.logits + row * a.V;
-  const int nv = a.V / 4;
-  float4 v[CE_PER];
+  const int n8 = a.V / 8;
+  float v[CE_IT][8];
   float mx = -INFINITY;
   int am = 0x7fffffff;
 #pragma unroll
-  for (int k = 0; k < CE_PER; ++k) {
+  for (int k = 0; k < CE_IT; ++k) {
     const int idx = k * CE_NT + threadIdx.x;
-    if (idx < nv) {
-      v[k] = reinterpret_cast<const float4*>(z)[idx];
-      const float e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    if (idx < n8) {
+      V8<float>::get(z + idx * 8, v[k]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (e[c] > mx) { mx = e[c]; am = idx * 4 + c; }
+      for (int c = 0; c < 8; ++c)
+        if (v[k][c] > mx) { mx = v[k][c]; am = idx * 8 + c; }
     }
   }
   // block argmax (lowest index among maxima)
@@ -353,15 +357,23 @@ __global__ __launch_bounds__(CE_NT) void ce_kernel(CEArgs a) {
   }
   float se = 0.f;
 #pragma unroll
-  for (int k = 0; k < CE_PER; ++k) {
+  for (int k = 0; k < CE_IT; ++k) {
     const int idx = k * CE_NT + threadIdx.x;
-    if (idx < nv) se += __expf(v[k].x - mx) + __expf(v[k].y - mx) + __expf(v[k].z - mx) + __expf(v[k].w - mx);
+    if (idx < n8) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        v[k][c] = __expf(v[k][c] - mx);
+        se += v[k][c];
+      }
+    }
   }
   se = block_sum(se, red);
   const float lse = mx + logf(se);
   const bool has_label = pos + 1 < a.n_ids;
   int label = -1;
   if (has_label) {
+    // ids are checked on the host before any launch; the clamp only keeps a
+    // corrupted id from reading outside the row
     label = a.ids[s * a.ids_seq_stride + pos + 1];
     label = label < 0 ? 0 : (label >= a.V ? a.V - 1 : label);
   }
@@ -378,26 +390,20 @@ __global__ __launch_bounds__(CE_NT) void ce_kernel(CEArgs a) {
       a.last_arg[s] = am;
     }
   }
-  if (a.dz && has_label) {
+  if (a.dz) {
     T* dz = reinterpret_cast<T*>(a.dz) + row * a.V;
-    const float inv = 1.f / se;
+    const float sc = has_label ? a.dz_scale / se : 0.f;
+    const float sl = has_label ? a.dz_scale : 0.f;
 #pragma unroll
-    for (int k = 0; k < CE_PER; ++k) {
+    for (int k = 0; k < CE_IT; ++k) {
       const int idx = k * CE_NT + threadIdx.x;
-      if (idx < nv) {
-        const float e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      if (idx < n8) {
+        float o[8];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int col = idx * 4 + c;
-          float p = __expf(e[c] - mx) * inv;
-          if (col == label) p -= 1.f;
-          dz[col] = from_f32<T>(p * a.dz_scale);
-        }
+        for (int c = 0; c < 8; ++c) o[c] = v[k][c] * sc - (idx * 8 + c == label ? sl : 0.f);
+        V8<T>::store(dz + idx * 8, o);
       }
     }
-  } else if (a.dz) {
-    T* dz = reinterpret_cast<T*>(a.dz) + row * a.V;
-    for (int col = threadIdx.x; col < a.V; col += CE_NT) dz[col] = from_f32<T>(0.f);
   }
 }
 
@@ -543,7 +549,7 @@ hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, co
 
 hipError_t act_fwd_launch(const float* z, int rows, int h, int64_t ldz, int glu, void* a, int64_t lda,
                           int dt, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
+  if (rows <= 0 || h <= 0) return hipSuccess;
   if (h % 8 || ldz % 8 || lda % 8) return hipErrorInvalidValue;
   dim3 g((h / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
@@ -554,7 +560,7 @@ hipError_t act_fwd_launch(const float* z, int rows, int h, int64_t ldz, int glu,
 
 hipError_t act_bwd_launch(const float* z, const float* da, int rows, int hcols, int64_t ldz, int64_t ldda,
                           int64_t up_off, int glu, void* dz, int64_t lddz, int dt, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
+  if (rows <= 0 || hcols <= 0) return hipSuccess;
   if (hcols % 8 || ldz % 8 || ldda % 8 || up_off % 8 || lddz % 8) return hipErrorInvalidValue;
   dim3 g((hcols / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
@@ -575,7 +581,7 @@ hipError_t attn_delta_launch(const void* o, const void* dout, int rows, int H, i
 
 hipError_t ce_launch(const CEArgs& a, int dt, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
-  if (a.V % 4 || a.V > CE_NT * CE_PER * 4) return hipErrorInvalidValue;
+  if (a.V % 8 || a.V > CE_NT * CE_IT * 8) return hipErrorInvalidValue;
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(ce_kernel<bf16>, dim3(a.rows), dim3(CE_NT), 0, st, a),
       hipLaunchKernelGGL(ce_kernel<float>, dim3(a.rows), dim3(CE_NT), 0, st, a));

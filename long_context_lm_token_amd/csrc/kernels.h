@@ -88,6 +88,8 @@ struct AttnArgs {
   int nsplit;
   float* part_o;                    // [nsplit][B*M][ldo]
   float* part_m; float* part_l;     // [nsplit][B][H][M]
+  // backward: which kernels attn_bwd_launch runs (0 both, 1 dQ only, 2 dK/dV only)
+  int parts;
 };
 
 hipError_t attn_fwd_launch(const AttnArgs& a, int dt, hipStream_t st);
