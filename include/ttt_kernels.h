@@ -90,6 +90,20 @@ int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc,
                    float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
                    float scale, int32_t nsplit, float* ws, void* stream);
 
+/* ttt_k_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and arguments without `ws`. The split partials go to a
+ * fixed 64 MiB device array (16 Mi floats) that the library holds on every
+ * device it runs on until the process ends; the call allocates and frees
+ * nothing. nsplit * B * M * (H*hd + 2*H) must not exceed 16 Mi floats
+ * (nsplit = 1 needs none), else TTT_EINVAL with the size in the message and
+ * nothing launched. Every partial the merge reads is written by the same call,
+ * so nothing needs clearing; calls that overlap on one device (other streams,
+ * other threads) share the array and race. */
+int ttt_k_attn_fwd_noalloc(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
+                           float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
+                           float scale, int32_t nsplit, void* stream);
+
 /* Backward of ttt_k_attn_fwd: dq (fp32, nsplit slices of [B*M][H*hd] whose
  * sum is the gradient; each query's window split as in the forward); dk, dv
  * (fp32 [B*M][H*hd]) for the keys at positions pos0..pos0+M-1 only (earlier

@@ -92,6 +92,8 @@ def load():
     lib.ttt_k_gemm_operands.restype = None
     lib.ttt_k_attn_fwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_f32, c_i32, c_vp, c_vp]
+    lib.ttt_k_attn_fwd_noalloc.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                           c_i32, c_i64, c_i32, c_f32, c_i32, c_vp]
     lib.ttt_k_attn_bwd.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                    c_i32, c_i32, c_i32, c_i64, c_i32, c_f32, c_i32, c_vp]
     lib.ttt_k_attn_fwd_kernel.argtypes = [c_i32]

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -9,8 +10,36 @@
 #include "../../include/ttt_kernels.h"
 #include "kernels.h"
 
+// Split partials of ttt_k_attn_fwd_noalloc: a fixed device array, so that
+// the call allocates nothing. Each device holds its own copy, at its own
+// address, for the life of the process; host code reaches it only through the
+// per-device address hipGetSymbolAddress returns.
+constexpr int64_t kScratchFloats = (int64_t)16 << 20;  // 64 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
 namespace {
 thread_local std::string k_err;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+hipError_t scratch_ptr(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
 int g_gemm_mn = 0;  // test hook: operands of ttt_k_gemm stored MN-major
 int kfail(int code, const char* msg) {
   k_err = msg;
@@ -77,12 +106,13 @@ static AttnArgs mk(const void* q, const void* kc, const void* vc, int32_t cap, i
   return a;
 }
 
-int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
-                   float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
-                   float scale, int32_t nsplit, float* ws, void* stream) {
-  if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
-    return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
-  if (nsplit < 1 || nsplit > 16 || (nsplit > 1 && !ws)) return kfail(TTT_EINVAL, "nsplit in 1..16, ws for > 1");
+static int64_t attn_ws_floats(int32_t B, int32_t M, int32_t H, int32_t hd, int32_t nsplit) {
+  return nsplit > 1 ? (int64_t)nsplit * B * M * ((int64_t)H * hd + 2 * H) : 0;
+}
+
+static int attn_fwd_ws(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o, float* lse,
+                       int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window, float scale,
+                       int32_t nsplit, float* ws, void* stream) {
   AttnArgs a = mk(q, kc, vc, cap, B, M, H, hd, pos0, window, scale);
   a.o = o; a.ldo = (int64_t)H * hd; a.lse = lse;
   a.nsplit = nsplit;
@@ -92,6 +122,35 @@ int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc,
     a.part_l = a.part_m + (int64_t)nsplit * B * H * M;
   }
   return kdone(attn_fwd_launch(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int ttt_k_attn_fwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
+                   float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
+                   float scale, int32_t nsplit, float* ws, void* stream) {
+  if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0)
+    return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
+  if (nsplit < 1 || nsplit > 16 || (nsplit > 1 && !ws)) return kfail(TTT_EINVAL, "nsplit in 1..16, ws for > 1");
+  return attn_fwd_ws(dtype, q, kc, vc, cap, o, lse, B, M, H, hd, pos0, window, scale, nsplit, ws, stream);
+}
+
+int ttt_k_attn_fwd_noalloc(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, void* o,
+                           float* lse, int32_t B, int32_t M, int32_t H, int32_t hd, int64_t pos0, int32_t window,
+                           float scale, int32_t nsplit, void* stream) {
+  if (cap % 64 || cap < window + M || window < 1 || B < 1 || M < 0 || H < 1 || hd < 1)
+    return kfail(TTT_EINVAL, "cap must be a multiple of 64 and >= window + M");
+  if (nsplit < 1 || nsplit > 16) return kfail(TTT_EINVAL, "nsplit in 1..16");
+  const int64_t need = attn_ws_floats(B, M, H, hd, nsplit);
+  if (need > kScratchFloats) {
+    k_err = "the split partials need " + std::to_string(need) + " floats; the static scratch holds " +
+            std::to_string(kScratchFloats) + " (fewer splits, rows or heads per call)";
+    return TTT_EINVAL;
+  }
+  float* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return kfail(TTT_EHIP, hipGetErrorString(e));
+  }
+  return attn_fwd_ws(dtype, q, kc, vc, cap, o, lse, B, M, H, hd, pos0, window, scale, nsplit, ws, stream);
 }
 
 int ttt_k_attn_bwd(int32_t dtype, const void* q, const void* kc, const void* vc, int32_t cap, const float* lse,

@@ -83,3 +83,17 @@ def test_mini_batch_alignment_rejected_at_create():
         assert lib.ttt_model_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(h)) == -1
         assert b"NULL" in lib.ttt_last_error()
 
+
+def test_noalloc_attention_rejects_oversize_before_any_device_call():
+    """The allocation-free attention forward checks its split partials
+    against the static scratch (16 Mi floats) on the host."""
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.skip("library not built")
+    lib = bd.load()
+    rc = lib.ttt_k_attn_fwd_noalloc(1, None, None, None, 9216, None, None, 2, 1024, 24, 128, 8192, 8192, 0.1, 4,
+                                    None)
+    assert rc == -1 and b"static scratch" in lib.ttt_k_last_error()
+    assert b"25559040" in lib.ttt_k_last_error()          # 4 splits * 2 * 1024 rows * (3072 + 48)
+    rc = lib.ttt_k_attn_fwd_noalloc(1, None, None, None, 9216, None, None, 1, 1024, 24, 128, 8192, 8192, 0.1, 17,
+                                    None)
+    assert rc == -1 and b"nsplit" in lib.ttt_k_last_error()
