@@ -24,10 +24,14 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 MFMA_PEAK = 2.5e15   # MI355X dense bf16 MFMA, flop/s
 HBM_PEAK = 8.0e12    # MI355X HBM3E, bytes/s
-# HBM bytes per launch of the roofline kernel, measured with rocprofv3 counters
-# (FETCH_SIZE, WRITE_SIZE) and scaled by the same counters on a plain copy; the
-# record names the hash of the GEMM source it was taken on and is ignored once
-# that source changes
+# HBM bytes per launch, measured with rocprofv3 counters (FETCH_SIZE,
+# WRITE_SIZE) and scaled by the same counters on a plain copy: per kernel
+# class of the 3B prefill, and for the frozen prefix's MLP up-projection alone.
+# Each record names the hash of the sources it was taken on and is ignored once
+# they change.
+CLASS_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_3b_128k_class_counters.md")
+CLASS_SOURCES = [os.path.join(ROOT, "long_context_lm_token_amd", "csrc", f)
+                 for f in ("gemm.hip", "attention.hip", "elementwise.hip", "runtime.cpp")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mlp_up_traffic_3b_span.md")
 GEMM_SOURCE = os.path.join(ROOT, "long_context_lm_token_amd", "csrc", "gemm.hip")
 
@@ -36,18 +40,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_bytes(kernel_class):
-    """Stored HBM bytes per launch for the kernel class, or None."""
-    if kernel_class != "mlp_up" or not os.path.exists(TRAFFIC_RECORD):
+def traffic_bytes(kernel_class, config):
+    """Stored HBM bytes per launch for the kernel class (3B prefill), or None."""
+    if config != "3b":
         return None
-    text = open(TRAFFIC_RECORD).read()
-    h = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
-    v = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if kernel_class == "mlp_up":
+        if not os.path.exists(TRAFFIC_RECORD):
+            return None
+        text = open(TRAFFIC_RECORD).read()
+        h = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+        v = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+        if not h or not v or hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest() != h.group(1):
+            return None
+        return int(v.group(1))
+    if not os.path.exists(CLASS_TRAFFIC):
+        return None
+    text = open(CLASS_TRAFFIC).read()
+    h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    v = re.search(r"traffic_bytes_per_launch %s:\s*([0-9]+)" % re.escape(kernel_class), text)
     if not h or not v:
         return None
-    if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest() != h.group(1):
-        return None
-    return int(v.group(1))
+    cur = hashlib.sha256(b"".join(open(f, "rb").read() for f in CLASS_SOURCES)).hexdigest()
+    return int(v.group(1)) if cur == h.group(1) else None
 
 
 def probe():
@@ -200,11 +214,11 @@ def main():
     if k_bytes / HBM_PEAK > k_flops / MFMA_PEAK:
         achieved = k_bytes / (k_ms / 1000) / 1e9 if k_ms > 0 else 0.0
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic_bytes(prof_class)}
+                "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic_bytes(prof_class, args.config)}
     else:
         achieved = k_flops / (k_ms / 1000) / 1e12 if k_ms > 0 else 0.0
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK / 1e12, "unit": "TFLOP/s",
-                "frac": round(achieved * 1e12 / MFMA_PEAK, 4), "traffic": traffic_bytes(prof_class)}
+                "frac": round(achieved * 1e12 / MFMA_PEAK, 4), "traffic": traffic_bytes(prof_class, args.config)}
     roof.update({"kernel": prof_class, "launches": k_launch,
                  "avg_launch_us": round(k_ms * 1000 / max(k_launch, 1), 2),
                  "step_frac": round(step_flops / peak_bf16 / (ms_step / 1000), 4),
