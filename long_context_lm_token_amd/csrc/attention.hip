@@ -1256,36 +1256,45 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
 }
 
+// workgroup barrier that orders LDS only: this wave's LDS accesses are done,
+// global loads and stores may still be in flight (__syncthreads would wait
+// for them too)
+TTT_DEV void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// base + a 32-bit byte offset (lets the load take a scalar base address)
+TTT_DEV const void* gaddr(const void* base, uint32_t bytes) { return static_cast<const char*>(base) + bytes; }
+
 // dK / dV kernel for bf16 with head dim 128: the computation of
-// attn_bwd_dkdv_kernel with eight waves per workgroup. Waves w and w+4 own
-// the same 32 keys (K, V fragments in registers) and take the two 32-query
-// halves of every 64-query tile, so two waves share each SIMD and each walks
-// half of the work; their partial dK, dV are summed through LDS at the end.
-// Q and dO tiles go straight into LDS (read both row-wise and transposed:
-// swizzle 2), the per-query statistics by 4-byte DMA; the mask is applied
-// only on tiles that cross the diagonal, the window edge or the last row.
+// attn_bwd_dkdv_kernel, balanced. The chunk's keys form blocks of 64; a
+// workgroup takes block x and block nkb-1-x in turn (nkb = blocks in the
+// chunk), so an early block, which many queries see, rides with a late one,
+// which few do: with a window of at least the chunk every workgroup walks the
+// same number of query tiles. Eight waves: wave w owns keys 32 (w % 2) .. +31
+// of the block (K fragments in registers, the block's V rows in LDS) and
+// queries 32 (w / 2) .. +31 of every 128-query tile; Q and dO tiles go
+// straight into a two-stage LDS ring (read both row-wise and transposed:
+// swizzle 2), the per-query statistics by 4-byte DMA. The four waves that
+// share keys sum their partial dK, dV through LDS, in a fixed order, once per
+// block, while the next block's first tile is loading.
 constexpr int DKDV_NT = 512;
+constexpr int DK_KB = 64;   // keys per block
+constexpr int DK_QT = 128;  // queries per tile
 __global__ __launch_bounds__(DKDV_NT) void attn_bwd_dkdv_dl_kernel(AttnArgs a) {
   constexpr int NKS = FD_HD / 16, DB = FD_HD / 32;
-  // Q tiles, then dO tiles (one array: the final exchange reuses all 64 KB)
-  __shared__ __attribute__((aligned(1024))) bf16 sQD[2][2][BQT * FD_HD];
-  __shared__ __attribute__((aligned(1024))) bf16 sVk[QB * FD_HD];  // this block's V rows
-  __shared__ __attribute__((aligned(16))) float sL[2][BQT], sDl[2][BQT];
-  bf16 (&sQ)[2][BQT * FD_HD] = sQD[0];
-  bf16 (&sD)[2][BQT * FD_HD] = sQD[1];
+  constexpr int XF = DB * 16 * 64;  // floats of one wave's dK (or dV) partial
+  // [stage][Q, dO][128 rows]: 128 KB; a stage doubles as the exchange buffer
+  __shared__ __attribute__((aligned(1024))) bf16 sQD[2][2][DK_QT * FD_HD];
+  __shared__ __attribute__((aligned(1024))) bf16 sVk[DK_KB * FD_HD];  // the block's V rows
+  __shared__ __attribute__((aligned(16))) float sL[2][DK_QT], sDl[2][DK_QT];
 
   const Blk bk = blk();
   const int s = bk.z, h = bk.y;
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int kq = w & 3, qg = w >> 2;  // key group, query half
+  const int kq = w & 1, qg = w >> 1;  // key half, query quarter
   const int M = a.M;
-  const int kb0 = bk.x * QB;
-  const int kw0 = kb0 + kq * WQ;
-  const int kr = kw0 + (lane & 31);  // key row within the chunk
-  const bool kvalid = kr < M;
+  const int nkb = (M + DK_KB - 1) / DK_KB;
   const int pos0 = (int)a.pos0;
-  const int pk = pos0 + (kvalid ? kr : M - 1);
   const int win = a.window;
   const bf16* Kc = reinterpret_cast<const bf16*>(a.kc) + s * a.seq_stride + h * FD_HD;
   const bf16* Vc = reinterpret_cast<const bf16*>(a.vc) + s * a.seq_stride + h * FD_HD;
@@ -1293,161 +1302,224 @@ __global__ __launch_bounds__(DKDV_NT) void attn_bwd_dkdv_dl_kernel(AttnArgs a) {
   const bf16* DO = reinterpret_cast<const bf16*>(a.dout) + (int64_t)s * M * a.lddo + h * FD_HD;
   const float* LSE = a.lse + ((int64_t)s * a.H + h) * M;
   const float* DLT = a.delta + ((int64_t)s * a.H + h) * M;
+  const float c2 = a.scale * LOG2E;
 
-  // K fragments in registers; the block's V rows (keys kb0 .., ring slots,
-  // past the last key the last one) in LDS, 4 one-KB loads per wave
+  // the (one or two) key blocks of this workgroup and their query tiles
+  // [qs, qs + 128 n): the queries that can see a key of block x lie in
+  // [64 x, min(M, last key + win))
+  int xb[2], qs[2], nq[2];
+  const int nblk = (bk.x == nkb - 1 - bk.x) ? 1 : 2;
+  xb[0] = bk.x;
+  xb[1] = nkb - 1 - bk.x;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int k0 = xb[b] * DK_KB, klast = min(k0 + DK_KB, M) - 1;
+    const int q_end = min(M, klast + win);
+    qs[b] = k0 & ~(DK_QT - 1);
+    nq[b] = (b < nblk && q_end > qs[b]) ? (q_end - qs[b] + DK_QT - 1) / DK_QT : 0;
+  }
+  const int nt = nq[0] + nq[1];
+
+  // this wave's 4 + 4 of the 64 one-KB loads of a tile (rows past the last
+  // query read the last row: their weights are masked to 0); waves 0..3 also
+  // bring 64 of the tile's log-sum-exps or deltas (4 bytes a lane)
+  // (offsets recomputed at each issue: registers are the scarce resource)
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int q0 = t < nq[0] ? qs[0] + t * DK_QT : qs[1] + (t - nq[0]) * DK_QT;
+    const int st = t & 1;
+    // addresses as a uniform base + a 32-bit byte offset per lane (the
+    // launcher checks that the operands span less than 4 GiB): 64-bit
+    // addresses per row would cost 16 registers
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rt = (w * 4 + i) * 4 + (lane >> 4);
+      const uint32_t c8 = (uint32_t)(((lane & 15) ^ fd_swz<2>(rt)) * 8);
+      const uint32_t r = (uint32_t)min(q0 + rt, M - 1);
+      __builtin_amdgcn_global_load_lds(gaddr(Q, (r * (uint32_t)a.ldq + c8) * 2),
+                                       (fd_lds_t*)(sQD[st][0] + (w * 4 + i) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gaddr(DO, (r * (uint32_t)a.lddo + c8) * 2),
+                                       (fd_lds_t*)(sQD[st][1] + (w * 4 + i) * 512), 16, 0, 0);
+    }
+    if (w < 4) {
+      const uint32_t r = (uint32_t)min(q0 + (w >> 1) * 64 + lane, M - 1);
+      __builtin_amdgcn_global_load_lds(gaddr((w & 1) ? DLT : LSE, r * 4),
+                                       (fd_lds_t*)(((w & 1) ? sDl[st] : sL[st]) + (w >> 1) * 64), 4, 0, 0);
+    }
+  };
+  // K fragments of this lane's key (registers) and the block's 64 V rows
+  // (ring slots; past the last key the last one), 2 one-KB loads per wave
   bf16x8 kf[NKS];
-  {
+  int kb0 = 0, kr = 0;
+  bool kvalid = false;
+  auto load_keys = [&](int b) __attribute__((always_inline)) {
+    kb0 = xb[b] * DK_KB;
+    kr = kb0 + kq * WQ + (lane & 31);
+    kvalid = kr < M;
+    const int pk = pos0 + (kvalid ? kr : M - 1);
     const bf16* krow = Kc + (int64_t)(pk % a.cap) * a.ldk;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) kf[ks] = kvalid ? *reinterpret_cast<const bf16x8*>(krow + ks * 16 + hl * 8) : bf16x8{};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (w * 4 + i) * 4 + (lane >> 4);
-      const int64_t slot = (pos0 + min(kb0 + r, M - 1)) % a.cap;
-      __builtin_amdgcn_global_load_lds((const void*)(Vc + slot * a.ldk + ((lane & 15) ^ fd_swz<0>(r)) * 8),
-                                       (fd_lds_t*)(sVk + (w * 4 + i) * 512), 16, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int r = (w * 2 + i) * 4 + (lane >> 4);
+      const uint32_t slot = (uint32_t)((pos0 + min(kb0 + r, M - 1)) % a.cap);
+      __builtin_amdgcn_global_load_lds(
+          gaddr(Vc, (slot * (uint32_t)a.ldk + (uint32_t)(((lane & 15) ^ fd_swz<0>(r)) * 8)) * 2),
+          (fd_lds_t*)(sVk + (w * 2 + i) * 512), 16, 0, 0);
     }
-  }
-  const float c2 = a.scale * LOG2E;
-  const int klast_blk = min(kb0 + QB, M) - 1;
-  const bool wactive = kw0 < M;
-  const int wk_first = kw0, wk_last = min(kw0 + WQ, M) - 1;
-  // query tiles that can see keys of this block: [kb0, klast_blk + win - 1]
-  const int q_end = min(M, klast_blk + win);
-  const int q_start = kb0 & ~(BQT - 1);
-  const int nt = q_end > q_start ? (q_end - q_start + BQT - 1) / BQT : 0;
+  };
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
-  // this wave's 2 of the 16 one-KB loads of a 64-row tile (rows past the
-  // last query read the last row: their weights are masked to 0); waves 0
-  // and 1 also bring the tile's 64 log-sum-exps / deltas (4 bytes a lane)
-  uint32_t qoff[2];
-  int qrow[2];
+  // Sum the four query quarters' partials of each key half through one stage
+  // of the ring (64 KB: [2 slots][2 key halves][XF], lane-contiguous), in a
+  // fixed order, (v0 + v2) + (v1 + v3), ending in slot 0; then all 512
+  // threads store the block's rows from there, 16 bytes at a time (each
+  // takes 4 consecutive columns of one key). dK first, then dV. Each step
+  // touches one of the two register arrays only (steps that pick between
+  // them by a condition get merged into one by address, which takes both
+  // out of registers).
+  auto reduce_store = [&](float* X, f32x16 (&v)[DB], float* outp, float sc, int kbase)
+                          __attribute__((always_inline)) {
+    if (qg >= 2) {
+      float* x = X + ((qg - 2) * 2 + kq) * XF;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (w * 2 + i) * 4 + (lane >> 4);
-    qrow[i] = r;
-    qoff[i] = (uint32_t)(((lane & 15) ^ fd_swz<2>(r)) * 8);
-  }
-  auto issue = [&](int t) {
-    const int q0 = q_start + t * BQT, b = t & 1;
+      for (int i = 0; i < DB; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t r = min(q0 + qrow[i], M - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(Q + r * a.ldq + qoff[i]), (fd_lds_t*)(sQ[b] + (w * 2 + i) * 512),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(DO + r * a.lddo + qoff[i]),
-                                       (fd_lds_t*)(sD[b] + (w * 2 + i) * 512), 16, 0, 0);
+        for (int e = 0; e < 16; ++e) x[(i * 16 + e) * 64 + lane] = v[i][e];
     }
-    if (w < 2) {
-      const float* src = (w == 0 ? LSE : DLT) + min(q0 + lane, M - 1);
-      __builtin_amdgcn_global_load_lds((const void*)src, (fd_lds_t*)(w == 0 ? sL[b] : sDl[b]), 4, 0, 0);
+    lds_sync();
+    if (qg < 2) {
+      const float* x = X + (qg * 2 + kq) * XF;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[i][e] += x[(i * 16 + e) * 64 + lane];
     }
+    lds_sync();
+    if (qg == 1) {
+      float* x = X + kq * XF;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[(i * 16 + e) * 64 + lane] = v[i][e];
+    }
+    lds_sync();
+    if (qg == 0) {
+      float* x = X + kq * XF;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[(i * 16 + e) * 64 + lane] += v[i][e];
+    }
+    lds_sync();
+    // slot 0 element (i, e) of lane l is key 32 kh + l % 32, column
+    // 32 i + acc_row(e, l / 32); e = 4 g + 0..3 are 4 consecutive columns
+#pragma unroll
+    for (int j = 0; j < 2 * XF / 4 / DKDV_NT; ++j) {
+      const int g = j * DKDV_NT + (int)threadIdx.x;
+      const int l = g & 63, grp = (g >> 6) & (XF / 256 - 1), kh = g / (XF / 4);
+      const int i = grp >> 2, eg = grp & 3;
+      const float* x = X + kh * XF + (i * 16 + eg * 4) * 64 + l;
+      const f32x4 val = {x[0] * sc, x[64] * sc, x[128] * sc, x[192] * sc};
+      const int r = kh * WQ + (l & 31);
+      if (kbase + r < M)
+        *reinterpret_cast<f32x4*>(outp + ((int64_t)s * M + kbase + r) * a.lddk + h * FD_HD + i * 32 + eg * 8 +
+                                  (l >> 5) * 4) = val;
+    }
+    lds_sync();  // slot 0 is read before it is written again
+  };
+  // the block's dK (scaled) and dV; `next` >= 0 loads that block's K
+  // fragments and V rows meanwhile (sVk is free: every wave is past this
+  // block's tiles)
+  auto finish = [&](int st, int next) __attribute__((always_inline)) {
+    float* X = reinterpret_cast<float*>(&sQD[st][0][0]);
+    lds_sync();  // every wave is past its last tile of this block
+    const int kb_done = kb0;
+    reduce_store(X, dk, a.dk, a.scale, kb_done);
+    if (next >= 0) load_keys(next);
+    reduce_store(X, dv, a.dv, 1.f, kb_done);
+#pragma unroll
+    for (int i = 0; i < DB; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
   };
 
-  if (nt > 0) issue(0);
-  for (int t = 0; t < nt; ++t) {
-    // this wave's loads of tile t are the only ones in flight; after the
-    // barrier every wave's are in LDS and tile t-1 is no longer read
-    fd_wait_loads();
-    __syncthreads();
-    if (t + 1 < nt) issue(t + 1);
-    const int qa = q_start + t * BQT + qg * WQ;  // this wave's 32 queries: qa ..
-    // does any (query, key) pair satisfy 0 <= q - k < win ?
-    if (!wactive || qa + WQ - 1 < wk_first || qa > wk_last + win - 1) continue;
-    const int b = t & 1;
-    const bf16* cQ = sQ[b];
-    const bf16* cD = sD[b];
-    f32x16 p = f32x16{}, dp = f32x16{};
-    const int row = qg * WQ + (lane & 31);
+  load_keys(0);
+  issue(0);  // (nt >= 1: see the end)
+  int t = 0;
+#pragma nounroll
+  for (int blkno = 0; blkno < nblk; ++blkno) {
+    const int tend = blkno == 0 ? nq[0] : nt;
+    for (; t < tend; ++t) {
+      // this wave's loads of tile t (and of the block's V rows) are the only
+      // ones in flight; after the barrier every wave's are in LDS and tile
+      // t-1 is no longer read
+      fd_wait_loads();
+      __syncthreads();
+      if (t + 1 < nt) issue(t + 1);
+      const int b = t & 1;
+      const int q0 = t < nq[0] ? qs[0] + t * DK_QT : qs[1] + (t - nq[0]) * DK_QT;
+      const int qa = q0 + qg * WQ;  // this wave's 32 queries: qa ..
+      const int kw0 = kb0 + kq * WQ;
+      const int wk_first = kw0, wk_last = min(kw0 + WQ, M) - 1;
+      // does any (query, key) pair satisfy 0 <= q - k < win ?
+      if (kw0 < M && !(qa + WQ - 1 < wk_first || qa > wk_last + win - 1)) {
+        const bf16* cQ = sQD[b][0];
+        const bf16* cD = sQD[b][1];
+        f32x16 p = f32x16{}, dp = f32x16{};
+        const int row = qg * WQ + (lane & 31);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      p = mfma(fd_frag<2>(cQ, row, ks * 2 + hl), kf[ks], p);
-      dp = mfma(fd_frag<2>(cD, row, ks * 2 + hl), fd_frag<0>(sVk, kq * WQ + (lane & 31), ks * 2 + hl), dp);
-      // fragments are read a couple of steps ahead, not all at once (with
-      // 160 registers of keys and accumulators held, more would spill)
-      if (ks & 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    // rows of the accumulators are queries: acc_row(e, hl) = 8 (e/4) + 4 hl + e%4,
-    // so each group of 4 registers takes 4 consecutive statistics
-    const float* Lq = &sL[b][qg * WQ + hl * 4];
-    const float* Dq = &sDl[b][qg * WQ + hl * 4];
+        for (int ks = 0; ks < NKS; ++ks) {
+          p = mfma(fd_frag<2>(cQ, row, ks * 2 + hl), kf[ks], p);
+          dp = mfma(fd_frag<2>(cD, row, ks * 2 + hl), fd_frag<0>(sVk, kq * WQ + (lane & 31), ks * 2 + hl), dp);
+          if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+        // accumulator rows are queries: acc_row(e, hl) = 8 (e/4) + 4 hl + e%4
+        const float* Lq = &sL[b][qg * WQ + hl * 4];
+        const float* Dq = &sDl[b][qg * WQ + hl * 4];
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lq + k4 * 8);
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lq + k4 * 8);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[k4 * 4 + e] = ex2(fmaf(p[k4 * 4 + e], c2, -l4[e] * LOG2E));
-    }
-    const bool full = qa - wk_last >= 0 && qa + WQ - 1 - wk_first < win && qa + WQ - 1 < M && wk_last == kw0 + WQ - 1;
-    if (!full) {
-      asm volatile("" ::: "memory");  // a real branch, not selects
-      // visible iff 0 <= q - k < win, the query row exists and the key does
-      const int dq0 = qa + hl * 4 - kr;
+          for (int e = 0; e < 4; ++e) p[k4 * 4 + e] = ex2(fmaf(p[k4 * 4 + e], c2, -l4[e] * LOG2E));
+        }
+        const bool full =
+            qa - wk_last >= 0 && qa + WQ - 1 - wk_first < win && qa + WQ - 1 < M && wk_last == kw0 + WQ - 1;
+        if (!full) {
+          asm volatile("" ::: "memory");  // a real branch, not selects
+          // visible iff 0 <= q - k < win, the query row exists and the key does
+          const int dq0 = qa + hl * 4 - kr;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int dqe = dq0 + (e >> 2) * 8 + (e & 3);
-        if ((unsigned)dqe >= (unsigned)win || qa + (e >> 2) * 8 + hl * 4 + (e & 3) >= M || !kvalid) p[e] = 0.f;
+          for (int e = 0; e < 16; ++e) {
+            const int dqe = dq0 + (e >> 2) * 8 + (e & 3);
+            if ((unsigned)dqe >= (unsigned)win || qa + (e >> 2) * 8 + hl * 4 + (e & 3) >= M || !kvalid) p[e] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dq + k4 * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[k4 * 4 + e] = p[k4 * 4 + e] * (dp[k4 * 4 + e] - d4[e]);  // dS
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pf = acc_frag<bf16>(p, u), sf = acc_frag<bf16>(dp, u);
+#pragma unroll
+          for (int i = 0; i < DB; ++i) dv[i] = mfma(fd_frag_tr<2>(cD, i * 32, qg, u, lane), pf, dv[i]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < DB; ++i) dk[i] = mfma(fd_frag_tr<2>(cQ, i * 32, qg, u, lane), sf, dk[i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dq + k4 * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dp[k4 * 4 + e] = p[k4 * 4 + e] * (dp[k4 * 4 + e] - d4[e]);  // dS
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bf16x8 pf = acc_frag<bf16>(p, u), sf = acc_frag<bf16>(dp, u);
-#pragma unroll
-      for (int i = 0; i < DB; ++i) dv[i] = mfma(fd_frag_tr<2>(cD, i * 32, qg, u, lane), pf, dv[i]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < DB; ++i) dk[i] = mfma(fd_frag_tr<2>(cQ, i * 32, qg, u, lane), sf, dk[i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // the block's sums use the stage of its last tile (the next block's first
+    // tile, if any, is loading into the other one)
+    finish((t - 1) & 1, blkno + 1 < nblk ? 1 : -1);
   }
-
-  // sum the two query halves' partials: dK, then dV, through the ring's LDS
-  // (per key group 4 x 16 x 64 floats, lane-contiguous)
-  float* xch = reinterpret_cast<float*>(&sQD[0][0][0]);
-  float* xg = xch + kq * (DB * 16 * 64);
-  __syncthreads();
-  if (qg == 1) {
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) xg[(i * 16 + e) * 64 + lane] = dk[i][e];
-  }
-  __syncthreads();
-  if (qg == 0) {
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) dk[i][e] += xg[(i * 16 + e) * 64 + lane];
-  }
-  __syncthreads();
-  if (qg == 1) {
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) xg[(i * 16 + e) * 64 + lane] = dv[i][e];
-  }
-  __syncthreads();
-  if (qg == 1 || !wactive || !kvalid) return;
-  float* dko = a.dk + ((int64_t)s * M + kr) * a.lddk + h * FD_HD;
-  float* dvo = a.dv + ((int64_t)s * M + kr) * a.lddk + h * FD_HD;
-#pragma unroll
-  for (int i = 0; i < DB; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int d = i * 32 + acc_row(e, hl);
-      dko[d] = dk[i][e] * a.scale;
-      dvo[d] = dv[i][e] + xg[(i * 16 + e) * 64 + lane];
-    }
+  // (every key sees at least its own query when window >= 1, so each block
+  // has a tile and every key's dK, dV are written above)
 }
 
 template <typename T, int HD>
@@ -1485,13 +1557,20 @@ hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.parts == 1) return e;
   }
-  dim3 grid2((a.M + QB - 1) / QB, a.H, a.B);
+  // (the direct-to-LDS kernel addresses one sequence's q, dO rows and ring
+  // slots with 32-bit byte offsets)
+  const bool small = (int64_t)a.M * std::max(a.ldq, a.lddo) * 2 < (1ll << 32) &&
+                     (int64_t)a.cap * a.ldk * 2 < (1ll << 32);
   const bool dl = sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && al16(a.q) &&
-                  al16(a.dout) && a.ldk % 8 == 0 && a.seq_stride % 8 == 0 && a.ldq % 8 == 0 && a.lddo % 8 == 0;
-  if (dl)
-    hipLaunchKernelGGL(attn_bwd_dkdv_dl_kernel, grid2, dim3(DKDV_NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid2, dim3(NT), 0, st, a);
+                  al16(a.dout) && al16(a.dk) && al16(a.dv) && a.ldk % 8 == 0 && a.seq_stride % 8 == 0 &&
+                  a.ldq % 8 == 0 && a.lddo % 8 == 0 && a.lddk % 4 == 0 && small;
+  if (dl) {
+    // key blocks of 64 in pairs
+    const int nkb = (a.M + DK_KB - 1) / DK_KB;
+    hipLaunchKernelGGL(attn_bwd_dkdv_dl_kernel, dim3((nkb + 1) / 2, a.H, a.B), dim3(DKDV_NT), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), dim3((a.M + QB - 1) / QB, a.H, a.B), dim3(NT), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -185,7 +185,7 @@ TTT_DEV void store_out(const GemmArgs& p, int z, int row, int col, float v, floa
 // master and the row-major copy are updated directly (lanes along columns).
 template <typename T, int BM, int BN, int WGM, int WGN>
 TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
-                                 T* lds) {
+                                 T* lds, const float (&pre)[BM / WGM / 32][BN / WGN / 32][16], bool use_pre) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN, TI = WTM / 32, TJ = WTN / 32;
   constexpr int NT = WGM * WGN * 64;
   constexpr int LT = BM + 8;  // row stride of the [col][row] staging tile
@@ -204,7 +204,7 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-        mv[j][r] = (row < p.M && col < p.N) ? Wm[(int64_t)row * p.ldw + col] : 0.f;
+        mv[j][r] = use_pre ? pre[i][j][r] : (row < p.M && col < p.N) ? Wm[(int64_t)row * p.ldw + col] : 0.f;
       }
     }
 #pragma unroll
@@ -253,7 +253,8 @@ TTT_DEV void sgd_epilogue_staged(const GemmArgs& p, int z, int m0, int n0, const
 // accumulator sets through scratch).
 template <bool CHECK, typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
 TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane,
-                      const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part) {
+                      const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part,
+                      const float (&pre)[BM / WGM / 32][BN / WGN / 32][16], bool use_pre) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TI = WTM / 32, TJ = WTN / 32;
   if (splits > 1) {
@@ -373,7 +374,9 @@ TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, 
           for (int r = 0; r < 16; ++r) {
             const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
             in[j][r] = 0.f;
-            if (!CHECK || (row < p.M && col < p.N))
+            if (use_pre)
+              in[j][r] = pre[i][j][r];
+            else if (!CHECK || (row < p.M && col < p.N))
               in[j][r] = EPI == EPI_ADD ? p.R[z * p.sR + (int64_t)row * p.ldr + col]
                                         : p.Wm[z * p.sW + (int64_t)row * p.ldw + col];
           }
@@ -396,19 +399,53 @@ TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, 
 
 // Epilogue of one block: split-K partials, or the EPI operation on the
 // accumulators of wave (wm, wn). smem: the block's LDS (staged SGD copy).
+// pre / use_pre: the epilogue operand (residual or fp32 master) of this
+// lane's accumulators, already loaded (see prefetch_operand)
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
 TTT_DEV void gemm_epilogue(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane,
-                           const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part, T* smem) {
+                           const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part, T* smem,
+                           const float (&pre)[BM / WGM / 32][BN / WGN / 32][16], bool use_pre) {
   if constexpr (EPI == EPI_SGD && sizeof(T) == 2) {
     if (splits == 1 && p.C2) {
-      sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, smem);
+      sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, smem, pre, use_pre);
       return;
     }
   }
   if (m0 + BM <= p.M && n0 + BN <= p.N)
-    epi_body<false, T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part);
+    epi_body<false, T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, pre, use_pre);
   else
-    epi_body<true, T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part);
+    epi_body<true, T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, pre, use_pre);
+}
+
+// The residual of an unsplit EPI_ADD tile at this lane's accumulator
+// positions, loaded before the main loop so that the epilogue does not wait
+// for it; only for wave tiles of at most 4 MFMA tiles (64 more registers,
+// which keeps two waves per SIMD). The SGD epilogue's fp32 master is not
+// prefetched: holding it lifts that kernel past 256 registers, one wave per
+// SIMD, and measured twice as slow.
+template <int BM, int BN, int WGM, int WGN, int EPI>
+TTT_DEV bool prefetch_operand(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane, int splits,
+                              float (&pre)[BM / WGM / 32][BN / WGN / 32][16]) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN, TI = WTM / 32, TJ = WTN / 32;
+  if constexpr (EPI == EPI_ADD && TI * TJ <= 4) {
+    if (splits != 1) return false;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          pre[i][j][r] = 0.f;
+          if (row < p.M && col < p.N)
+            pre[i][j][r] = p.R[z * p.sR + (int64_t)row * p.ldr + col];
+        }
+      }
+    return true;
+  } else {
+    return false;
+  }
 }
 
 
@@ -484,7 +521,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     __syncthreads();
   }
 
-  gemm_epilogue<T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, &smem[0][0]);
+  float pre[TI][TJ][16];
+  const bool use_pre = prefetch_operand<BM, BN, WGM, WGN, EPI>(p, z, m0, n0, wm, wn, lane, splits, pre);
+  gemm_epilogue<T, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, &smem[0][0], pre,
+                                                use_pre);
 }
 
 // ---------------- direct-to-LDS variant (bf16, K % BK == 0) ----------------
@@ -609,6 +649,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int
   // the range): tiles that share an operand panel then ask for a given K
   // slice an iteration or more apart, so one takes the miss beyond L2 and the
   // others find the slice in L2, instead of all waiting on the same miss
+  // the epilogue's residual / master values, in flight during the main loop
+  float pre[TI][TJ][16];
+  const bool use_pre = prefetch_operand<BM, BN, WGM, WGN, EPI>(p, z, m0, n0, wm, wn, lane, splits, pre);
   const int nkt = kt1 - kt0;
   const int rot = nkt > 0 ? (tm + tn) % nkt : 0;
   auto issue = [&](int kt, int st) {
@@ -694,7 +737,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int
     }
   }
   __syncthreads();
-  gemm_epilogue<bf16, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, &smem[0][0]);
+  gemm_epilogue<bf16, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, &smem[0][0], pre,
+                                                   use_pre);
 }
 
 // sum split-K partials in order and apply the epilogue
