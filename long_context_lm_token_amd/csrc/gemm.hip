@@ -399,12 +399,95 @@ TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, 
 
 // Epilogue of one block: split-K partials, or the EPI operation on the
 // accumulators of wave (wm, wn). smem: the block's LDS (staged SGD copy).
+// The SGD epilogue of a full 128 x 128 bf16 tile (2 x 2 waves of 64 x 64)
+// with wide memory accesses: the fp32 master is read as float4 rows (512
+// bytes per row of the tile); per half of 64 rows, the owning waves stage
+// lr * acc in LDS ([64][132] fp32), and each thread updates 4 consecutive
+// columns of 8 rows: the
+// master written back with 16-byte stores, the row-major bf16 copy with
+// 8-byte stores, and the transposed copy staged ([128 cols][72] bf16) for
+// 16-byte stores of 8 rows. Same arithmetic as sgd_epilogue_staged.
+constexpr int SGDV_LA = 128 + 4, SGDV_LT = 64 + 8;
+constexpr int SGDV_LDS = 64 * SGDV_LA * 4 + 128 * SGDV_LT * 2;
+TTT_DEV bool sgd_vec_ok(const GemmArgs& p, int m0, int n0) {
+  const auto al = [](const void* q, int b) { return reinterpret_cast<uintptr_t>(q) % b == 0; };
+  return m0 + 128 <= p.M && n0 + 128 <= p.N && p.ldw % 4 == 0 && p.sW % 4 == 0 && al(p.Wm, 16) &&
+         (!p.C || (p.ldc % 4 == 0 && p.sC % 4 == 0 && al(p.C, 8))) && p.ldc2 % 8 == 0 && p.sC2 % 8 == 0 &&
+         al(p.C2, 16);
+}
+TTT_DEV void sgd_epilogue_vec(const GemmArgs& p, int z, int m0, int n0, const f32x16 (&acc)[2][2], void* lds) {
+  float* A = reinterpret_cast<float*>(lds);
+  bf16* Tt = reinterpret_cast<bf16*>(A + 64 * SGDV_LA);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1, hl = lane >> 5;
+  const int c4 = tid & 31, rr = tid >> 5;  // 4 columns from 4 c4; rows rr, rr + 8, ...
+  float* Wm = p.Wm + z * p.sW;
+  bf16* C = p.C ? reinterpret_cast<bf16*>(p.C) + z * p.sC : nullptr;
+  bf16* C2 = reinterpret_cast<bf16*>(p.C2) + z * p.sC2;
+  const int col = n0 + c4 * 4;
+  // one half's master values at a time (two would lift the kernel past 256
+  // registers): the second half's loads go out as soon as the first half's
+  // are consumed, ahead of the first half's transposed stores
+  f32x4 mv[8];
+  auto load_master = [&](int h) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      mv[k] = *reinterpret_cast<const f32x4*>(Wm + (int64_t)(m0 + h * 64 + k * 8 + rr) * p.ldw + col);
+  };
+  load_master(0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            A[(i * 32 + (e >> 2) * 8 + hl * 4 + (e & 3)) * SGDV_LA + wn * 64 + j * 32 + (lane & 31)] =
+                p.lr * acc[i][j][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = k * 8 + rr, row = m0 + h * 64 + r;
+      const f32x4 g = *reinterpret_cast<const f32x4*>(A + r * SGDV_LA + c4 * 4);
+      f32x4 nw;
+      bf16x4 cv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        nw[q] = mv[k][q] - g[q];
+        cv[q] = round_copy<bf16>(nw[q], p.sr_seed, z, row, col + q);
+        Tt[(c4 * 4 + q) * SGDV_LT + r] = cv[q];
+      }
+      *reinterpret_cast<f32x4*>(Wm + (int64_t)row * p.ldw + col) = nw;
+      if (C) *reinterpret_cast<bf16x4*>(C + (int64_t)row * p.ldc + col) = cv;
+    }
+    if (h == 0) load_master(1);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ch = q * 256 + tid, cl = ch >> 3, rs = (ch & 7) * 8;
+      *reinterpret_cast<bf16x8*>(C2 + (int64_t)(n0 + cl) * p.ldc2 + m0 + h * 64 + rs) =
+          *reinterpret_cast<const bf16x8*>(Tt + cl * SGDV_LT + rs);
+    }
+    __syncthreads();
+  }
+}
+
 // pre / use_pre: the epilogue operand (residual or fp32 master) of this
 // lane's accumulators, already loaded (see prefetch_operand)
-template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
+// LDS: the block's operand ring, LDS_BYTES long (free once the main loop is done)
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT, int LDS_BYTES = 0>
 TTT_DEV void gemm_epilogue(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, int lane,
                            const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int splits, float* part, T* smem,
                            const float (&pre)[BM / WGM / 32][BN / WGN / 32][16], bool use_pre) {
+  if constexpr (EPI == EPI_SGD && sizeof(T) == 2 && BM == 128 && BN == 128 && WGM == 2 && WGN == 2 &&
+                LDS_BYTES >= SGDV_LDS) {
+    if (splits == 1 && p.C2 && sgd_vec_ok(p, m0, n0)) {
+      sgd_epilogue_vec(p, z, m0, n0, acc, smem);
+      return;
+    }
+  }
   if constexpr (EPI == EPI_SGD && sizeof(T) == 2) {
     if (splits == 1 && p.C2) {
       sgd_epilogue_staged<T, BM, BN, WGM, WGN>(p, z, m0, n0, acc, smem, pre, use_pre);
@@ -616,7 +699,7 @@ TTT_DEV bf16x8 mn_frag(const bf16* t, int d0, int ks, int lane) {
 }
 
 template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT, bool MN = false>
-__global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int splits, float* part) {
+__global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 2 : 1) void gemm_dl_kernel(GemmArgs p, int splits, float* part) {
   static_assert(!MN || (BM == 128 && BN == 128 && BK == 64), "MN-major operands: 128 x 128 tiles, 64 deep");
   static_assert(EPI != EPI_SGD || BN * (BM + 8) <= S * (BM + BN) * BK, "the staged SGD tile must fit in the ring");
   static_assert(S >= 2 && S <= 4, "ring depth");
@@ -737,8 +820,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_dl_kernel(GemmArgs p, int
     }
   }
   __syncthreads();
-  gemm_epilogue<bf16, BM, BN, WGM, WGN, EPI, OutT>(p, z, m0, n0, wm, wn, lane, acc, splits, part, &smem[0][0], pre,
-                                                   use_pre);
+  gemm_epilogue<bf16, BM, BN, WGM, WGN, EPI, OutT, (int)sizeof(smem)>(p, z, m0, n0, wm, wn, lane, acc, splits, part,
+                                                                     &smem[0][0], pre, use_pre);
 }
 
 // sum split-K partials in order and apply the epilogue

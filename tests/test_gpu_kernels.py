@@ -164,10 +164,13 @@ def test_gemm_residual_add(dtype, tile):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("tile,ws", [(0, 0), (1, 0), (3, 1 << 22), (6, 0), (7, 1 << 22)])
 @pytest.mark.parametrize("sr_seed", [0, 12345])
-def test_gemm_sgd_epilogue(dtype, tile, ws, sr_seed):
-    """W <- W - lr * (gradient); both compute copies = the same rounding of W."""
+@pytest.mark.parametrize("M,N", [(96, 136), (256, 392)])
+def test_gemm_sgd_epilogue(dtype, tile, ws, sr_seed, M, N):
+    """W <- W - lr * (gradient); both compute copies = the same rounding of W.
+    256 x 392 has whole 128 x 128 tiles (the wide-access epilogue of the
+    direct-to-LDS kernels) beside a ragged column edge."""
     lr = 0.37
-    ref, got_c, got_w, got_c2 = run_gemm(dtype, 2, 96, 136, 1024, batch=2, lr=lr, tile=tile, ws_elems=ws,
+    ref, got_c, got_w, got_c2 = run_gemm(dtype, 2, M, N, 1024, batch=2, lr=lr, tile=tile, ws_elems=ws,
                                          sr_seed=sr_seed)
     np.testing.assert_allclose(got_w, ref, rtol=1e-5, atol=1e-4)
     np.testing.assert_array_equal(got_c2, got_c.transpose(0, 2, 1))
