@@ -67,7 +67,8 @@ enum ttt_mat { TTT_UP = 0, TTT_GATE = 1, TTT_DOWN = 2 };
  * batch = number of independent sequences, each with its own fast weights,
  * attention cache and position counter. max_positions bounds the stream
  * length (ids) per sequence. prefill_span bounds how many positions the
- * frozen lower blocks process per pass (0 = library default).
+ * frozen lower blocks process per pass (0 = library default: four
+ * mini-batches, at least 2048).
  * max_device_bytes (0 = unlimited) caps the library's allocation.
  * forward_only != 0 turns the inner loop off: every position is scored at
  * the initial weights and no backward or SGD step runs (the static model;
