@@ -99,6 +99,41 @@ __global__ void rmsnorm_fwd_kernel(const float* x, int d, const T* g, float eps,
   if (threadIdx.x == 0) rstd[r] = rs;
 }
 
+// The same with the row held in registers (C float4 per thread, d <= C*4*NT):
+// x is read once.
+template <typename T, int C>
+__global__ void rmsnorm_fwd_reg_kernel(const float* x, int d, const T* g, float eps, T* y, float* rstd) {
+  __shared__ float red[16];
+  const int64_t r = blockIdx.x;
+  const float* xr = x + r * d;
+  float v[C][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    const int c = (k * NT + threadIdx.x) * 4;
+    if (c < d) {
+      get4(xr + c, v[k]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += v[k][e] * v[k][e];
+    }
+  }
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / d + eps);
+  T* yr = y + r * d;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    const int c = (k * NT + threadIdx.x) * 4;
+    if (c < d) {
+      float gg[4];
+      get4(g + c, gg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[k][e] *= rs * gg[e];
+      put4(yr + c, v[k]);
+    }
+  }
+  if (threadIdx.x == 0) rstd[r] = rs;
+}
+
 // dx = r*g*dn - x * r^3 * mean(x*g*dn); dres (+)= dx; optional compute copy.
 // Four consecutive columns per thread (d % 4 == 0).
 template <typename T>
@@ -132,6 +167,50 @@ __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g
     for (int e = 0; e < 4; ++e) v[e] = rs * gv[e] * dv[e] - xv[e] * k + (accumulate ? v[e] : 0.f);
     put4(o + c, v);
     if (oc) put4(oc + c, v);
+  }
+}
+
+// The same with the row's x, dn (and dres) held in registers (d <= C*4*NT).
+template <typename T, int C>
+__global__ void rmsnorm_bwd_reg_kernel(const float* x, const float* rstd, const T* g, const float* dn,
+                                       int d, float* dres, T* dres_c, bool accumulate) {
+  __shared__ float red[16];
+  const int64_t r = blockIdx.x;
+  const float* xr = x + r * d;
+  const float* dr = dn + r * d;
+  float xv[C][4], gd[C][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    const int c = (k * NT + threadIdx.x) * 4;
+    if (c < d) {
+      float gv[4], dv[4];
+      get4(xr + c, xv[k]);
+      get4(g + c, gv);
+      get4(dr + c, dv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gd[k][e] = gv[e] * dv[e];
+        dot += xv[k][e] * gd[k][e];
+      }
+    }
+  }
+  dot = block_sum(dot, red);
+  const float rs = rstd[r];
+  const float kk = rs * rs * rs * dot / d;
+  float* o = dres + r * d;
+  T* oc = dres_c ? dres_c + r * d : nullptr;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    const int c = (k * NT + threadIdx.x) * 4;
+    if (c < d) {
+      float v[4];
+      if (accumulate) get4(o + c, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = rs * gd[k][e] - xv[k][e] * kk + (accumulate ? v[e] : 0.f);
+      put4(o + c, v);
+      if (oc) put4(oc + c, v);
+    }
   }
 }
 
@@ -509,6 +588,21 @@ hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, fl
                               float* rstd, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (d % 4) return hipErrorInvalidValue;
+  // rows of up to 4096 columns stay in registers (x read once)
+  const int C = (d + 4 * NT - 1) / (4 * NT);
+#define TTT_NORM_FWD(TT, CC) \
+  hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, d, cp<TT>(g), eps, mp<TT>(y), rstd)
+  if (C <= 4) {
+    if (dt == 1) {
+      if (C == 1) TTT_NORM_FWD(bf16, 1); else if (C == 2) TTT_NORM_FWD(bf16, 2);
+      else if (C == 3) TTT_NORM_FWD(bf16, 3); else TTT_NORM_FWD(bf16, 4);
+    } else {
+      if (C == 1) TTT_NORM_FWD(float, 1); else if (C == 2) TTT_NORM_FWD(float, 2);
+      else if (C == 3) TTT_NORM_FWD(float, 3); else TTT_NORM_FWD(float, 4);
+    }
+    return hipGetLastError();
+  }
+#undef TTT_NORM_FWD
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, d, cp<bf16>(g), eps, mp<bf16>(y), rstd),
       hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, d, cp<float>(g), eps, mp<float>(y), rstd));
@@ -519,6 +613,21 @@ hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, 
                               int d, float* dres, void* dres_c, bool accumulate, int dt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (d % 4) return hipErrorInvalidValue;
+  const int C = (d + 4 * NT - 1) / (4 * NT);
+#define TTT_NORM_BWD(TT, CC)                                                                                       \
+  hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, rstd, cp<TT>(g), dn, d, dres, \
+                     mp<TT>(dres_c), accumulate)
+  if (C <= 4) {
+    if (dt == 1) {
+      if (C == 1) TTT_NORM_BWD(bf16, 1); else if (C == 2) TTT_NORM_BWD(bf16, 2);
+      else if (C == 3) TTT_NORM_BWD(bf16, 3); else TTT_NORM_BWD(bf16, 4);
+    } else {
+      if (C == 1) TTT_NORM_BWD(float, 1); else if (C == 2) TTT_NORM_BWD(float, 2);
+      else if (C == 3) TTT_NORM_BWD(float, 3); else TTT_NORM_BWD(float, 4);
+    }
+    return hipGetLastError();
+  }
+#undef TTT_NORM_BWD
   DT_DISPATCH(dt,
       hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<bf16>(g), dn, d, dres, mp<bf16>(dres_c), accumulate),
       hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<float>(g), dn, d, dres, mp<float>(dres_c), accumulate));

@@ -447,8 +447,10 @@ def test_cross_entropy(dtype, V, rows):
 # ----------------------------- RMSNorm ---------------------------------------
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("d", [64, 3072])
+@pytest.mark.parametrize("d", [64, 2048, 3072, 4096, 4100])
 def test_rmsnorm(dtype, d):
+    """Rows of up to 4096 columns are held in registers (1 to 4 float4 per
+    thread); wider rows take the two-pass kernel (4100)."""
     lib = bd.load()
     rows = 19
     x, xd = rnd((rows, d), 7, torch.float32, scale=2.0)
