@@ -647,6 +647,33 @@ TTT_DEV void dl_issue(const bf16* __restrict__ base, int64_t ld, int row0, int n
   }
 }
 
+// The same loads with each lane's byte offset from the tile's first column
+// computed once (`off`, see dl_offsets) and a uniform base per K tile: a load
+// is then an M0 write and the load, with no 64-bit address arithmetic
+// (operands must span less than 4 GiB; the launcher checks).
+template <int ROWS, int NW, int BK>
+TTT_DEV void dl_offsets(int64_t ld, int row0, int nrows, int w, int lane, uint32_t (&off)[ROWS / DL<BK>::RPI / NW]) {
+  typedef DL<BK> D;
+  constexpr int PER = ROWS / D::RPI / NW;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = w * PER + i;
+    const int r = q * D::RPI + lane / D::CPR;
+    const int c = (lane % D::CPR) ^ D::swz(r);
+    const int gr = min(row0 + r, nrows - 1);
+    off[i] = (uint32_t)(((int64_t)gr * ld + c * 8) * 2);
+  }
+}
+template <int ROWS, int NW, int BK>
+TTT_DEV void dl_issue_off(const bf16* __restrict__ base_k0, const uint32_t (&off)[ROWS / DL<BK>::RPI / NW], bf16* tile,
+                          int w) {
+  constexpr int PER = ROWS / DL<BK>::RPI / NW;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(base_k0) + off[i]),
+                                     (lds_void_t*)(tile + (w * PER + i) * 512), 16, 0, 0);
+}
+
 template <int BK>
 TTT_DEV bf16x8 dl_frag(const bf16* tile, int r, int c) {
   return *reinterpret_cast<const bf16x8*>(tile + r * BK + ((c ^ DL<BK>::swz(r)) << 3));
@@ -737,6 +764,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 
   const bool use_pre = prefetch_operand<BM, BN, WGM, WGN, EPI>(p, z, m0, n0, wm, wn, lane, splits, pre);
   const int nkt = kt1 - kt0;
   const int rot = nkt > 0 ? (tm + tn) % nkt : 0;
+  // per-lane byte offsets of this wave's tile loads (K-contiguous operands)
+  uint32_t offa[MN ? 1 : BM / DL<BK>::RPI / NW], offb[MN ? 1 : BN / DL<BK>::RPI / NW];
+  if constexpr (!MN) {
+    dl_offsets<BM, NW, BK>(p.lda, m0, p.M, w, lane, offa);
+    dl_offsets<BN, NW, BK>(p.ldb, n0, p.N, w, lane, offb);
+  }
   auto issue = [&](int kt, int st) {
     int kp = kt - kt0 + rot;
     kp = kt0 + (kp >= nkt ? kp - nkt : kp);
@@ -744,8 +777,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 
       mn_issue(A, p.lda, m0, kp * BK, smem[st], w, lane);
       mn_issue(B, p.ldb, n0, kp * BK, smem[st] + BM * BK, w, lane);
     } else {
-      dl_issue<BM, NW, BK>(A, p.lda, m0, p.M, kp * BK, smem[st], w, lane);
-      dl_issue<BN, NW, BK>(B, p.ldb, n0, p.N, kp * BK, smem[st] + BM * BK, w, lane);
+      dl_issue_off<BM, NW, BK>(A + kp * BK, offa, smem[st], w);
+      dl_issue_off<BN, NW, BK>(B + kp * BK, offb, smem[st] + BM * BK, w);
     }
   };
 #pragma unroll
@@ -1126,13 +1159,16 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
     if (!cfg && p.M <= GV_MAXM) return launch_gemv<EPI, OutT>(p, batch, st);
   }
   if (p.nx) return hipErrorInvalidValue;  // a folded RMSNorm needs the skinny kernel
+  // the direct-to-LDS kernels address each operand with 32-bit byte offsets
+  const bool small32 = (int64_t)p.M * p.lda * 2 < (1ll << 32) && (int64_t)p.N * p.ldb * 2 < (1ll << 32) &&
+                       (int64_t)p.K * 2 < (1ll << 31);
   if (!cfg) {
     // direct-to-LDS 256x256 when there are enough large tiles (or K >= 8192,
     // long enough for split-K over few tiles to fill the CUs in one round);
     // register-staged kernels otherwise
     // (also when a short K leaves 128x128 tiles unsplit over more than one
     // round of block slots, and the large tiles alone cover over half the CUs)
-    const bool dl = sizeof(T) == 2 && p.K % 64 == 0;
+    const bool dl = sizeof(T) == 2 && p.K % 64 == 0 && small32;
     const bool ragged128 = t256 > CUS / 2 && t128 > 2 * CUS && p.K <= 48 * 64;
     if (dl && EPI != EPI_SGD && (t256 >= CUS || ragged128 || p.K >= 8192)) cfg = 4;
     else if (dl) cfg = 6;
@@ -1142,6 +1178,7 @@ hipError_t pick(const GemmArgs& p, int batch, float* ws, int64_t ws_elems, hipSt
     const int sp = k_splits<T>(p, batch, t256, CUS, ws_elems);
     return launch_t<T, 256, 256, 2, 4, EPI, OutT>(p, batch, sp, sp > 1 ? ws : nullptr, st);
   }
+  if (!small32 && cfg >= 4) cfg = (cfg == 4 || cfg == 5) ? 1 : 3;
   if constexpr (sizeof(T) == 2) {
     if ((cfg == 6 || cfg == 7) && p.K % 64 == 0) {
       // 128x128, two blocks per CU: at least 3/4 of the 512 slots, and short K
