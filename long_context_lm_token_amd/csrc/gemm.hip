@@ -403,10 +403,11 @@ TTT_DEV void epi_body(const GemmArgs& p, int z, int m0, int n0, int wm, int wn, 
 // with wide memory accesses: the fp32 master is read as float4 rows (512
 // bytes per row of the tile); per half of 64 rows, the owning waves stage
 // lr * acc in LDS ([64][132] fp32), and each thread updates 4 consecutive
-// columns of 8 rows: the
-// master written back with 16-byte stores, the row-major bf16 copy with
-// 8-byte stores, and the transposed copy staged ([128 cols][72] bf16) for
-// 16-byte stores of 8 rows. Same arithmetic as sgd_epilogue_staged.
+// columns of 8 rows: the master written back with 16-byte stores, the
+// row-major bf16 copy with 8-byte stores, and the transposed copy staged
+// ([128 cols][72] bf16) for 16-byte stores of 8 rows. The update is that of
+// sgd_epilogue_staged with lr * acc rounded to fp32 before the subtraction
+// (the other path may fuse the two: the results differ by at most an ulp).
 constexpr int SGDV_LA = 128 + 4, SGDV_LT = 64 + 8;
 constexpr int SGDV_LDS = 64 * SGDV_LA * 4 + 128 * SGDV_LT * 2;
 TTT_DEV bool sgd_vec_ok(const GemmArgs& p, int m0, int n0) {
