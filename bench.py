@@ -7,8 +7,9 @@ step). Inputs (weights, tokens) are resident in HBM before the timed region.
 
 Prints one JSON line (rank 0): tokens/s, ms per step, seconds per 1K tokens,
 the roofline of the dominant kernel class (the one with the largest share of
-kernel time in a profiled step), measured with HIP events on the stream each
-launch runs on over the timed steps, every class's roofline fraction from the
+kernel time in a profiled step), measured with HIP events attached to the
+dispatches of every 8th launch of that class over the timed steps (each timed
+dispatch costs its stream a few microseconds), every class's roofline fraction from the
 profiled step, the config-4 greedy decode (2048 tokens, two update pauses) and
 the CPU oracle timed on a bounded sample of the same workload beside the GPU
 on the same sample.
@@ -105,6 +106,9 @@ def main():
     ap.add_argument("--prof-class", default=None,
                     help="kernel class timed with HIP events during the timed steps (default: the class "
                          "with the largest share of kernel time in the profiled step)")
+    ap.add_argument("--prof-every", type=int, default=8,
+                    help="during the timed steps, time every N-th launch of the roofline class (1: all; each "
+                         "timed dispatch costs its stream a few microseconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=None,
                     help="labelled positions of the CPU-oracle sample (default: one chunk)")
@@ -175,7 +179,7 @@ def main():
     classes = class_table(prof_all)
     prof_class = args.prof_class or max(classes, key=lambda c: classes[c]["ms_per_step"])
     log(f"[bench] roofline class: {prof_class}")
-    model.prof_begin(prof_class)
+    model.prof_begin(prof_class, every=args.prof_every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -219,7 +223,7 @@ def main():
         achieved = k_flops / (k_ms / 1000) / 1e12 if k_ms > 0 else 0.0
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK / 1e12, "unit": "TFLOP/s",
                 "frac": round(achieved * 1e12 / MFMA_PEAK, 4), "traffic": traffic_bytes(prof_class, args.config)}
-    roof.update({"kernel": prof_class, "launches": k_launch,
+    roof.update({"kernel": prof_class, "launches": k_launch, "sampled_every": args.prof_every,
                  "avg_launch_us": round(k_ms * 1000 / max(k_launch, 1), 2),
                  "step_frac": round(step_flops / peak_bf16 / (ms_step / 1000), 4),
                  # the span passes run concurrently with the chunk loop, so

@@ -2,8 +2,9 @@
  * ttt_prof.h - kernel timing hooks of the TTT-E2E library (measurement only).
  *
  * ttt_prof_begin selects a kernel class. Every launch of that class made by
- * the following ttt_prefill / ttt_decode calls is bracketed by two hipEvents
- * recorded on the stream it runs on, and the launch's algorithmic work (flops
+ * the following ttt_prefill / ttt_decode calls is timed by two hipEvents
+ * attached to the dispatches of its own kernels (the first kernel records the
+ * start, the last the end; hipExtLaunchKernelGGL), and the launch's algorithmic work (flops
  * and HBM bytes of what the step must compute, not of what a kernel happens
  * to re-read or recompute) is accumulated. The classes:
  *   TTT_PROF_GEMM        every matrix product (the union of 5, 6 and 7)
@@ -31,11 +32,15 @@
  * and its output written once. GEMM launches include their split-K reduce.
  * TTT_PROF_ALL times every launch, each under exactly one of the disjoint
  * classes 1, 3 and 5..11 (read back with ttt_prof_end_classes).
+ * ttt_prof_sample(m, every), after ttt_prof_begin, times only every
+ * `every`-th launch of the selected class (in launch order, starting with the
+ * first; 1 = every launch): the sums then cover those launches, and their
+ * ratio (work per time) estimates the class's rate at a fraction of the cost.
  * ttt_prof_end waits for the recorded events and returns the summed event
  * time (ms), the launch count and the summed flops (bytes for CE, NORM and
- * OTHER), then switches timing off. Timing adds event records between
- * launches; leave it off for throughput.
- * Errors: TTT_EINVAL (NULL model, unknown class), TTT_EHIP.
+ * OTHER), then switches timing off. A timed dispatch still costs its stream a
+ * few microseconds; sample, or leave timing off, for throughput.
+ * Errors: TTT_EINVAL (NULL model, unknown class, every < 1), TTT_EHIP.
  */
 #ifndef TTT_PROF_H
 #define TTT_PROF_H
@@ -63,6 +68,7 @@ extern "C" {
 
 struct ttt_model;
 int ttt_prof_begin(struct ttt_model* m, int32_t kernel_class);
+int ttt_prof_sample(struct ttt_model* m, int32_t every);
 int ttt_prof_end(struct ttt_model* m, double* total_ms, int64_t* launches, double* total_work);
 /* Per-class totals (arrays of n entries, class index = array index; n <=
  * TTT_PROF_NCLASS): summed event time (ms), launches, flops and bytes of the

@@ -78,6 +78,7 @@ def load():
     lib.ttt_device_bytes_by_part.argtypes = [c_vp, c_vp]
     lib.ttt_model_create_session.argtypes = [c_vp, c_i32, c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(c_vp)]
     lib.ttt_prof_begin.argtypes = [c_vp, c_i32]
+    lib.ttt_prof_sample.argtypes = [c_vp, c_i32]
     lib.ttt_prof_end.argtypes = [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64),
                                  ctypes.POINTER(ctypes.c_double)]
     lib.ttt_prof_end_classes.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]
@@ -265,8 +266,11 @@ class TTTModel:
     def device_bytes(self):
         return load().ttt_device_bytes(self.h)
 
-    def prof_begin(self, cls: str):
+    def prof_begin(self, cls: str, every: int = 1):
+        """Time the launches of class `cls` (every `every`-th one)."""
         check(load().ttt_prof_begin(self.h, PROF[cls]))
+        if every != 1:
+            check(load().ttt_prof_sample(self.h, every))
 
     def prof_end(self):
         ms, n, work = ctypes.c_double(), c_i64(), ctypes.c_double()

@@ -1530,17 +1530,17 @@ hipError_t fwd_t(const AttnArgs& a, hipStream_t st) {
   const bool dl = sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
                   a.seq_stride % 8 == 0;
   if (dl && g_attn_dl == 1 && a.M <= ONE_MAXM && al16(a.q) && a.ldq % 8 == 0)
-    hipLaunchKernelGGL(attn_fwd_one_kernel, dim3(a.M, a.H, a.B * ns), dim3(256), 0, st, a);
+    TTT_LAUNCH(attn_fwd_one_kernel, dim3(a.M, a.H, a.B * ns), dim3(256), 0, st, a);
   else if (dl)
-    hipLaunchKernelGGL(attn_fwd_dl_kernel, grid, dim3(NT), 0, st, a);
+    TTT_LAUNCH(attn_fwd_dl_kernel, grid, dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+    TTT_LAUNCH((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   if (a.M <= ONE_MAXM)
-    hipLaunchKernelGGL((attn_combine_head_kernel<T>), dim3(a.B * a.M, a.H), dim3(64), 0, st, a);
+    TTT_LAUNCH((attn_combine_head_kernel<T>), dim3(a.B * a.M, a.H), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<T>), dim3(a.B * a.M), dim3(256), 0, st, a);
+    TTT_LAUNCH((attn_combine_kernel<T>), dim3(a.B * a.M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 template <typename T, int HD>
@@ -1551,9 +1551,9 @@ hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
   if (a.parts != 2) {
     if (sizeof(T) == 2 && HD == FD_HD && g_attn_dl && al16(a.kc) && al16(a.vc) && a.ldk % 8 == 0 &&
         a.seq_stride % 8 == 0)
-      hipLaunchKernelGGL(attn_bwd_dq_dl_kernel, grid, dim3(NT), 0, st, a);
+      TTT_LAUNCH(attn_bwd_dq_dl_kernel, grid, dim3(NT), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+      TTT_LAUNCH((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.parts == 1) return e;
   }
@@ -1567,9 +1567,9 @@ hipError_t bwd_t(const AttnArgs& a, hipStream_t st) {
   if (dl) {
     // key blocks of 64 in pairs
     const int nkb = (a.M + DK_KB - 1) / DK_KB;
-    hipLaunchKernelGGL(attn_bwd_dkdv_dl_kernel, dim3((nkb + 1) / 2, a.H, a.B), dim3(DKDV_NT), 0, st, a);
+    TTT_LAUNCH(attn_bwd_dkdv_dl_kernel, dim3((nkb + 1) / 2, a.H, a.B), dim3(DKDV_NT), 0, st, a);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), dim3((a.M + QB - 1) / QB, a.H, a.B), dim3(NT), 0, st, a);
+    TTT_LAUNCH((attn_bwd_dkdv_kernel<T, HD>), dim3((a.M + QB - 1) / QB, a.H, a.B), dim3(NT), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -579,8 +579,8 @@ hipError_t embed_launch(const int32_t* ids, int64_t ids_ss, int64_t p0, int S, i
   if (S <= 0 || B <= 0) return hipSuccess;
   dim3 g(S, B);
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(embed_kernel<bf16>, g, dim3(NT), 0, st, ids, ids_ss, p0, S, cp<bf16>(E), d, vocab, x),
-      hipLaunchKernelGGL(embed_kernel<float>, g, dim3(NT), 0, st, ids, ids_ss, p0, S, cp<float>(E), d, vocab, x));
+      TTT_LAUNCH(embed_kernel<bf16>, g, dim3(NT), 0, st, ids, ids_ss, p0, S, cp<bf16>(E), d, vocab, x),
+      TTT_LAUNCH(embed_kernel<float>, g, dim3(NT), 0, st, ids, ids_ss, p0, S, cp<float>(E), d, vocab, x));
   return hipGetLastError();
 }
 
@@ -591,7 +591,7 @@ hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, fl
   // rows of up to 4096 columns stay in registers (x read once)
   const int C = (d + 4 * NT - 1) / (4 * NT);
 #define TTT_NORM_FWD(TT, CC) \
-  hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, d, cp<TT>(g), eps, mp<TT>(y), rstd)
+  TTT_LAUNCH((rmsnorm_fwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, d, cp<TT>(g), eps, mp<TT>(y), rstd)
   if (C <= 4) {
     if (dt == 1) {
       if (C == 1) TTT_NORM_FWD(bf16, 1); else if (C == 2) TTT_NORM_FWD(bf16, 2);
@@ -604,8 +604,8 @@ hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, fl
   }
 #undef TTT_NORM_FWD
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, d, cp<bf16>(g), eps, mp<bf16>(y), rstd),
-      hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, d, cp<float>(g), eps, mp<float>(y), rstd));
+      TTT_LAUNCH(rmsnorm_fwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, d, cp<bf16>(g), eps, mp<bf16>(y), rstd),
+      TTT_LAUNCH(rmsnorm_fwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, d, cp<float>(g), eps, mp<float>(y), rstd));
   return hipGetLastError();
 }
 
@@ -615,7 +615,7 @@ hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, 
   if (d % 4) return hipErrorInvalidValue;
   const int C = (d + 4 * NT - 1) / (4 * NT);
 #define TTT_NORM_BWD(TT, CC)                                                                                       \
-  hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, rstd, cp<TT>(g), dn, d, dres, \
+  TTT_LAUNCH((rmsnorm_bwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, rstd, cp<TT>(g), dn, d, dres, \
                      mp<TT>(dres_c), accumulate)
   if (C <= 4) {
     if (dt == 1) {
@@ -629,8 +629,8 @@ hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, 
   }
 #undef TTT_NORM_BWD
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<bf16>(g), dn, d, dres, mp<bf16>(dres_c), accumulate),
-      hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<float>(g), dn, d, dres, mp<float>(dres_c), accumulate));
+      TTT_LAUNCH(rmsnorm_bwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<bf16>(g), dn, d, dres, mp<bf16>(dres_c), accumulate),
+      TTT_LAUNCH(rmsnorm_bwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<float>(g), dn, d, dres, mp<float>(dres_c), accumulate));
   return hipGetLastError();
 }
 
@@ -640,8 +640,8 @@ hipError_t rope_split_launch(const float* qkv, int rows, int S, int H, int hd, i
   if (rows <= 0) return hipSuccess;
   if (hd % 8) return hipErrorInvalidValue;
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(rope_split_kernel<bf16>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<bf16>(q), mp<bf16>(kc), mp<bf16>(vc), cap, seq_stride),
-      hipLaunchKernelGGL(rope_split_kernel<float>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<float>(q), mp<float>(kc), mp<float>(vc), cap, seq_stride));
+      TTT_LAUNCH(rope_split_kernel<bf16>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<bf16>(q), mp<bf16>(kc), mp<bf16>(vc), cap, seq_stride),
+      TTT_LAUNCH(rope_split_kernel<float>, dim3(rows), dim3(NT), 0, st, qkv, S, H, hd, p0, tab, mp<float>(q), mp<float>(kc), mp<float>(vc), cap, seq_stride));
   return hipGetLastError();
 }
 
@@ -651,8 +651,8 @@ hipError_t rope_bwd_pack_launch(const float* dq, int nsplit, const float* dk, co
   if (hd % 8) return hipErrorInvalidValue;
   const int64_t R = rows;
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(rope_bwd_pack_kernel<bf16>, dim3(rows), dim3(NT), 0, st, dq, nsplit, R, dk, dv, S, H, hd, p0, tab, mp<bf16>(dqkv)),
-      hipLaunchKernelGGL(rope_bwd_pack_kernel<float>, dim3(rows), dim3(NT), 0, st, dq, nsplit, R, dk, dv, S, H, hd, p0, tab, mp<float>(dqkv)));
+      TTT_LAUNCH(rope_bwd_pack_kernel<bf16>, dim3(rows), dim3(NT), 0, st, dq, nsplit, R, dk, dv, S, H, hd, p0, tab, mp<bf16>(dqkv)),
+      TTT_LAUNCH(rope_bwd_pack_kernel<float>, dim3(rows), dim3(NT), 0, st, dq, nsplit, R, dk, dv, S, H, hd, p0, tab, mp<float>(dqkv)));
   return hipGetLastError();
 }
 
@@ -662,8 +662,8 @@ hipError_t act_fwd_launch(const float* z, int rows, int h, int64_t ldz, int glu,
   if (h % 8 || ldz % 8 || lda % 8) return hipErrorInvalidValue;
   dim3 g((h / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(act_fwd_kernel<bf16>, g, dim3(NT), 0, st, z, h, ldz, glu, mp<bf16>(a), lda),
-      hipLaunchKernelGGL(act_fwd_kernel<float>, g, dim3(NT), 0, st, z, h, ldz, glu, mp<float>(a), lda));
+      TTT_LAUNCH(act_fwd_kernel<bf16>, g, dim3(NT), 0, st, z, h, ldz, glu, mp<bf16>(a), lda),
+      TTT_LAUNCH(act_fwd_kernel<float>, g, dim3(NT), 0, st, z, h, ldz, glu, mp<float>(a), lda));
   return hipGetLastError();
 }
 
@@ -673,8 +673,8 @@ hipError_t act_bwd_launch(const float* z, const float* da, int rows, int hcols, 
   if (hcols % 8 || ldz % 8 || ldda % 8 || up_off % 8 || lddz % 8) return hipErrorInvalidValue;
   dim3 g((hcols / 8 + NT - 1) / NT, rows);
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(act_bwd_kernel<bf16>, g, dim3(NT), 0, st, z, da, hcols, ldz, ldda, up_off, glu, mp<bf16>(dz), lddz),
-      hipLaunchKernelGGL(act_bwd_kernel<float>, g, dim3(NT), 0, st, z, da, hcols, ldz, ldda, up_off, glu, mp<float>(dz), lddz));
+      TTT_LAUNCH(act_bwd_kernel<bf16>, g, dim3(NT), 0, st, z, da, hcols, ldz, ldda, up_off, glu, mp<bf16>(dz), lddz),
+      TTT_LAUNCH(act_bwd_kernel<float>, g, dim3(NT), 0, st, z, da, hcols, ldz, ldda, up_off, glu, mp<float>(dz), lddz));
   return hipGetLastError();
 }
 
@@ -683,8 +683,8 @@ hipError_t attn_delta_launch(const void* o, const void* dout, int rows, int H, i
   if (rows <= 0) return hipSuccess;
   if (hd % 8 || hd / 8 > 64 || ((hd / 8) & (hd / 8 - 1))) return hipErrorInvalidValue;
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(rows), dim3(NT), 0, st, cp<bf16>(o), cp<bf16>(dout), H, hd, ld, S, delta),
-      hipLaunchKernelGGL(attn_delta_kernel<float>, dim3(rows), dim3(NT), 0, st, cp<float>(o), cp<float>(dout), H, hd, ld, S, delta));
+      TTT_LAUNCH(attn_delta_kernel<bf16>, dim3(rows), dim3(NT), 0, st, cp<bf16>(o), cp<bf16>(dout), H, hd, ld, S, delta),
+      TTT_LAUNCH(attn_delta_kernel<float>, dim3(rows), dim3(NT), 0, st, cp<float>(o), cp<float>(dout), H, hd, ld, S, delta));
   return hipGetLastError();
 }
 
@@ -692,8 +692,8 @@ hipError_t ce_launch(const CEArgs& a, int dt, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
   if (a.V % 8 || a.V > CE_NT * CE_IT * 8) return hipErrorInvalidValue;
   DT_DISPATCH(dt,
-      hipLaunchKernelGGL(ce_kernel<bf16>, dim3(a.rows), dim3(CE_NT), 0, st, a),
-      hipLaunchKernelGGL(ce_kernel<float>, dim3(a.rows), dim3(CE_NT), 0, st, a));
+      TTT_LAUNCH(ce_kernel<bf16>, dim3(a.rows), dim3(CE_NT), 0, st, a),
+      TTT_LAUNCH(ce_kernel<float>, dim3(a.rows), dim3(CE_NT), 0, st, a));
   return hipGetLastError();
 }
 
@@ -706,30 +706,30 @@ hipError_t transpose_launch(const void* src, int rows, int cols, int64_t lds, in
                   reinterpret_cast<uintptr_t>(dst) % 16 == 0;
   if (v8) {
     if (sdt == 1 && ddt == 1)
-      hipLaunchKernelGGL((transpose8_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
+      TTT_LAUNCH((transpose8_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
     else if (sdt == 1 && ddt == 0)
-      hipLaunchKernelGGL((transpose8_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
+      TTT_LAUNCH((transpose8_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
     else if (sdt == 0 && ddt == 1)
-      hipLaunchKernelGGL((transpose8_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
+      TTT_LAUNCH((transpose8_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
     else
-      hipLaunchKernelGGL((transpose8_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
+      TTT_LAUNCH((transpose8_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
     return hipGetLastError();
   }
   if (sdt == 1 && ddt == 1)
-    hipLaunchKernelGGL((transpose_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
+    TTT_LAUNCH((transpose_kernel<bf16, bf16>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
   else if (sdt == 1 && ddt == 0)
-    hipLaunchKernelGGL((transpose_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
+    TTT_LAUNCH((transpose_kernel<bf16, float>), g, dim3(256), 0, st, cp<bf16>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
   else if (sdt == 0 && ddt == 1)
-    hipLaunchKernelGGL((transpose_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
+    TTT_LAUNCH((transpose_kernel<float, bf16>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<bf16>(dst), ldd, s_src, s_dst);
   else
-    hipLaunchKernelGGL((transpose_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
+    TTT_LAUNCH((transpose_kernel<float, float>), g, dim3(256), 0, st, cp<float>(src), rows, cols, lds, mp<float>(dst), ldd, s_src, s_dst);
   return hipGetLastError();
 }
 
 hipError_t copy_rows_f32_launch(const float* src, int64_t sss, float* dst, int64_t dss, int S, int d, int B,
                                 hipStream_t st) {
   if (S <= 0 || B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_rows_kernel, dim3(S, B), dim3(NT), 0, st, src, sss, dst, dss, S, d);
+  TTT_LAUNCH(copy_rows_kernel, dim3(S, B), dim3(NT), 0, st, src, sss, dst, dss, S, d);
   return hipGetLastError();
 }
 
@@ -737,14 +737,14 @@ hipError_t fill_f32_launch(float* p, int64_t n, float v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + NT - 1) / NT;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(NT), 0, st, p, n, v);
+  TTT_LAUNCH(fill_kernel, dim3((unsigned)blocks), dim3(NT), 0, st, p, n, v);
   return hipGetLastError();
 }
 
 hipError_t decode_emit_launch(const int32_t* next, const float* lse, const float* mx, int B, int vocab,
                               int32_t* ids, int64_t ids_ss, int64_t pos, int32_t* out, int64_t out_ld, int64_t i,
                               float* losses, int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(decode_emit_kernel, dim3(1), dim3(((B + 63) / 64) * 64), 0, st, next, lse, mx, B, vocab, ids,
+  TTT_LAUNCH(decode_emit_kernel, dim3(1), dim3(((B + 63) / 64) * 64), 0, st, next, lse, mx, B, vocab, ids,
                      ids_ss, pos, out, out_ld, i, losses, status);
   return hipGetLastError();
 }

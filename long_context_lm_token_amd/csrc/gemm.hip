@@ -1053,7 +1053,7 @@ hipError_t launch_gemv(const GemmArgs& p, int batch, hipStream_t st) {
     return hipErrorInvalidValue;
   const int nout = (EPI == EPI_SWIGLU || EPI == EPI_ROPE) ? p.N / 2 : p.N;
   const int blocks = std::min((nout + 7) / 8, 4096);  // 4 waves of 2 outputs
-  hipLaunchKernelGGL((gemv_kernel<EPI, OutT>), dim3(blocks, 1, batch), dim3(256), 0, st, p);
+  TTT_LAUNCH((gemv_kernel<EPI, OutT>), dim3(blocks, 1, batch), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1067,28 +1067,28 @@ int g_force_splits = 0;
 template <int BM, int BN, int WGM, int WGN, int BK, int S, int EPI, typename OutT, bool MN = false>
 hipError_t launch_dl(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dl_kernel<BM, BN, WGM, WGN, BK, S, EPI, OutT, MN>), dim3(tiles, splits, batch),
+  TTT_LAUNCH((gemm_dl_kernel<BM, BN, WGM, WGN, BK, S, EPI, OutT, MN>), dim3(tiles, splits, batch),
                      dim3(WGM * WGN * 64), 0, st, p, splits, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
   const int64_t elems = (int64_t)p.M * p.N;
   int blocks = (int)std::min<int64_t>((elems + 255) / 256, 4096);
-  hipLaunchKernelGGL((gemm_reduce<bf16, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
+  TTT_LAUNCH((gemm_reduce<bf16, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
   return hipGetLastError();
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, typename OutT>
 hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStream_t st) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI, OutT>), dim3(tiles, splits, batch),
+  TTT_LAUNCH((gemm_kernel<T, BM, BN, WGM, WGN, EPI, OutT>), dim3(tiles, splits, batch),
                      dim3(WGM * WGN * 64), 0, st, p, splits, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
   const int64_t MN = (int64_t)p.M * p.N;
   int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
-  hipLaunchKernelGGL((gemm_reduce<T, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
+  TTT_LAUNCH((gemm_reduce<T, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
   return hipGetLastError();
 }
 

@@ -62,6 +62,19 @@ struct GemmArgs {
 };
 constexpr int GEMV_MAX_ROWS = 8;  // products with at most this many rows of A stream B once
 
+// Timing of launches. While `start` and `stop` are set (the runtime sets them
+// around the launches of a timed class), every kernel is launched with them
+// attached to its own dispatch (hipExtLaunchKernelGGL): the first kernel of
+// the group records `start` when it begins, each kernel records `stop` when
+// it ends (the last one wins), so the pair spans the group with no marker
+// packets between kernels. Unset (null), a launch is a plain launch. Per host
+// thread; defined in runtime.cpp.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchEvents& launch_events();
+
 // ws: fp32 split-K workspace of ws_elems elements (may be null: no split)
 hipError_t gemm_launch(const GemmArgs& p, int dt, int epi, bool out_f32, int batch, float* ws,
                        int64_t ws_elems, hipStream_t st);

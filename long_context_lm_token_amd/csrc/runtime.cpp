@@ -41,6 +41,11 @@
 #include "../../include/ttt_prof.h"
 #include "kernels.h"
 
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents le{nullptr, nullptr};
+  return le;
+}
+
 namespace {
 
 thread_local std::string g_err;
@@ -58,6 +63,8 @@ int fail(int code, const std::string& msg) {
 
 struct Prof {
   int cls = -1;  // kernel class being timed (TTT_PROF_ALL: every launch), -1 = off
+  int every = 1;     // time every `every`-th launch of the class
+  int64_t seen = 0;  // launches of the class so far
   std::vector<hipEvent_t> pool;
   size_t used = 0;
   std::vector<int> cls_of;     // per timed launch: its (disjoint) class
@@ -240,8 +247,11 @@ struct Alloc {
   void* el(int64_t n) { return get(n * (int64_t)m->es); }
 };
 
-// ---------- timing hooks (HIP events around launches of selected classes) ----------
-hipEvent_t prof_begin(ttt_model* m, hipStream_t st) {
+// ---------- timing hooks (HIP events on the launches of selected classes) ----------
+// The events ride on the kernels' own dispatches (launch_events(), kernels.h):
+// events recorded between the kernels of a stream would each add a marker
+// packet, and the stream would idle for it between the kernels.
+hipEvent_t prof_begin(ttt_model* m, hipStream_t) {
   Prof& p = m->prof;
   if (p.used + 2 > p.pool.size()) {
     for (int i = 0; i < 256; ++i) {
@@ -250,13 +260,19 @@ hipEvent_t prof_begin(ttt_model* m, hipStream_t st) {
       p.pool.push_back(e);
     }
   }
-  hipEvent_t e0 = p.pool[p.used];
-  (void)hipEventRecord(e0, st);
-  return e0;
+  LaunchEvents& le = launch_events();
+  le.start = p.pool[p.used];
+  le.stop = p.pool[p.used + 1];
+  return le.start;
 }
 void prof_end(ttt_model* m, hipStream_t st, int cls, double flops, double bytes) {
   Prof& p = m->prof;
-  (void)hipEventRecord(p.pool[p.used + 1], st);
+  LaunchEvents& le = launch_events();
+  if (le.start) {  // no kernel was launched: an empty interval at this point of the stream
+    (void)hipEventRecord(p.pool[p.used], st);
+    (void)hipEventRecord(p.pool[p.used + 1], st);
+  }
+  le.start = le.stop = nullptr;
   p.used += 2;
   p.cls_of.push_back(cls);
   p.flops.push_back(flops);
@@ -282,7 +298,7 @@ struct Ctx {
   template <class F>
   void run(int cls, double flops, double bytes, F&& f, hipStream_t s = nullptr, int alias = -1) {
     hipStream_t ss = s ? s : st;
-    if (!prof_wants(m->prof, cls, alias)) {
+    if (!prof_wants(m->prof, cls, alias) || m->prof.seen++ % m->prof.every != 0) {
       f();
       return;
     }
@@ -1535,10 +1551,20 @@ int ttt_prof_begin(ttt_model* m, int32_t kernel_class) {
   if (kernel_class < 0 || kernel_class > TTT_PROF_ALL) return fail(TTT_EINVAL, "kernel_class");
   Prof& p = m->prof;
   p.cls = kernel_class;
+  p.every = 1;
+  p.seen = 0;
   p.used = 0;
   p.cls_of.clear();
   p.flops.clear();
   p.bytes.clear();
+  return TTT_OK;
+}
+
+int ttt_prof_sample(ttt_model* m, int32_t every) {
+  if (!m) return fail(TTT_EINVAL, "model is NULL");
+  if (every < 1) return fail(TTT_EINVAL, "every must be >= 1");
+  m->prof.every = every;
+  m->prof.seen = 0;
   return TTT_OK;
 }
 

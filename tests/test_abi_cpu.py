@@ -97,3 +97,12 @@ def test_noalloc_attention_rejects_oversize_before_any_device_call():
     rc = lib.ttt_k_attn_fwd_noalloc(1, None, None, None, 9216, None, None, 1, 1024, 24, 128, 8192, 8192, 0.1, 17,
                                     None)
     assert rc == -1 and b"nsplit" in lib.ttt_k_last_error()
+
+
+def test_prof_sample_rejects_bad_arguments_without_gpu():
+    """Launch-timing selection is validated on the host."""
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.skip("library not built")
+    lib = bd.load()
+    assert lib.ttt_prof_sample(None, 4) == -1 and b"NULL" in lib.ttt_last_error()
+    assert lib.ttt_prof_begin(None, 6) == -1
