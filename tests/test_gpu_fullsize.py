@@ -135,6 +135,15 @@ def test_first_four_chunks(name):
         assert np.isfinite(gf[1:]).all()
         log(cfg, "full 131072-position prefill, first four chunks:")
         check_losses(cfg, gf[:n], o, name)
+        # at full size, a property of every chunk: the run is deterministic
+        # (fixed-order split reductions, no atomics), so a reset and the same
+        # ids give bitwise the same 131072 losses and final fast weights
+        w1 = model.get_weights(0, cfg["n_blocks"] - 1, "w_down").cpu().numpy()
+        model.reset()
+        gf2 = model.prefill(torch.as_tensor(toks).cuda()).cpu().numpy()[0]
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gf2, gf)
+        np.testing.assert_array_equal(model.get_weights(0, cfg["n_blocks"] - 1, "w_down").cpu().numpy(), w1)
     model.close()
 
 
