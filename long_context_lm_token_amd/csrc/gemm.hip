@@ -797,7 +797,6 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 
     else wait_vm<0>();
     // a plain barrier: a fenced one would also drain the younger tiles' loads
     asm volatile("s_barrier" ::: "memory");
-    if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
     const bf16* sa = smem[it % S] + (MN ? 0 : wm * WTM * BK);
     const bf16* sb = smem[it % S] + BM * BK + (MN ? 0 : wn * WTN * BK);
     // fragments double-buffered in registers: step ks+1 is read from LDS
@@ -817,7 +816,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 
         for (int j = 0; j < TJ; ++j) fb[b][j] = dl_frag<BK>(sb, j * 32 + (lane & 31), c);
       }
     };
+    // the first step's fragments are read before this wave issues its loads
+    // of the tile S-1 ahead (into the other stage), so their LDS latency
+    // passes during that issue instead of before the first MFMA
     read(0, 0);
+    if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) read(ks + 1, (ks + 1) & 1);
@@ -826,11 +829,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
     }
-    // schedule: the first step's reads, then each step's MFMAs alternate with
-    // the next step's reads (mask 0x8 = MFMA, 0x100 = LDS read); MN-major
-    // fragments take two reads each
+    // schedule: each step's MFMAs alternate with the next step's reads (mask
+    // 0x8 = MFMA, 0x100 = LDS read); MN-major fragments take two reads each
     constexpr int RD = (MN ? 2 : 1) * (TI + TJ);
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) {
