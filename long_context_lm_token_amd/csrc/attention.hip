@@ -459,8 +459,13 @@ TTT_DEV bf16x8 fd_frag_tr(const bf16* t, int d0, int g, int u, int lane) {
 
 __global__ __launch_bounds__(NT, 2) void attn_fwd_dl_kernel(AttnArgs a) {
   constexpr int NKS = FD_HD / 16, DB = FD_HD / 32;
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][BKEY * FD_HD];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][BKEY * FD_HD];
+  // K and V slots in one array. With an array per operand the compiler gives
+  // each its own alias scope and then waits for every LDS-DMA load in flight
+  // (vmcnt(0)) before each LDS read of that operand, which drains the step's
+  // prefetch; the kernel's own waits and barriers order every slot it reads.
+  __shared__ __attribute__((aligned(1024))) bf16 sKV[4][BKEY * FD_HD];
+  bf16(*const sK)[BKEY * FD_HD] = sKV;
+  bf16(*const sV)[BKEY * FD_HD] = sKV + 2;
 
   const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
   const Blk bk = blk();
@@ -977,8 +982,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(AttnArgs a) {
 // stored: their weights are masked to 0, and the caches hold finite values.
 __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_dl_kernel(AttnArgs a) {
   constexpr int NKS = FD_HD / 16, DB = FD_HD / 32;
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][BKEY * FD_HD];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][BKEY * FD_HD];
+  // K and V slots in one array (see attn_fwd_dl_kernel: no compiler waits on
+  // the LDS-DMA loads in flight before the reads of the other slot)
+  __shared__ __attribute__((aligned(1024))) bf16 sKV[4][BKEY * FD_HD];
+  bf16(*const sK)[BKEY * FD_HD] = sKV;
+  bf16(*const sV)[BKEY * FD_HD] = sKV + 2;
 
   const int nsplit = a.nsplit > 0 ? a.nsplit : 1;
   const Blk bk = blk();
@@ -1283,9 +1291,14 @@ __global__ __launch_bounds__(DKDV_NT) void attn_bwd_dkdv_dl_kernel(AttnArgs a) {
   constexpr int NKS = FD_HD / 16, DB = FD_HD / 32;
   constexpr int XF = DB * 16 * 64;  // floats of one wave's dK (or dV) partial
   // [stage][Q, dO][128 rows]: 128 KB; a stage doubles as the exchange buffer
-  __shared__ __attribute__((aligned(1024))) bf16 sQD[2][2][DK_QT * FD_HD];
-  __shared__ __attribute__((aligned(1024))) bf16 sVk[DK_KB * FD_HD];  // the block's V rows
-  __shared__ __attribute__((aligned(16))) float sL[2][DK_QT], sDl[2][DK_QT];
+  // one array for every tile the LDS-DMA loads fill (see attn_fwd_dl_kernel:
+  // no compiler waits on the loads in flight before the reads of other parts)
+  constexpr int QD_B = 2 * 2 * DK_QT * FD_HD * 2, VK_B = DK_KB * FD_HD * 2, ST_B = 2 * DK_QT * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[QD_B + VK_B + 2 * ST_B];
+  bf16(*const sQD)[2][DK_QT * FD_HD] = reinterpret_cast<bf16(*)[2][DK_QT * FD_HD]>(lds);
+  bf16* const sVk = reinterpret_cast<bf16*>(lds + QD_B);  // the block's V rows
+  float(*const sL)[DK_QT] = reinterpret_cast<float(*)[DK_QT]>(lds + QD_B + VK_B);
+  float(*const sDl)[DK_QT] = reinterpret_cast<float(*)[DK_QT]>(lds + QD_B + VK_B + ST_B);
 
   const Blk bk = blk();
   const int s = bk.z, h = bk.y;
