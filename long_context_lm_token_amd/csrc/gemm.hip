@@ -799,23 +799,39 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 
     asm volatile("s_barrier" ::: "memory");
     const bf16* sa = smem[it % S] + (MN ? 0 : wm * WTM * BK);
     const bf16* sb = smem[it % S] + BM * BK + (MN ? 0 : wn * WTN * BK);
-    // fragments double-buffered in registers: step ks+1 is read from LDS
-    // while the MFMAs of step ks run
+    // (K-contiguous operands) fragments double-buffered in registers: step
+    // ks+1 is read from LDS while the MFMAs of step ks run
     bf16x8 fa[2][TI], fb[2][TJ];
     auto read = [&](int ks, int b) {
-      if constexpr (MN) {
+      const int c = ks * 2 + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < TI; ++i) fa[b][i] = mn_frag(sa, wm * WTM + i * 32, ks, lane);
+      for (int i = 0; i < TI; ++i) fa[b][i] = dl_frag<BK>(sa, i * 32 + (lane & 31), c);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) fb[b][j] = mn_frag(sb, wn * WTN + j * 32, ks, lane);
-      } else {
-        const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < TI; ++i) fa[b][i] = dl_frag<BK>(sa, i * 32 + (lane & 31), c);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) fb[b][j] = dl_frag<BK>(sb, j * 32 + (lane & 31), c);
-      }
+      for (int j = 0; j < TJ; ++j) fb[b][j] = dl_frag<BK>(sb, j * 32 + (lane & 31), c);
     };
+    if constexpr (MN) {
+      // every fragment of the tile is read before this wave issues its loads
+      // of the tile S-1 ahead: the compiler makes a transposing LDS read wait
+      // for all LDS-DMA loads in flight (it carries no alias information), so
+      // a read after the issue would drain the prefetch before the tile's
+      // MFMAs had run
+      bf16x8 ga[BK / 16][TI], gb[BK / 16][TJ];
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) ga[ks][i] = mn_frag(sa, wm * WTM + i * 32, ks, lane);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) gb[ks][j] = mn_frag(sb, wn * WTN + j * 32, ks, lane);
+      }
+      if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma(ga[ks][i], gb[ks][j], acc[i][j]);
+      continue;
+    }
     // the first step's fragments are read before this wave issues its loads
     // of the tile S-1 ahead (into the other stage), so their LDS latency
     // passes during that issue instead of before the first MFMA
@@ -830,25 +846,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 && EPI == EPI_SGD ? 
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
     }
     // schedule: each step's MFMAs alternate with the next step's reads (mask
-    // 0x8 = MFMA, 0x100 = LDS read); MN-major fragments take two reads each
-    constexpr int RD = (MN ? 2 : 1) * (TI + TJ);
+    // 0x8 = MFMA, 0x100 = LDS read)
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) {
-        if constexpr (MN) {
 #pragma unroll
-          for (int q = 0; q < TI * TJ; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, (RD + TI * TJ - 1) / (TI * TJ), 0);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < TI + TJ; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ - (TI + TJ), 0);
+        for (int q = 0; q < TI + TJ; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ - (TI + TJ), 0);
       } else {
         __builtin_amdgcn_sched_group_barrier(0x8, TI * TJ, 0);
       }
