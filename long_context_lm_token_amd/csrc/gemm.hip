@@ -131,7 +131,9 @@ TTT_DEV T round_copy(float x, uint32_t seed, int z, int row, int col) {
 
 // MLP activations applied to fp32 accumulators (exact GELU; SiLU gate)
 TTT_DEV float gelu_acc(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
-TTT_DEV float swiglu_acc(float g, float u) { return g / (1.f + __expf(-g)) * u; }
+// silu(g) * u with the hardware reciprocal (1 ulp; the result is rounded to
+// the compute dtype) instead of an IEEE division sequence
+TTT_DEV float swiglu_acc(float g, float u) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u; }
 
 // interleaved column of hidden unit u's gate (its up column is 32 further)
 TTT_DEV int gate_col(int u) { return (u >> 5) * 64 + (u & 31); }
