@@ -134,11 +134,24 @@ __global__ void rmsnorm_fwd_reg_kernel(const float* x, int d, const T* g, float 
   if (threadIdx.x == 0) rstd[r] = rs;
 }
 
+// Four consecutive columns of dn: with splits > 1, dn arrives as the K-split
+// partial sums of the product that made it (split s at dn + s * ss), added
+// here in split order, the order a split-K reduce adds them in.
+TTT_DEV void get_dn4(const float* dr, int splits, int64_t ss, float (&v)[4]) {
+  get4(dr, v);
+  for (int s = 1; s < splits; ++s) {
+    float t[4];
+    get4(dr + s * ss, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += t[e];
+  }
+}
+
 // dx = r*g*dn - x * r^3 * mean(x*g*dn); dres (+)= dx; optional compute copy.
 // Four consecutive columns per thread (d % 4 == 0).
 template <typename T>
 __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g, const float* dn,
-                                   int d, float* dres, T* dres_c, bool accumulate) {
+                                   int dn_splits, int64_t dn_ss, int d, float* dres, T* dres_c, bool accumulate) {
   __shared__ float red[16];
   const int64_t r = blockIdx.x;
   const float* xr = x + r * d;
@@ -148,7 +161,7 @@ __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g
     float xv[4], gv[4], dv[4];
     get4(xr + c, xv);
     get4(g + c, gv);
-    get4(dr + c, dv);
+    get_dn4(dr + c, dn_splits, dn_ss, dv);
 #pragma unroll
     for (int e = 0; e < 4; ++e) dot += xv[e] * gv[e] * dv[e];
   }
@@ -161,7 +174,7 @@ __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g
     float xv[4], gv[4], dv[4], v[4];
     get4(xr + c, xv);
     get4(g + c, gv);
-    get4(dr + c, dv);
+    get_dn4(dr + c, dn_splits, dn_ss, dv);
     if (accumulate) get4(o + c, v);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = rs * gv[e] * dv[e] - xv[e] * k + (accumulate ? v[e] : 0.f);
@@ -173,7 +186,8 @@ __global__ void rmsnorm_bwd_kernel(const float* x, const float* rstd, const T* g
 // The same with the row's x, dn (and dres) held in registers (d <= C*4*NT).
 template <typename T, int C>
 __global__ void rmsnorm_bwd_reg_kernel(const float* x, const float* rstd, const T* g, const float* dn,
-                                       int d, float* dres, T* dres_c, bool accumulate) {
+                                       int dn_splits, int64_t dn_ss, int d, float* dres, T* dres_c,
+                                       bool accumulate) {
   __shared__ float red[16];
   const int64_t r = blockIdx.x;
   const float* xr = x + r * d;
@@ -187,7 +201,7 @@ __global__ void rmsnorm_bwd_reg_kernel(const float* x, const float* rstd, const 
       float gv[4], dv[4];
       get4(xr + c, xv[k]);
       get4(g + c, gv);
-      get4(dr + c, dv);
+      get_dn4(dr + c, dn_splits, dn_ss, dv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         gd[k][e] = gv[e] * dv[e];
@@ -610,13 +624,14 @@ hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, fl
 }
 
 hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, const float* dn, int rows,
-                              int d, float* dres, void* dres_c, bool accumulate, int dt, hipStream_t st) {
+                              int d, float* dres, void* dres_c, bool accumulate, int dt, hipStream_t st,
+                              int dn_splits, int64_t dn_ss) {
   if (rows <= 0) return hipSuccess;
-  if (d % 4) return hipErrorInvalidValue;
+  if (d % 4 || dn_splits < 1 || (dn_splits > 1 && dn_ss < (int64_t)rows * d)) return hipErrorInvalidValue;
   const int C = (d + 4 * NT - 1) / (4 * NT);
 #define TTT_NORM_BWD(TT, CC)                                                                                       \
-  TTT_LAUNCH((rmsnorm_bwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, rstd, cp<TT>(g), dn, d, dres, \
-                     mp<TT>(dres_c), accumulate)
+  TTT_LAUNCH((rmsnorm_bwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, rstd, cp<TT>(g), dn, dn_splits,      \
+             dn_ss, d, dres, mp<TT>(dres_c), accumulate)
   if (C <= 4) {
     if (dt == 1) {
       if (C == 1) TTT_NORM_BWD(bf16, 1); else if (C == 2) TTT_NORM_BWD(bf16, 2);
@@ -629,8 +644,10 @@ hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, 
   }
 #undef TTT_NORM_BWD
   DT_DISPATCH(dt,
-      TTT_LAUNCH(rmsnorm_bwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<bf16>(g), dn, d, dres, mp<bf16>(dres_c), accumulate),
-      TTT_LAUNCH(rmsnorm_bwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<float>(g), dn, d, dres, mp<float>(dres_c), accumulate));
+      TTT_LAUNCH(rmsnorm_bwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<bf16>(g), dn, dn_splits, dn_ss, d,
+                 dres, mp<bf16>(dres_c), accumulate),
+      TTT_LAUNCH(rmsnorm_bwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, rstd, cp<float>(g), dn, dn_splits, dn_ss,
+                 d, dres, mp<float>(dres_c), accumulate));
   return hipGetLastError();
 }
 

@@ -1082,6 +1082,12 @@ hipError_t launch_dl(const GemmArgs& p, int batch, int splits, float* ws, hipStr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
+  if constexpr (EPI == EPI_STORE && sizeof(OutT) == 4) {
+    if (p.split_out) {  // the consumer adds the partials
+      *p.split_out = splits;
+      return hipSuccess;
+    }
+  }
   const int64_t elems = (int64_t)p.M * p.N;
   int blocks = (int)std::min<int64_t>((elems + 255) / 256, 4096);
   TTT_LAUNCH((gemm_reduce<bf16, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
@@ -1096,6 +1102,12 @@ hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
+  if constexpr (EPI == EPI_STORE && sizeof(OutT) == 4) {
+    if (p.split_out) {  // the consumer adds the partials
+      *p.split_out = splits;
+      return hipSuccess;
+    }
+  }
   const int64_t MN = (int64_t)p.M * p.N;
   int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
   TTT_LAUNCH((gemm_reduce<T, EPI, OutT>), dim3(blocks, batch), dim3(256), 0, st, p, splits, batch, ws);
@@ -1254,6 +1266,7 @@ void gemm_force_tile(int cfg) {
 
 hipError_t gemm_launch(const GemmArgs& p, int dtype, int epi, bool out_f32, int batch, float* ws, int64_t ws_elems,
                        hipStream_t st) {
+  if (p.split_out) *p.split_out = 1;
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
   if (p.K % (dtype == 1 ? 8 : 4)) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU && p.N % 64) return hipErrorInvalidValue;

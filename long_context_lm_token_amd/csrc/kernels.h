@@ -59,6 +59,12 @@ struct GemmArgs {
   int64_t ldnx, snx;
   const void* ng;
   float neps;
+  // EPI_STORE with fp32 output: if set (a host pointer), a product split over
+  // K leaves its partial sums in the workspace for the consumer to add, in
+  // split order: split s of output row r (rows of all batches counted
+  // together) at ws + (s * batch * M + r) * N. The number of splits is
+  // written here (1: no split, C holds the result).
+  int* split_out;
 };
 constexpr int GEMV_MAX_ROWS = 8;  // products with at most this many rows of A stream B once
 
@@ -116,9 +122,11 @@ hipError_t embed_launch(const int32_t* ids, int64_t ids_seq_stride, int64_t p0, 
                         const void* E, int d, int vocab, float* x, int dt, hipStream_t st);
 hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, float eps, void* y,
                               float* rstd, int dt, hipStream_t st);
+// dn_splits > 1: dn holds that many partial sums of the gradient (split s at
+// dn + s * dn_ss, dn_ss >= rows * d), added in order (GemmArgs::split_out)
 hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, const float* dn,
                               int rows, int d, float* dres, void* dres_c, bool accumulate, int dt,
-                              hipStream_t st);
+                              hipStream_t st, int dn_splits = 1, int64_t dn_ss = 0);
 hipError_t rope_split_launch(const float* qkv, int rows, int S, int H, int hd, int64_t p0,
                              const float2* rope_tab, void* q, void* kc, void* vc, int cap,
                              int64_t seq_stride, int dt, hipStream_t st);

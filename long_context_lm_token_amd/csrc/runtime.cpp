@@ -406,13 +406,20 @@ void norm_fwd(Ctx& c, const float* x, int R, const void* g, void* y, float* rstd
   });
 }
 
+// dn: the gradient at the norm's output. dn_splits > 1: the product that
+// made it was split over K and left its partial sums in this stream's split-K
+// workspace (GemmArgs::split_out); the norm adds them, in split order.
 void norm_bwd(Ctx& c, const float* x, const float* rstd, const void* g, const float* dn, int R, float* dres,
-              void* dres_c, bool accumulate) {
+              void* dres_c, bool accumulate, int dn_splits = 1) {
   ttt_model* m = c.m;
   const int d = m->d;
-  const double bytes = (double)R * d * (8.0 + (accumulate ? 8.0 : 4.0) + (dres_c ? m->es : 0.0)) + 4.0 * R;
+  const double bytes =
+      (double)R * d * (4.0 * (1 + dn_splits) + (accumulate ? 8.0 : 4.0) + (dres_c ? m->es : 0.0)) + 4.0 * R;
+  const float* src = dn_splits > 1 ? m->ws : dn;
   c.run(TTT_PROF_NORM, 0, bytes, [&] {
-    c.chk(rmsnorm_bwd_launch(x, rstd, g, dn, R, d, dres, dres_c, accumulate, m->dt, c.st), "norm_bwd");
+    c.chk(rmsnorm_bwd_launch(x, rstd, g, src, R, d, dres, dres_c, accumulate, m->dt, c.st, dn_splits,
+                             (int64_t)R * d),
+          "norm_bwd");
   });
 }
 
@@ -658,8 +665,15 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
   // gradients: input grads use the [in][out] copies of the weights; weight
   // grads read the activations and output gradients token-major (MN-major
   // operands), or token-contiguous copies of them
-  c.gemm(EPI_STORE, true, ga(m->tdz, V, m->wout_b, V, m->dn, d, R, d, V));
-  norm_bwd(c, m->txL, m->trf, m->gfin, m->dn, R, m->dres, m->dres_b[m->nt - 1], false);
+  // each input-gradient product that feeds a norm backward leaves its K
+  // splits to it (dn_sp: the split count)
+  int dn_sp = 1;
+  {
+    GemmArgs g = ga(m->tdz, V, m->wout_b, V, m->dn, d, R, d, V);
+    g.split_out = &dn_sp;
+    c.gemm(EPI_STORE, true, g);
+  }
+  norm_bwd(c, m->txL, m->trf, m->gfin, m->dn, R, m->dres, m->dres_b[m->nt - 1], false, dn_sp);
   const bool master = m->dt == 1, mnw = m->mn_dw;
   const int64_t sbgu = (int64_t)d * zw, sbd = (int64_t)hf * d;  // per-seq strides of the [in][out] copies
   for (int j = m->nt - 1; j >= 0; --j) {
@@ -698,6 +712,9 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       // dn = dZ . W_gu^T (reads W_c before its update below)
       g = ga(dz, zw, m->fb_gu[j], zw, m->dn, d, M, d, zw);
       g.sA = (int64_t)M * zw; g.sB = sbgu; g.sC = (int64_t)M * d;
+      // (the multi-head fast MLP adds its part to dn itself)
+      dn_sp = 1;
+      if (!m->mh) g.split_out = &dn_sp;
       c.gemm(EPI_STORE, true, g, B);
     }
     // multi-head fast MLP: its input gradient added to dn, then its update
@@ -739,7 +756,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       c.gemm(EPI_SGD, false, g, by_part ? mg : B, gu_st);
     }
     if (j == 0) break;
-    norm_bwd(c, m->ty[j], m->tr2[j], m->g_mlp[l], m->dn, R, m->dres, m->dres_c, true);
+    norm_bwd(c, m->ty[j], m->tr2[j], m->g_mlp[l], m->dn, R, m->dres, m->dres_c, true, dn_sp);
     // attention sublayer
     c.gemm(EPI_STORE, false, ga(m->dres_c, d, m->wo_b[l], d, m->dO, HD, R, HD, d));
     c.run(TTT_PROF_OTHER, 0, (double)R * (2.0 * HD * es + 4.0 * m->H), [&] {
@@ -770,9 +787,11 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
                                  m->cfg.rope ? m->rope : nullptr, m->dqkv, m->dt, c.st),
             "rope_bwd");
     });
-    c.gemm(EPI_STORE, true, ga(m->dqkv, 3 * HD, m->wqkv_b[l], 3 * HD, m->dn, d, R, d, 3 * HD));
+    g = ga(m->dqkv, 3 * HD, m->wqkv_b[l], 3 * HD, m->dn, d, R, d, 3 * HD);
+    g.split_out = &dn_sp;
+    c.gemm(EPI_STORE, true, g);
     // the gradient at block j's input is the one at block j-1's MLP output
-    norm_bwd(c, m->tx[j], m->tr1[j], m->g_attn[l], m->dn, R, m->dres, m->dres_b[j - 1], true);
+    norm_bwd(c, m->tx[j], m->tr1[j], m->g_attn[l], m->dn, R, m->dres, m->dres_b[j - 1], true, dn_sp);
   }
   // the next use of the fast weights (and of the per-block operand copies) waits
   // for every SGD step of this chunk
