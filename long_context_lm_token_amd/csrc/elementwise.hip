@@ -74,19 +74,53 @@ __global__ void embed_kernel(const int32_t* ids, int64_t ids_ss, int64_t p0, int
 }
 
 // ------------------------------- RMSNorm ---------------------------------
+// Where the norm's input row comes from. Plain: x (row stride d). Split
+// (splits > 1): x holds the K-split partial sums of the product whose output
+// is the row (split s at x + s * ss) and `res` the residual that product's
+// epilogue adds; the norm adds the partials in split order, then the
+// residual, as a split-K reduce does, and stores the row to `out`.
+struct NormIn {
+  const float* x;
+  int splits;
+  int64_t ss;
+  const float* res;
+  float* out;
+};
+
+// four consecutive columns (offset o of the row block) of the input row
+TTT_DEV void norm_in4(const NormIn& in, int64_t o, float (&v)[4]) {
+  get4(in.x + o, v);
+  if (in.splits > 1) {
+    for (int s = 1; s < in.splits; ++s) {
+      float t[4];
+      get4(in.x + s * in.ss + o, t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += t[e];
+    }
+    float t[4];
+    get4(in.res + o, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += t[e];
+    put4(in.out + o, v);
+  }
+}
+
 // y = x * (mean(x^2) + eps)^(-1/2) * g ; rstd saved for the backward.
 template <typename T>
-__global__ void rmsnorm_fwd_kernel(const float* x, int d, const T* g, float eps, T* y, float* rstd) {
+__global__ void rmsnorm_fwd_kernel(NormIn in, int d, const T* g, float eps, T* y, float* rstd) {
   __shared__ float red[16];
   const int64_t r = blockIdx.x;
-  const float* xr = x + r * d;
   float ss = 0.f;
   for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    float v[4];
+    norm_in4(in, r * d + c, v);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
   ss = block_sum(ss, red);
   const float rs = rsqrtf(ss / d + eps);
+  // the second pass reads the row back where the first pass left it (each
+  // thread its own columns)
+  const float* xr = (in.splits > 1 ? in.out : in.x) + r * d;
   T* yr = y + r * d;
   for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
     float v[4], gg[4];
@@ -102,17 +136,16 @@ __global__ void rmsnorm_fwd_kernel(const float* x, int d, const T* g, float eps,
 // The same with the row held in registers (C float4 per thread, d <= C*4*NT):
 // x is read once.
 template <typename T, int C>
-__global__ void rmsnorm_fwd_reg_kernel(const float* x, int d, const T* g, float eps, T* y, float* rstd) {
+__global__ void rmsnorm_fwd_reg_kernel(NormIn in, int d, const T* g, float eps, T* y, float* rstd) {
   __shared__ float red[16];
   const int64_t r = blockIdx.x;
-  const float* xr = x + r * d;
   float v[C][4];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < C; ++k) {
     const int c = (k * NT + threadIdx.x) * 4;
     if (c < d) {
-      get4(xr + c, v[k]);
+      norm_in4(in, r * d + c, v[k]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) ss += v[k][e] * v[k][e];
     }
@@ -599,13 +632,16 @@ hipError_t embed_launch(const int32_t* ids, int64_t ids_ss, int64_t p0, int S, i
 }
 
 hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, float eps, void* y,
-                              float* rstd, int dt, hipStream_t st) {
+                              float* rstd, int dt, hipStream_t st, int x_splits, int64_t x_ss,
+                              const float* x_res, float* x_out) {
   if (rows <= 0) return hipSuccess;
-  if (d % 4) return hipErrorInvalidValue;
+  if (d % 4 || x_splits < 1) return hipErrorInvalidValue;
+  if (x_splits > 1 && (x_ss < (int64_t)rows * d || !x_res || !x_out)) return hipErrorInvalidValue;
+  const NormIn in{x, x_splits, x_ss, x_res, x_out};
   // rows of up to 4096 columns stay in registers (x read once)
   const int C = (d + 4 * NT - 1) / (4 * NT);
 #define TTT_NORM_FWD(TT, CC) \
-  TTT_LAUNCH((rmsnorm_fwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, x, d, cp<TT>(g), eps, mp<TT>(y), rstd)
+  TTT_LAUNCH((rmsnorm_fwd_reg_kernel<TT, CC>), dim3(rows), dim3(NT), 0, st, in, d, cp<TT>(g), eps, mp<TT>(y), rstd)
   if (C <= 4) {
     if (dt == 1) {
       if (C == 1) TTT_NORM_FWD(bf16, 1); else if (C == 2) TTT_NORM_FWD(bf16, 2);
@@ -618,8 +654,8 @@ hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, fl
   }
 #undef TTT_NORM_FWD
   DT_DISPATCH(dt,
-      TTT_LAUNCH(rmsnorm_fwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, x, d, cp<bf16>(g), eps, mp<bf16>(y), rstd),
-      TTT_LAUNCH(rmsnorm_fwd_kernel<float>, dim3(rows), dim3(NT), 0, st, x, d, cp<float>(g), eps, mp<float>(y), rstd));
+      TTT_LAUNCH(rmsnorm_fwd_kernel<bf16>, dim3(rows), dim3(NT), 0, st, in, d, cp<bf16>(g), eps, mp<bf16>(y), rstd),
+      TTT_LAUNCH(rmsnorm_fwd_kernel<float>, dim3(rows), dim3(NT), 0, st, in, d, cp<float>(g), eps, mp<float>(y), rstd));
   return hipGetLastError();
 }
 

@@ -1082,7 +1082,7 @@ hipError_t launch_dl(const GemmArgs& p, int batch, int splits, float* ws, hipStr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
-  if constexpr (EPI == EPI_STORE && sizeof(OutT) == 4) {
+  if constexpr ((EPI == EPI_STORE || EPI == EPI_ADD) && sizeof(OutT) == 4) {
     if (p.split_out) {  // the consumer adds the partials
       *p.split_out = splits;
       return hipSuccess;
@@ -1102,7 +1102,7 @@ hipError_t launch_t(const GemmArgs& p, int batch, int splits, float* ws, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if constexpr (EPI == EPI_ROPE) return hipErrorInvalidValue;  // never split
-  if constexpr (EPI == EPI_STORE && sizeof(OutT) == 4) {
+  if constexpr ((EPI == EPI_STORE || EPI == EPI_ADD) && sizeof(OutT) == 4) {
     if (p.split_out) {  // the consumer adds the partials
       *p.split_out = splits;
       return hipSuccess;

@@ -59,11 +59,11 @@ struct GemmArgs {
   int64_t ldnx, snx;
   const void* ng;
   float neps;
-  // EPI_STORE with fp32 output: if set (a host pointer), a product split over
-  // K leaves its partial sums in the workspace for the consumer to add, in
-  // split order: split s of output row r (rows of all batches counted
-  // together) at ws + (s * batch * M + r) * N. The number of splits is
-  // written here (1: no split, C holds the result).
+  // EPI_STORE / EPI_ADD with fp32 output: if set (a host pointer), a product
+  // split over K leaves its partial sums in the workspace for the consumer to
+  // add, in split order (then R, for EPI_ADD): split s of output row r (rows
+  // of all batches counted together) at ws + (s * batch * M + r) * N. The
+  // number of splits is written here (1: no split, C holds the result).
   int* split_out;
 };
 constexpr int GEMV_MAX_ROWS = 8;  // products with at most this many rows of A stream B once
@@ -120,8 +120,13 @@ int attn_splits(int M, int H, int B, int64_t keys_per_query);
 // elementwise / row kernels
 hipError_t embed_launch(const int32_t* ids, int64_t ids_seq_stride, int64_t p0, int S, int B,
                         const void* E, int d, int vocab, float* x, int dt, hipStream_t st);
+// x_splits > 1: x holds that many partial sums of an EPI_ADD product's output
+// (split s at x + s * x_ss, x_ss >= rows * d; GemmArgs::split_out) and x_res
+// its residual; the row, sum of the partials in order plus x_res, is also
+// stored to x_out (all rows of stride d)
 hipError_t rmsnorm_fwd_launch(const float* x, int rows, int d, const void* g, float eps, void* y,
-                              float* rstd, int dt, hipStream_t st);
+                              float* rstd, int dt, hipStream_t st, int x_splits = 1, int64_t x_ss = 0,
+                              const float* x_res = nullptr, float* x_out = nullptr);
 // dn_splits > 1: dn holds that many partial sums of the gradient (split s at
 // dn + s * dn_ss, dn_ss >= rows * d), added in order (GemmArgs::split_out)
 hipError_t rmsnorm_bwd_launch(const float* x, const float* rstd, const void* g, const float* dn,

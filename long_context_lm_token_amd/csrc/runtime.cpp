@@ -397,12 +397,23 @@ void qkv(Ctx& c, const void* u, int l, int R, int S, int64_t p0, float* qkv32, v
   });
 }
 
-// RMSNorm forward of R rows of width d (fp32 in, compute dtype out, rstd)
-void norm_fwd(Ctx& c, const float* x, int R, const void* g, void* y, float* rstd) {
+// RMSNorm forward of R rows of width d (fp32 in, compute dtype out, rstd).
+// x_splits > 1: the rows are the output of an EPI_ADD product (residual
+// x_res) that was split over K and left its partial sums in this stream's
+// split-K workspace (GemmArgs::split_out); the norm adds them, in split
+// order, then x_res, and stores the rows to x.
+void norm_fwd(Ctx& c, float* x, int R, const void* g, void* y, float* rstd, int x_splits = 1,
+              const float* x_res = nullptr) {
   ttt_model* m = c.m;
   const int d = m->d;
-  c.run(TTT_PROF_NORM, 0, (double)R * d * (4.0 + m->es) + 4.0 * R, [&] {
-    c.chk(rmsnorm_fwd_launch(x, R, d, g, m->cfg.norm_eps, y, rstd, m->dt, c.st), "norm");
+  const double bytes = (double)R * d * (x_splits > 1 ? 4.0 * x_splits + 8.0 : 4.0) + (double)R * d * m->es + 4.0 * R;
+  c.run(TTT_PROF_NORM, 0, bytes, [&] {
+    if (x_splits > 1)
+      c.chk(rmsnorm_fwd_launch(m->ws, R, d, g, m->cfg.norm_eps, y, rstd, m->dt, c.st, x_splits, (int64_t)R * d,
+                               x_res, x),
+            "norm");
+    else
+      c.chk(rmsnorm_fwd_launch(x, R, d, g, m->cfg.norm_eps, y, rstd, m->dt, c.st), "norm");
   });
 }
 
@@ -604,12 +615,16 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
   c.run(TTT_PROF_OTHER, 0, 8.0 * R * d, [&] {
     c.chk(copy_rows_f32_launch(m->ystage + P0 * d, m->maxpos * d, m->tx[0], (int64_t)M * d, M, d, B, c.st), "copy");
   });
+  // the down projection of each tail block leaves its K splits (x_sp) and
+  // residual (x_res) to the norm that reads its output
+  int x_sp = 1;
+  const float* x_res = nullptr;
   for (int j = 0; j < m->nt; ++j) {
     const int l = m->t0 + j;
     float* y = m->tx[j];  // block t0: the residual after its attention
     if (j >= 1) {
       y = m->ty[j];
-      if (!fold_r) norm_fwd(c, m->tx[j], R, m->g_attn[l], m->tU, m->tr1[j]);
+      if (!fold_r) norm_fwd(c, m->tx[j], R, m->g_attn[l], m->tU, m->tr1[j], x_sp, x_res);
       qkv(c, m->tU, l, R, M, P0, m->tQKV, m->tq[j], m->cap_t, fold_r ? m->tx[j] : nullptr, m->g_attn[l],
           TTT_PROF_GEMM_CHUNK);
       AttnArgs a;
@@ -638,10 +653,14 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     g = ga(m->ta[j], hf, m->f_d[j], hf, xo, d, M, d, hf);
     g.sA = (int64_t)M * hf; g.sB = sd; g.sC = (int64_t)M * d;
     g.R = y; g.ldr = d; g.sR = (int64_t)M * d;
+    // (the multi-head fast MLP adds its output to xo itself)
+    x_sp = 1;
+    x_res = y;
+    if (!fold_r && !m->mh) g.split_out = &x_sp;
     c.gemm(EPI_ADD, true, g, B);
     if (m->mh) mh_forward(c, j, M, xo);
   }
-  if (!fold_r) norm_fwd(c, m->txL, R, m->gfin, m->tf, m->trf);
+  if (!fold_r) norm_fwd(c, m->txL, R, m->gfin, m->tf, m->trf, x_sp, x_res);
   {
     GemmArgs g = ga(m->tf, d, m->wout_t, d, m->tlog, V, R, V, d);
     if (fold_r) fold_norm(g, m->txL, d, 0, m->gfin, eps);
