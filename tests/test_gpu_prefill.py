@@ -128,6 +128,32 @@ def test_bf16_small_model():
     model.close()
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_products_split_over_k(dtype):
+    """Every product that may split over K split in two (the GEMM test hook):
+    the chunk loop's norms then take the partial sums of the products that
+    feed them (head dX, MLP and QKV input gradients into the norm backward;
+    the down projection and its residual into the next norm forward) in place
+    of the reduce kernel. Two tail blocks, several chunks, against the oracle
+    at the unsplit runs' bounds."""
+    lib = bd.load()
+    if dtype == "fp32":
+        cfg, n, std, tol = small_cfg(), 6 * 16 + 5, 0.2, FP32_TOL
+    else:
+        cfg = small_cfg(dtype="bf16", vocab=512, d_model=256, n_heads=4, head_dim=64, mlp_hidden=512,
+                        ttt_hidden=256, static_hidden=256, n_blocks=4, n_ttt_blocks=2, window=128,
+                        mini_batch=64, lr=0.05, span=32, period=256)
+        n, std, tol = 5 * 64 + 9, 0.05, BF16_TOL
+    lib.ttt_k_gemm_tile(2 << 8)  # automatic tiles, two K splits
+    try:
+        model, wn, g, o, ors, _ = run_prefill(cfg, n, std=std)
+    finally:
+        lib.ttt_k_gemm_tile(0)
+    check_losses(g, o, tol["loss"])
+    compare_weights(cfg, model, ors, wn, tol["w"], tol["dw"])
+    model.close()
+
+
 def test_bf16_two_sequences_head_dim_128():
     """bf16 with head dim 128 (the direct-to-LDS attention kernels) and two
     sequences (per-sequence strides of every product, incl. the weight
