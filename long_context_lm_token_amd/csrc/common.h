@@ -56,15 +56,14 @@ TTT_DEV float block_max(float v, float* red) {
 // Host-side launch error check used by the launchers.
 #define TTT_LAUNCH_CHECK() (hipGetLastError())
 
-// Every kernel launch of the library: a plain launch, or, while the events
-// of launch_events() (kernels.h) are set, one with them attached to its own
-// dispatch.
+// Every kernel launch of the library: a plain launch, or, while the timing
+// events of launch_events() (kernels.h) are set, one with them attached to
+// its own dispatch.
 #define TTT_LAUNCH(kernel, grid, block, shmem, stream, ...)                                       \
   do {                                                                                            \
     LaunchEvents& le_ = launch_events();                                                          \
     hipEvent_t start_ = le_.start;                                                                \
     le_.start = nullptr;                                                                          \
-    ++le_.launches;                                                                               \
     hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)(shmem), stream, start_, le_.stop, 0u, \
                           __VA_ARGS__);                                                           \
   } while (0)

@@ -68,20 +68,16 @@ struct GemmArgs {
 };
 constexpr int GEMV_MAX_ROWS = 8;  // products with at most this many rows of A stream B once
 
-// Events carried by launches. While `start` and `stop` are set (the runtime
-// sets them around the launches of a timed class), every kernel is launched
-// with them attached to its own dispatch (hipExtLaunchKernelGGL): the first
-// kernel of the group records `start` when it begins, each kernel records
-// `stop` when it ends (the last one wins), so the pair spans the group with
-// no marker packets between kernels. `stop` alone, set around an untimed
-// group, is an event another stream can wait on for that group (the stream
-// is in order, so for all its work before). Unset (null), a launch is a plain
-// launch. `launches` counts every launch. Per host thread; defined in
-// runtime.cpp.
+// Timing of launches. While `start` and `stop` are set (the runtime sets them
+// around the launches of a timed class), every kernel is launched with them
+// attached to its own dispatch (hipExtLaunchKernelGGL): the first kernel of
+// the group records `start` when it begins, each kernel records `stop` when
+// it ends (the last one wins), so the pair spans the group with no marker
+// packets between kernels. Unset (null), a launch is a plain launch. Per host
+// thread; defined in runtime.cpp.
 struct LaunchEvents {
   hipEvent_t start;
   hipEvent_t stop;
-  int64_t launches;
 };
 LaunchEvents& launch_events();
 

@@ -42,7 +42,7 @@
 #include "kernels.h"
 
 LaunchEvents& launch_events() {
-  static thread_local LaunchEvents le{nullptr, nullptr, 0};
+  static thread_local LaunchEvents le{nullptr, nullptr};
   return le;
 }
 
@@ -284,8 +284,6 @@ struct Ctx {
   ttt_model* m;
   hipStream_t st;
   bool own_ws = true;  // the split-K workspace belongs to the caller's stream
-  hipEvent_t pend_ev = nullptr;  // order_after_next
-  hipStream_t pend_to = nullptr;
   hipError_t err = hipSuccess;
   const char* where = "";
   void chk(hipError_t e, const char* w) {
@@ -297,42 +295,16 @@ struct Ctx {
   // Run `f` (one or more launches on stream s, default st); when the timing
   // hooks select class `cls` (or `alias`), bracket it with events and record
   // its algorithmic flops and HBM bytes.
-  // With an order set by order_after_next, stream `pend_to` is then made to
-  // wait for these launches.
   template <class F>
   void run(int cls, double flops, double bytes, F&& f, hipStream_t s = nullptr, int alias = -1) {
     hipStream_t ss = s ? s : st;
-    const hipEvent_t pe = pend_ev;
-    pend_ev = nullptr;
     if (!prof_wants(m->prof, cls, alias) || m->prof.seen++ % m->prof.every != 0) {
-      LaunchEvents& le = launch_events();
-      const int64_t n0 = le.launches;
-      if (pe) le.stop = pe;
       f();
-      if (pe) {
-        le.stop = nullptr;
-        finish_order(pe, ss, le.launches > n0);
-      }
       return;
     }
     hipEvent_t e0 = prof_begin(m, ss);
     f();
     if (e0) prof_end(m, ss, cls, flops, bytes);
-    if (pe) finish_order(pe, ss, false);
-  }
-  // Make stream `to` wait for everything enqueued on this context's stream up
-  // to and including the launches of the next run(): those kernels carry `e`
-  // as their dispatches' end event, so no marker packet sits between them and
-  // the next kernel (~5 us of idle stream each). When that run is timed (its
-  // kernels carry the timing events) or launches nothing, `e` is recorded
-  // after it instead.
-  void order_after_next(hipEvent_t e, hipStream_t to) {
-    pend_ev = e;
-    pend_to = to;
-  }
-  void finish_order(hipEvent_t e, hipStream_t from, bool attached) {
-    if (!attached) chk(hipEventRecord(e, from), "event record");
-    chk(hipStreamWaitEvent(pend_to, e, 0), "stream wait");
   }
   // C = A . B^T-ish per GemmArgs, optionally batched over sequences. cls: the
   // timing class (span pass, chunk loop or weight gradient + SGD).
@@ -731,11 +703,11 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
     // dA = dres . W_down^T  (reads W_c before its update below)
     GemmArgs g = ga(drc, d, m->fb_d[j], d, m->dA, hf, M, hcols, d);
     g.sA = (int64_t)M * d; g.sB = sbd; g.sC = (int64_t)M * hf;
-    if (mnw) c.order_after_next(m->ev[2 * j], m->side);
     c.gemm(EPI_STORE, true, g, B);
     // W_down trainable columns: W^T[d][ht] -= eta * dres^T . A_t  (side stream,
     // after the dA GEMM above has read W_c)
     if (mnw) {
+      c.order(c.st, m->side, m->ev[2 * j]);
       g = ga(drc, d, m->ta[j], hf, master ? m->f_d[j] : nullptr, hf, d, ht, M);
       g.sA = (int64_t)M * d; g.sB = (int64_t)M * hf; g.mn = 1;
     } else {
@@ -762,8 +734,6 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       // (the multi-head fast MLP adds its part to dn itself)
       dn_sp = 1;
       if (!m->mh) g.split_out = &dn_sp;
-      // the gate/up update below waits for this product (it reads W_c)
-      if (mnw && !m->mh) c.order_after_next(m->ev[2 * j + 1], m->side);
       c.gemm(EPI_STORE, true, g, B);
     }
     // multi-head fast MLP: its input gradient added to dn, then its update
@@ -782,7 +752,7 @@ void tail_pass(Ctx& c, int64_t P0, int M, bool bwd, float* losses, int64_t loss_
       }
     }
     hipStream_t gu_st = j == 0 ? nullptr : m->side;
-    if (j > 0 && !(mnw && !m->mh)) c.order(c.st, m->side, m->ev[2 * j + 1]);
+    if (j > 0) c.order(c.st, m->side, m->ev[2 * j + 1]);
     const bool by_part = B == 1 && mg > 1;
     for (int part = 0; part < (by_part ? 1 : mg); ++part) {
       const int64_t zoff = (int64_t)part * hf;      // column of dZ / row of the forward copy
